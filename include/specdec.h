@@ -1,0 +1,154 @@
+/*
+ * specdec.h -- C ABI of the MI355X (gfx950) batched speculative-decoding verify step.
+ *
+ * The operation (one "round" per sequence) is the draft-then-verify rule that all three
+ * source pages state:
+ *   - "Decodificação especulativa explicada: rascunhe barato, verifique numa passada"
+ *     (gsantana.dev), sections "O ciclo de rascunho e verificação" and
+ *     "A regra de amostragem por rejeição";
+ *   - "ch15 · Speculative Decoding" (snowch.github.io, LLM serving from scratch), section
+ *     "Why the result is exactly the target model" (its accept_sampled interface:
+ *     target logits, draft probabilities, proposed ids, sampling parameters, a random
+ *     generator -> emitted tokens and the number accepted);
+ *   - "Speculative decoding: el secretario que adelanta lo que va a decir el jefe"
+ *     (blog.lo0.es), section "El mecanismo desnudo", step 3.
+ *
+ * For sequence b with k = k_b drafts x_0..x_{k-1}, target logit rows z_0..z_k and drafter
+ * distributions q_0..q_{k-1}:
+ *   p_i = softmax(z_i / T_b)                       (T_b = 0: greedy, p_i = point mass on argmax)
+ *   for i = 0..k-1, left to right:
+ *     accept x_i  iff  u[b,i] * q_i(x_i) < p_i(x_i)          (probability min(1, p/q))
+ *     on the first rejection: emit y ~ norm(max(0, p_i - q_i)) drawn with u[b,K]; stop
+ *   if all k are accepted: emit a bonus y ~ p_k drawn with u[b,K]
+ *   accept_len[b] = number of accepted drafts A in [0, k]; the round emits A + 1 tokens.
+ * Greedy rows accept x_i iff x_i is the lowest-index argmax of z_i and emit that argmax at
+ * the first mismatch (or as the bonus).  Sampling is inverse-CDF over ascending token id:
+ * the first token whose running weight sum exceeds u times the total.  One-hot rows
+ * (n-gram / prompt-lookup drafters, q_i = onehot(x_i)) accept iff u < p_i(x_i) and redraw
+ * from p_i with x_i removed.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is DEVICE memory on the current HIP device, except where
+ *     noted.  The caller owns every buffer; the library allocates nothing, keeps no
+ *     per-call state and never synchronises: work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and the call returns immediately.
+ *   - Layouts are dense row-major, innermost dimension contiguous.
+ *   - The returned status covers what the host can check (NULL pointers, sizes, dtype,
+ *     element alignment, workspace size) plus launch errors.  Data errors are found on the
+ *     device and poison only their sequence: accept_len[b] = -1, every out_tokens slot
+ *     -1, every out_probs slot 0.  A sequence is invalid when k_b is outside [0, K]; T_b is
+ *     negative, NaN, infinite or in (0, SPECDEC_TEMPERATURE_MIN); a used logit row
+ *     (rows 0..k_b) holds a NaN or +inf or is all -inf; a proposed id in slots < k_b is
+ *     outside [0, V); for a sampled row a used uniform (columns < k_b and column K) is
+ *     outside [0, 1); or for a sampled model-draft row a gathered q_i(x_i) is negative or
+ *     not finite, or draft_probs is NULL.
+ *   - Padded rows and slots (rows k_b+1..K of the logits, draft rows k_b..K-1, proposed
+ *     and uniform columns k_b..K-1) are never read.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
+ */
+#ifndef SPECDEC_H_
+#define SPECDEC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPECDEC_OK = 0,
+  SPECDEC_ERR_NULL = -1,      /* a required pointer is NULL                               */
+  SPECDEC_ERR_SHAPE = -2,     /* B < 0, K < 0, K > SPECDEC_MAX_K, V < 1, or sizes overflow */
+  SPECDEC_ERR_DTYPE = -3,     /* logits_dtype is not a specdec_dtype                      */
+  SPECDEC_ERR_ALIGN = -4,     /* a tensor base is not aligned to its element size         */
+  SPECDEC_ERR_WORKSPACE = -5, /* workspace NULL or smaller than specdec_workspace_size()  */
+  SPECDEC_ERR_LAUNCH = -6     /* a kernel launch or event record failed                   */
+} specdec_status;
+
+typedef enum {
+  SPECDEC_F32 = 0,            /* IEEE binary32 logits                                     */
+  SPECDEC_BF16 = 1            /* bfloat16 logits (upper 16 bits of a binary32)            */
+} specdec_dtype;
+
+#define SPECDEC_MAX_K 63                  /* drafts per sequence (K+1 rows fit one wave64) */
+#define SPECDEC_TEMPERATURE_MIN 1e-6f     /* smallest non-zero temperature accepted       */
+
+/* Bytes of device workspace specdec_verify / specdec_verify_greedy need for these sizes
+ * (a pure function of B, K, V; 0 for B == 0).  The workspace holds per-row partial
+ * statistics and per-sequence sampling state; its contents need no initialisation and
+ * are meaningless after the call.  Returns 0 for invalid sizes. */
+size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V);
+
+/* Batched rejection-sampling verify (sampled and greedy rows mixed by temperature).
+ *
+ * target_logits  [B, K+1, V]  logits_dtype; row i of sequence b is the target's
+ *                             next-token logits after the prefix and drafts x_0..x_{i-1}.
+ * draft_probs    [B, K, V]    float32 drafter probabilities q_i, used exactly as given
+ *                             (never renormalised).  Only the gathered q_i(x_i) and, for a
+ *                             rejected model-draft row, the one row q_j are read.  May be
+ *                             NULL when no sampled row is a model-draft row.
+ * draft_onehot   [B]          uint8, nonzero = one-hot (n-gram) row.  NULL = none.
+ * proposed       [B, K]       int32 drafted ids x_i.  May be NULL when K == 0.
+ * num_draft      [B]          int32 k_b in [0, K].  NULL = every sequence has K drafts.
+ * temperature    [B]          float32; 0 = greedy row (reads neither q nor u).
+ * uniforms       [B, K+1]     float32 in [0, 1): column i < K is accept test i, column K
+ *                             the one correction-or-bonus draw.
+ * accept_len     [B]    out   int32 A_b in [0, k_b], or -1 for an invalid sequence.
+ * out_tokens     [B, K+1] out int32: slots 0..A_b hold the emitted tokens (accepted drafts,
+ *                             then the correction or bonus token); other slots -1.
+ * out_probs      [B, K+1] out float32 or NULL: the target probability p_i(token) of each
+ *                             emitted token (greedy rows report softmax at T = 1); other
+ *                             slots 0.
+ * workspace                   device scratch of at least workspace_bytes >=
+ *                             specdec_workspace_size(B, K, V) bytes, 16-byte aligned.
+ * stream                      hipStream_t (NULL = default stream).
+ * The caller rolls both KV caches back to prefix + accept_len[b] + 1 tokens.
+ */
+specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
+                              const float* draft_probs, const uint8_t* draft_onehot,
+                              const int32_t* proposed, const int32_t* num_draft,
+                              const float* temperature, const float* uniforms,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Greedy-only verify: every row is treated as temperature 0 (accept x_i iff it is the
+ * lowest-index argmax of z_i; emit the argmax at the first mismatch or as the bonus).
+ * Arguments as for specdec_verify; no q, T or u is read.  out_probs may be NULL; when
+ * given it receives softmax at T = 1 of each emitted token. */
+specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_dtype,
+                                     const int32_t* proposed, const int32_t* num_draft,
+                                     int32_t B, int32_t K, int32_t V,
+                                     int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement hook: HIP events (hipEvent_t, host handles) recorded on `stream` immediately
+ * before and after the streaming logit-row kernel (the one that reads every target row).
+ * Either may be NULL.  Passing opts == NULL to specdec_verify_ex is the same as
+ * specdec_verify. */
+typedef struct {
+  void* hot_event_begin;
+  void* hot_event_end;
+} specdec_options;
+
+specdec_status specdec_verify_ex(const void* target_logits, int32_t logits_dtype,
+                                 const float* draft_probs, const uint8_t* draft_onehot,
+                                 const int32_t* proposed, const int32_t* num_draft,
+                                 const float* temperature, const float* uniforms,
+                                 int32_t B, int32_t K, int32_t V,
+                                 int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 const specdec_options* opts);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* specdec_status_string(int32_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t specdec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H_ */

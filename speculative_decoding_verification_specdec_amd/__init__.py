@@ -1,0 +1,12 @@
+"""MI355X-native batched speculative-decoding verify step.
+
+The compute lives in ``libspecdec.so`` (hand-written HIP for gfx950 behind a C ABI declared in
+``include/specdec.h``); ``specdec_verify`` and friends below only marshal torch device tensors
+into that ABI.  Importing the package does not load the library; the first call does, and it
+raises if the library is missing.
+"""
+from .binding import (SpecdecError, specdec_verify, specdec_verify_greedy, specdec_workspace_size,
+                      specdec_status_string, library_path, load_library)
+
+__all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_workspace_size",
+           "specdec_status_string", "library_path", "load_library"]

@@ -1,0 +1,192 @@
+"""ctypes binding of ``libspecdec.so`` (the C ABI in ``include/specdec.h``).
+
+Argument marshalling only: torch device tensors are checked for device, dtype, contiguity and
+shape, turned into raw pointers and handed to the library together with the current HIP
+stream.  Every step of the verify computation runs in the library's HIP kernels; there is no
+CPU or PyTorch fallback, and a missing library raises ``SpecdecError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+
+import torch
+
+_LIB = None
+
+SPECDEC_F32 = 0
+SPECDEC_BF16 = 1
+SPECDEC_MAX_K = 63
+
+
+class SpecdecError(RuntimeError):
+    pass
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("hot_event_begin", ctypes.c_void_p), ("hot_event_end", ctypes.c_void_p)]
+
+
+def library_path() -> pathlib.Path:
+    env = os.environ.get("SPECDEC_LIBRARY")
+    return pathlib.Path(env) if env else pathlib.Path(__file__).with_name("libspecdec.so")
+
+
+def load_library():
+    """Load the HIP library once; raise SpecdecError if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not path.exists():
+        raise SpecdecError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                           f"g.build()'` (hipcc, gfx950). There is no fallback path.")
+    lib = ctypes.CDLL(str(path))
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    common = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.specdec_verify.argtypes = common
+    lib.specdec_verify.restype = i32
+    lib.specdec_verify_ex.argtypes = common + [ctypes.POINTER(_Options)]
+    lib.specdec_verify_ex.restype = i32
+    lib.specdec_verify_greedy.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.specdec_verify_greedy.restype = i32
+    lib.specdec_workspace_size.argtypes = [i32, i32, i32]
+    lib.specdec_workspace_size.restype = sz
+    lib.specdec_status_string.argtypes = [i32]
+    lib.specdec_status_string.restype = ctypes.c_char_p
+    lib.specdec_version.argtypes = []
+    lib.specdec_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def specdec_status_string(status: int) -> str:
+    return load_library().specdec_status_string(int(status)).decode()
+
+
+def specdec_workspace_size(B: int, K: int, V: int) -> int:
+    return int(load_library().specdec_workspace_size(int(B), int(K), int(V)))
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor | None, name: str, dtype, shape, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise SpecdecError(f"{name} is required")
+    if t.device != device:
+        raise SpecdecError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise SpecdecError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise SpecdecError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise SpecdecError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _outputs(B, K, device, out, want_probs):
+    if out is not None:
+        return out
+    acc = torch.empty(B, dtype=torch.int32, device=device)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=device)
+    prb = torch.empty((B, K + 1), dtype=torch.float32, device=device) if want_probs else None
+    return acc, tok, prb
+
+
+def _workspace(B, K, V, device, workspace):
+    need = specdec_workspace_size(B, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def _raise(status: int, fn: str):
+    if status != 0:
+        raise SpecdecError(f"{fn}: {specdec_status_string(status)} (status {status})")
+
+
+def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None,
+                   proposed: torch.Tensor | None, temperature: torch.Tensor,
+                   uniforms: torch.Tensor, *, draft_onehot: torch.Tensor | None = None,
+                   num_draft: torch.Tensor | None = None, out=None, workspace=None,
+                   want_probs: bool = True, stream=None, hot_events=None):
+    """Batched verify.  Shapes: target_logits [B, K+1, V] (bf16 or fp32), draft_probs
+    [B, K, V] fp32 or None, proposed [B, K] int32, temperature [B] fp32, uniforms [B, K+1]
+    fp32, draft_onehot [B] uint8 or None, num_draft [B] int32 or None.  Returns
+    (accept_len [B] int32, out_tokens [B, K+1] int32, out_probs [B, K+1] fp32 or None),
+    enqueued on ``stream`` (default: torch's current stream) without synchronising.
+    ``hot_events``: optional (begin, end) torch.cuda.Event pair recorded around the
+    streaming logit-row kernel."""
+    lib = load_library()
+    if target_logits.dim() != 3:
+        raise SpecdecError("target_logits must be [B, K+1, V]")
+    B, K1, V = (int(s) for s in target_logits.shape)
+    K = K1 - 1
+    dev = target_logits.device
+    if target_logits.dtype == torch.bfloat16:
+        dt = SPECDEC_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = SPECDEC_F32
+    else:
+        raise SpecdecError(f"target_logits dtype {target_logits.dtype} is not bf16/fp32")
+    if not target_logits.is_contiguous():
+        raise SpecdecError("target_logits must be contiguous")
+    _check(draft_probs, "draft_probs", torch.float32, (B, K, V), dev, optional=True)
+    _check(proposed, "proposed", torch.int32, (B, K), dev, optional=(K == 0))
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    _check(draft_onehot, "draft_onehot", torch.uint8, (B,), dev, optional=True)
+    _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
+    acc, tok, prb = _outputs(B, K, dev, out, want_probs)
+    ws, need = _workspace(B, K, V, dev, workspace)
+    args = (_ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_onehot), _ptr(proposed),
+            _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc), _ptr(tok),
+            _ptr(prb), _ptr(ws), ws.numel(), _stream_handle(stream))
+    if hot_events is None:
+        status = lib.specdec_verify(*args)
+    else:
+        opts = _Options(ctypes.c_void_p(hot_events[0].cuda_event if hot_events[0] is not None else 0),
+                        ctypes.c_void_p(hot_events[1].cuda_event if hot_events[1] is not None else 0))
+        status = lib.specdec_verify_ex(*args, ctypes.byref(opts))
+    _raise(status, "specdec_verify")
+    return acc, tok, prb
+
+
+def specdec_verify_greedy(target_logits: torch.Tensor, proposed: torch.Tensor | None, *,
+                          num_draft: torch.Tensor | None = None, out=None, workspace=None,
+                          want_probs: bool = True, stream=None):
+    """Greedy-only verify (every row at temperature 0).  Returns (accept_len, out_tokens,
+    out_probs or None)."""
+    lib = load_library()
+    if target_logits.dim() != 3:
+        raise SpecdecError("target_logits must be [B, K+1, V]")
+    B, K1, V = (int(s) for s in target_logits.shape)
+    K = K1 - 1
+    dev = target_logits.device
+    if target_logits.dtype == torch.bfloat16:
+        dt = SPECDEC_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = SPECDEC_F32
+    else:
+        raise SpecdecError(f"target_logits dtype {target_logits.dtype} is not bf16/fp32")
+    if not target_logits.is_contiguous():
+        raise SpecdecError("target_logits must be contiguous")
+    _check(proposed, "proposed", torch.int32, (B, K), dev, optional=(K == 0))
+    _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
+    acc, tok, prb = _outputs(B, K, dev, out, want_probs)
+    ws, need = _workspace(B, K, V, dev, workspace)
+    status = lib.specdec_verify_greedy(_ptr(target_logits), dt, _ptr(proposed), _ptr(num_draft),
+                                       B, K, V, _ptr(acc), _ptr(tok), _ptr(prb), _ptr(ws),
+                                       ws.numel(), _stream_handle(stream))
+    _raise(status, "specdec_verify_greedy")
+    return acc, tok, prb
