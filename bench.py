@@ -1,0 +1,213 @@
+"""Benchmark of the batched verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--replicas R] [--no-cpu-baseline]
+
+Workload: the batch workload -- B=64 sequences, k=5 drafts, V=128256, bf16 target logits, fp32
+draft probabilities, per-row temperature U[0.5, 1.2] (seeded synthetic inputs).  One step is
+one specdec_verify call over that batch: row statistics of all 384 target rows, the accept
+scan, and the residual / bonus draw.  Inputs are resident in HBM before timing starts; R
+copies of them are rotated step by step so the 256 MB Infinity Cache cannot serve a step from
+the previous one.
+
+Prints ONE JSON line: verified draft positions per second (sum_b k_b per step / step time),
+plus a roofline object for the streaming row-statistics kernel (algorithmic logit bytes per
+launch / its HIP-event-timed duration, against the 8 TB/s HBM peak) and the fp64 CPU oracle's
+rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec and HBM GB/s (% of peak), B=64 V=128256 k=5"
+HBM_PEAK_GBS = 8000.0
+HOT_KERNEL = "row_stats_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_kernel_batch64_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_verification_specdec_amd", "csrc",
+                             "kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(bytes_alg_per_launch: float):
+    """HBM bytes per launch of the hot kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration it records), or None when
+    the summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """The fp64 oracle (as it stands) on the same inputs: whole batches, repeated until about
+    ``budget_s`` of single-core CPU work has run."""
+    import oracle
+    positions = int(inp.draft_counts().sum())
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify(inp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 200:
+            break
+    return dict(value=positions * n / el, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{n} full oracle calls on the same B=64 V=128256 k=5 batch "
+                       f"({el:.1f} s, single thread, numpy fp64)")
+
+
+def algorithmic_bytes(inp, acc_np):
+    """Bytes the method must move per call: every used target row once, ids, q gathers,
+    uniforms, temperatures, one draft row per rejected model-draft sampled sequence, outputs."""
+    import numpy as np
+    kb = inp.draft_counts()
+    sz = 2 if inp.logits_dtype == "bf16" else 4
+    V = inp.V
+    sampled = inp.temperature > 0
+    onehot = np.zeros(inp.B, bool) if inp.draft_onehot is None else inp.draft_onehot.astype(bool)
+    model = sampled & ~onehot
+    rejected = (acc_np >= 0) & (acc_np < kb)
+    logits = float(((kb + 1) * V * sz).sum())
+    small = float((4 * kb + 4 * kb * model + 4 * (kb + 1) * sampled + 4 + 8 * (kb + 1) + 4).sum())
+    draft_rows = float((rejected & model).sum() * 4 * V)
+    return logits, logits + small + draft_rows
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verify step shards by sequence with no "
+              "communication, so only --gpus 1 is supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verification_specdec_amd import (inputs_to_device, specdec_verify,
+                                                               specdec_workspace_size)
+    from speculative_decoding_verification_specdec_amd.inputs import batch64
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating the B=64 V=128256 k=5 batch", file=sys.stderr, flush=True)
+    inp = batch64()
+    reps = [inputs_to_device(inp, dev) for _ in range(args.replicas)]
+    B, K, V = inp.B, inp.K, inp.V
+    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    prb = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+    out = (acc, tok, prb)
+    stream = torch.cuda.current_stream()
+
+    def step(i, hot=None):
+        d = reps[i % len(reps)]
+        specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
+                       d["uniforms"], draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
+                       out=out, workspace=ws, stream=stream, hot_events=hot)
+
+    print(f"[bench] warmup {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` whole steps, bracketed by synchronisation and HIP events.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+
+    # Same loop again with HIP events around the streaming row-statistics kernel of each step.
+    hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, hot=hot[i])
+    torch.cuda.synchronize()
+    hot_ms = sum(b.elapsed_time(e) for b, e in hot) / args.steps
+
+    acc_np = acc.cpu().numpy()
+    assert (acc_np >= 0).all(), "invalid rows in the benchmark batch"
+    logit_bytes, call_bytes = algorithmic_bytes(inp, acc_np)
+    positions = int(inp.draft_counts().sum())
+    value = positions / (ms_per_step * 1e-3)
+    achieved = logit_bytes / (hot_ms * 1e-3) / 1e9
+    traffic = measured_traffic(logit_bytes)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "batch64: B=64 sequences, k=5 drafts, V=128256, bf16 target logits "
+                        "~N(0,3^2), fp32 draft probs from 0.8z+N(0,1.5^2), T~U[0.5,1.2]",
+            "global_batch": B, "k": K, "vocab": V, "logits_dtype": "bf16",
+            "replicas_rotated": args.replicas,
+        },
+        "roofline": {
+            "kernel": HOT_KERNEL,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel_us": hot_ms * 1e3,
+            "bytes_per_launch": logit_bytes,
+        },
+        "whole_step": {
+            "us": ms_per_step * 1e3,
+            "wall_us": wall / args.steps * 1e6,
+            "algorithmic_bytes": call_bytes,
+            "algorithmic_GBps": call_bytes / (ms_per_step * 1e-3) / 1e9,
+            "frac_of_hbm_peak": call_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "rejected_sequences": int((acc_np < K).sum()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,7 +6,8 @@ into that ABI.  Importing the package does not load the library; the first call 
 raises if the library is missing.
 """
 from .binding import (SpecdecError, specdec_verify, specdec_verify_greedy, specdec_workspace_size,
-                      specdec_status_string, library_path, load_library)
+                      specdec_status_string, library_path, load_library,
+                      inputs_to_device)
 
 __all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_workspace_size",
-           "specdec_status_string", "library_path", "load_library"]
+           "specdec_status_string", "library_path", "load_library", "inputs_to_device"]

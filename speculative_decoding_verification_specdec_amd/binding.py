@@ -190,3 +190,23 @@ def specdec_verify_greedy(target_logits: torch.Tensor, proposed: torch.Tensor | 
                                        ws.numel(), _stream_handle(stream))
     _raise(status, "specdec_verify_greedy")
     return acc, tok, prb
+
+
+def inputs_to_device(inp, device) -> dict:
+    """Copy a host ``VerifyInputs`` batch to device tensors (bf16 bit patterns become bf16)."""
+    def dev(a, dtype=None):
+        if a is None:
+            return None
+        t = torch.from_numpy(a)
+        if dtype is not None:
+            t = t.view(dtype)
+        return t.to(device).contiguous()
+    if inp.logits_dtype == "bf16":
+        logits = dev(inp.logits.view("int16"), torch.bfloat16)
+    elif inp.logits_dtype == "f32":
+        logits = dev(inp.logits)
+    else:
+        raise SpecdecError(f"logits dtype {inp.logits_dtype!r} has no device form")
+    return dict(logits=logits, draft_probs=dev(inp.draft_probs), draft_onehot=dev(inp.draft_onehot),
+                proposed=dev(inp.proposed), num_draft=dev(inp.num_draft),
+                temperature=dev(inp.temperature), uniforms=dev(inp.uniforms))

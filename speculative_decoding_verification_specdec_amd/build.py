@@ -1,0 +1,50 @@
+"""Build step of libspecdec.so: hipcc for gfx950, in-tree next to this file.
+
+    python -m speculative_decoding_verification_specdec_amd.build
+"""
+from __future__ import annotations
+
+import os
+import pathlib
+import subprocess
+import sys
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+SOURCES = [PKG / "csrc" / "kernels.hip", PKG / "csrc" / "api.cpp"]
+HEADERS = [PKG / "csrc" / "kernels.h", ROOT / "include" / "specdec.h"]
+OUTPUT = PKG / "libspecdec.so"
+ARCH = os.environ.get("SPECDEC_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # Keep the compiler from emitting packed fp32 VALU ops (v_pk_*_f32).
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = pathlib.Path(rocm) / "bin" / "hipcc"
+    return str(cand) if cand.exists() else "hipcc"
+
+
+def build_library(verbose: bool = True) -> pathlib.Path:
+    tmp = OUTPUT.with_suffix(".so.tmp")
+    cmd = [hipcc(), *FLAGS, f"-I{ROOT / 'include'}", *map(str, SOURCES), "-o", str(tmp)]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "packed-fp32-ops"   # the host pass does not know the device feature flag
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, OUTPUT)
+    return OUTPUT
+
+
+if __name__ == "__main__":
+    print(build_library())

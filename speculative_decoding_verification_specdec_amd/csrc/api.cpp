@@ -1,0 +1,134 @@
+// C ABI of the verify step (declared in include/specdec.h): host-side argument checks and
+// stream-ordered launches.  Allocates nothing, keeps no state, never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "kernels.h"
+#include "specdec.h"
+
+namespace {
+
+bool misaligned(const void* p, size_t a) {
+  return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0;
+}
+
+specdec_status check_sizes(int32_t B, int32_t K, int32_t V, int32_t dtype) {
+  if (B < 0 || K < 0 || K > SPECDEC_MAX_K || V < 1) return SPECDEC_ERR_SHAPE;
+  if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_ERR_DTYPE;
+  // B*(K+1)*V elements must be addressable with 64-bit signed offsets (always true for
+  // int32 sizes); keep the chunked work count in range as well.
+  const long long rows = static_cast<long long>(B) * (K + 1);
+  if (rows * specdec::num_chunks(V) > (1LL << 40)) return SPECDEC_ERR_SHAPE;
+  return SPECDEC_OK;
+}
+
+specdec_status run(const void* target_logits, int32_t logits_dtype, const float* draft_probs,
+                   const uint8_t* draft_onehot, const int32_t* proposed,
+                   const int32_t* num_draft, const float* temperature, const float* uniforms,
+                   int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                   float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
+                   const specdec_options* opts, bool greedy_all) {
+  specdec_status st = check_sizes(B, K, V, logits_dtype);
+  if (st != SPECDEC_OK) return st;
+  if (B == 0) return SPECDEC_OK;
+  if (!target_logits || !accept_len || !out_tokens || !workspace) return SPECDEC_ERR_NULL;
+  if (K > 0 && !proposed) return SPECDEC_ERR_NULL;
+  if (!greedy_all && (!temperature || !uniforms)) return SPECDEC_ERR_NULL;
+  const size_t esize = logits_dtype == SPECDEC_BF16 ? 2 : 4;
+  if (misaligned(target_logits, esize) || misaligned(draft_probs, 4) ||
+      misaligned(proposed, 4) || misaligned(num_draft, 4) || misaligned(temperature, 4) ||
+      misaligned(uniforms, 4) || misaligned(accept_len, 4) || misaligned(out_tokens, 4) ||
+      misaligned(out_probs, 4) || misaligned(workspace, 16))
+    return SPECDEC_ERR_ALIGN;
+  size_t off_p, off_s, off_c;
+  const size_t need = specdec::workspace_layout(B, K, V, &off_p, &off_s, &off_c);
+  if (workspace_bytes < need) return SPECDEC_ERR_WORKSPACE;
+
+  specdec::LaunchArgs a{};
+  a.logits = target_logits;
+  a.logits_bf16 = logits_dtype == SPECDEC_BF16;
+  a.draft_probs = greedy_all ? nullptr : draft_probs;
+  a.onehot = greedy_all ? nullptr : draft_onehot;
+  a.proposed = proposed;
+  a.num_draft = num_draft;
+  a.temperature = greedy_all ? nullptr : temperature;
+  a.uniforms = greedy_all ? nullptr : uniforms;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.greedy_all = greedy_all ? 1 : 0;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.out_probs = out_probs;
+  char* base = static_cast<char*>(workspace);
+  a.ws.partials = reinterpret_cast<specdec::RowPartial*>(base + off_p);
+  a.ws.states = reinterpret_cast<specdec::SeqState*>(base + off_s);
+  a.ws.sums = reinterpret_cast<specdec::ChunkSums*>(base + off_c);
+  a.stream = static_cast<hipStream_t>(stream);
+  a.hot_begin = opts ? static_cast<hipEvent_t>(opts->hot_event_begin) : nullptr;
+  a.hot_end = opts ? static_cast<hipEvent_t>(opts->hot_event_end) : nullptr;
+  return specdec::launch_verify(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V) {
+  if (check_sizes(B, K, V, SPECDEC_F32) != SPECDEC_OK || B == 0) return 0;
+  size_t a, b, c;
+  return specdec::workspace_layout(B, K, V, &a, &b, &c);
+}
+
+specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
+                              const float* draft_probs, const uint8_t* draft_onehot,
+                              const int32_t* proposed, const int32_t* num_draft,
+                              const float* temperature, const float* uniforms, int32_t B,
+                              int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                              float* out_probs, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return run(target_logits, logits_dtype, draft_probs, draft_onehot, proposed, num_draft,
+             temperature, uniforms, B, K, V, accept_len, out_tokens, out_probs, workspace,
+             workspace_bytes, stream, nullptr, false);
+}
+
+specdec_status specdec_verify_ex(const void* target_logits, int32_t logits_dtype,
+                                 const float* draft_probs, const uint8_t* draft_onehot,
+                                 const int32_t* proposed, const int32_t* num_draft,
+                                 const float* temperature, const float* uniforms, int32_t B,
+                                 int32_t K, int32_t V, int32_t* accept_len,
+                                 int32_t* out_tokens, float* out_probs, void* workspace,
+                                 size_t workspace_bytes, void* stream,
+                                 const specdec_options* opts) {
+  return run(target_logits, logits_dtype, draft_probs, draft_onehot, proposed, num_draft,
+             temperature, uniforms, B, K, V, accept_len, out_tokens, out_probs, workspace,
+             workspace_bytes, stream, opts, false);
+}
+
+specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_dtype,
+                                     const int32_t* proposed, const int32_t* num_draft,
+                                     int32_t B, int32_t K, int32_t V, int32_t* accept_len,
+                                     int32_t* out_tokens, float* out_probs, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return run(target_logits, logits_dtype, nullptr, nullptr, proposed, num_draft, nullptr,
+             nullptr, B, K, V, accept_len, out_tokens, out_probs, workspace, workspace_bytes,
+             stream, nullptr, true);
+}
+
+const char* specdec_status_string(int32_t status) {
+  switch (status) {
+    case SPECDEC_OK: return "ok";
+    case SPECDEC_ERR_NULL: return "a required pointer is NULL";
+    case SPECDEC_ERR_SHAPE: return "invalid sizes (B, K, V)";
+    case SPECDEC_ERR_DTYPE: return "unsupported logits dtype";
+    case SPECDEC_ERR_ALIGN: return "a tensor is not aligned to its element size";
+    case SPECDEC_ERR_WORKSPACE: return "workspace too small";
+    case SPECDEC_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t specdec_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the C-ABI host code (api.cpp) and the gfx950 kernels
+// (kernels.hip).  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specdec {
+
+constexpr int kThreads = 256;     // 4 x wave64 per workgroup
+constexpr int kChunk = 8192;      // logits per row chunk (statistics and sampling passes)
+constexpr int kGroup = 8;         // consecutive tokens per thread step of the sampling scan
+
+// Per (row, chunk) partial statistics of the streaming pass.
+struct RowPartial {
+  float m;      // max logit in the chunk (-inf if none)
+  float s;      // sum of exp2((z - m) * c) over the chunk
+  int32_t arg;  // lowest index attaining m (greedy rows only)
+  int32_t pad;
+};
+
+// What the sampling passes must draw for one sequence.
+enum SampleMode : int32_t {
+  kNone = 0,          // nothing to draw (greedy, invalid, or already emitted)
+  kResidual = 1,      // max(0, p_j - q_j) for a model-draft row
+  kResidualOnehot = 2,// p_j with the rejected draft x_j removed (one-hot / n-gram row)
+  kBonus = 3,         // p_k (every draft accepted)
+};
+
+struct SeqState {
+  int32_t mode;   // SampleMode
+  int32_t row;    // target row j the draw is taken from
+  int32_t excl;   // x_j for kResidualOnehot
+  int32_t pad0;
+  float c;        // log2(e) / T
+  float m;        // max of row j
+  float s;        // sum_v exp2((z_j[v] - m) * c) of row j
+  float pad1;
+};
+
+struct ChunkSums {
+  double w;       // sum of the draw's weights over the chunk
+  double e;       // sum of exp2((z - m) * c) over the chunk (fallback when the residual is empty)
+};
+
+struct Workspace {
+  RowPartial* partials;  // [B*(K+1)*S]
+  SeqState* states;      // [B]
+  ChunkSums* sums;       // [B*S]
+};
+
+inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Byte layout of the caller's workspace; returns the total (0 on overflow).
+size_t workspace_layout(int B, int K, int V, size_t* off_partials, size_t* off_states,
+                        size_t* off_sums);
+
+struct LaunchArgs {
+  const void* logits;
+  int logits_bf16;           // 1: bf16 bit patterns, 0: fp32
+  const float* draft_probs;
+  const uint8_t* onehot;
+  const int32_t* proposed;
+  const int32_t* num_draft;
+  const float* temperature;
+  const float* uniforms;
+  int B, K, V;
+  int greedy_all;            // 1: every row is temperature 0 (no q, T, u read)
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* out_probs;
+  Workspace ws;
+  hipStream_t stream;
+  hipEvent_t hot_begin;      // optional, recorded around the streaming row-statistics kernel
+  hipEvent_t hot_end;
+};
+
+hipError_t launch_verify(const LaunchArgs& a);
+
+}  // namespace specdec
