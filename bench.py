@@ -55,6 +55,38 @@ def measured_traffic(bytes_alg_per_launch: float):
     return float(t.group(1))
 
 
+class HipEvents:
+    """Raw hipEvent_t pairs from the HIP runtime (handed to the library, which records them on
+    the kernel's own stream)."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = [(self._make(), self._make()) for _ in range(n)]
+
+    def _make(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), *self.pairs[i]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed (event not recorded?)")
+        return ms.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
 def cpu_baseline(inp, budget_s: float = 12.0):
     """The fp64 oracle (as it stands) on the same inputs: whole batches, repeated until about
     ``budget_s`` of single-core CPU work has run."""
@@ -97,6 +129,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 20 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verify step shards by sequence with no "
@@ -112,49 +146,89 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate the
+        # hot kernel's (bytes read = bytes written = MIB MiB per copy).
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 20}))
+        return
+    from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
+
     print("[bench] generating the B=64 V=128256 k=5 batch", file=sys.stderr, flush=True)
     inp = batch64()
-    reps = [inputs_to_device(inp, dev) for _ in range(args.replicas)]
     B, K, V = inp.B, inp.K, inp.V
     ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     prb = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
-    out = (acc, tok, prb)
-    stream = torch.cuda.current_stream()
-
-    def step(i, hot=None):
-        d = reps[i % len(reps)]
-        specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
-                       d["uniforms"], draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
-                       out=out, workspace=ws, stream=stream, hot_events=hot)
+    calls = []
+    for _ in range(args.replicas):
+        d = inputs_to_device(inp, dev)
+        calls.append(PreparedVerify(d["logits"], d["draft_probs"], d["proposed"],
+                                    d["temperature"], d["uniforms"],
+                                    draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
+                                    out=(acc, tok, prb), workspace=ws))
+    R = len(calls)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
 
     print(f"[bench] warmup {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            calls[i % R]()
+    torch.cuda.synchronize()
+
+    # One HIP graph holds R consecutive steps (one per input replica); a second holds the
+    # remainder, so the timed region replays exactly `steps` steps with no host launch gaps.
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                calls[i % R]()
+        return g
+    full, rem = divmod(args.steps, R)
+    g_full = capture(R) if full else None
+    g_rem = capture(rem) if rem else None
+    torch.cuda.synchronize()
+    if g_full is not None:
+        g_full.replay()                      # one untimed replay of each graph
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` whole steps, bracketed by synchronisation and HIP events.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
 
-    # Same loop again with HIP events around the streaming row-statistics kernel of each step.
-    hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The same steps launched eagerly, with HIP events recorded by the library around the
+    # streaming row-statistics kernel of each step.  A spin kernel in front lets the host
+    # queue every launch before the GPU reaches them, so the events bracket kernel time only.
+    hot = HipEvents(args.steps)
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, hot=hot[i])
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2e8))
+        for i in range(args.steps):
+            calls[i % R](hot_events=hot.pairs[i])
     torch.cuda.synchronize()
-    hot_ms = sum(b.elapsed_time(e) for b, e in hot) / args.steps
+    hot_ms = sum(hot.elapsed_ms(i) for i in range(args.steps)) / args.steps
+    hot.close()
 
     acc_np = acc.cpu().numpy()
     assert (acc_np >= 0).all(), "invalid rows in the benchmark batch"

@@ -125,7 +125,7 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     fp32, draft_onehot [B] uint8 or None, num_draft [B] int32 or None.  Returns
     (accept_len [B] int32, out_tokens [B, K+1] int32, out_probs [B, K+1] fp32 or None),
     enqueued on ``stream`` (default: torch's current stream) without synchronising.
-    ``hot_events``: optional (begin, end) torch.cuda.Event pair recorded around the
+    ``hot_events``: optional (begin, end) pair of hipEvent_t handles (ints) recorded around the
     streaming logit-row kernel."""
     lib = load_library()
     if target_logits.dim() != 3:
@@ -155,8 +155,8 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     if hot_events is None:
         status = lib.specdec_verify(*args)
     else:
-        opts = _Options(ctypes.c_void_p(hot_events[0].cuda_event if hot_events[0] is not None else 0),
-                        ctypes.c_void_p(hot_events[1].cuda_event if hot_events[1] is not None else 0))
+        opts = _Options(*(e if isinstance(e, int) or e is None else e.cuda_event
+                          for e in hot_events))
         status = lib.specdec_verify_ex(*args, ctypes.byref(opts))
     _raise(status, "specdec_verify")
     return acc, tok, prb
@@ -210,3 +210,43 @@ def inputs_to_device(inp, device) -> dict:
     return dict(logits=logits, draft_probs=dev(inp.draft_probs), draft_onehot=dev(inp.draft_onehot),
                 proposed=dev(inp.proposed), num_draft=dev(inp.num_draft),
                 temperature=dev(inp.temperature), uniforms=dev(inp.uniforms))
+
+
+class PreparedVerify:
+    """A specdec_verify call with its arguments marshalled once (for tight loops and HIP-graph
+    capture).  ``__call__(stream=None, hot_events=None)`` enqueues it on ``stream`` (default:
+    torch's current stream) and raises on a non-zero status."""
+
+    def __init__(self, target_logits, draft_probs, proposed, temperature, uniforms, *,
+                 draft_onehot=None, num_draft=None, out=None, workspace=None):
+        # Validate once through the checked entry point's rules.
+        B, K1, V = (int(s) for s in target_logits.shape)
+        dev = target_logits.device
+        self.lib = load_library()
+        self.keep = (target_logits, draft_probs, proposed, temperature, uniforms, draft_onehot,
+                     num_draft)
+        dt = SPECDEC_BF16 if target_logits.dtype == torch.bfloat16 else SPECDEC_F32
+        _check(draft_probs, "draft_probs", torch.float32, (B, K1 - 1, V), dev, optional=True)
+        _check(proposed, "proposed", torch.int32, (B, K1 - 1), dev, optional=(K1 == 1))
+        _check(temperature, "temperature", torch.float32, (B,), dev)
+        _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
+        _check(draft_onehot, "draft_onehot", torch.uint8, (B,), dev, optional=True)
+        _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
+        self.out = _outputs(B, K1 - 1, dev, out, True)
+        self.ws, _ = _workspace(B, K1 - 1, V, dev, workspace)
+        acc, tok, prb = self.out
+        self.args = (_ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_onehot),
+                     _ptr(proposed), _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B,
+                     K1 - 1, V, _ptr(acc), _ptr(tok), _ptr(prb), _ptr(self.ws), self.ws.numel())
+
+    def __call__(self, stream=None, hot_events=None):
+        s = _stream_handle(stream)
+        if hot_events is None:
+            status = self.lib.specdec_verify(*self.args, s)
+        else:
+            opts = _Options(*(e if isinstance(e, int) or e is None else e.cuda_event
+                              for e in hot_events))
+            status = self.lib.specdec_verify_ex(*self.args, s, ctypes.byref(opts))
+        if status != 0:
+            _raise(status, "specdec_verify")
+        return self.out
