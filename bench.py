@@ -30,8 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "verified draft positions/sec and HBM GB/s (% of peak), B=64 V=128256 k=5"
 HBM_PEAK_GBS = 8000.0
-HOT_KERNEL = "row_stats_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_kernel_batch64_counters.txt")
+HOT_KERNEL = "stats_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_kernel_batch64_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_verification_specdec_amd", "csrc",
                              "kernels.hip")
 
@@ -162,7 +162,7 @@ def main():
     print("[bench] generating the B=64 V=128256 k=5 batch", file=sys.stderr, flush=True)
     inp = batch64()
     B, K, V = inp.B, inp.K, inp.V
-    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     prb = torch.empty((B, K + 1), dtype=torch.float32, device=dev)

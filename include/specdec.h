@@ -59,7 +59,8 @@ extern "C" {
 typedef enum {
   SPECDEC_OK = 0,
   SPECDEC_ERR_NULL = -1,      /* a required pointer is NULL                               */
-  SPECDEC_ERR_SHAPE = -2,     /* B < 0, K < 0, K > SPECDEC_MAX_K, V < 1, or sizes overflow */
+  SPECDEC_ERR_SHAPE = -2,     /* B < 0, K < 0, K > SPECDEC_MAX_K, V < 1, or                */
+                              /* B*(K+1)*ceil(V/8192) >= 2^31                               */
   SPECDEC_ERR_DTYPE = -3,     /* logits_dtype is not a specdec_dtype                      */
   SPECDEC_ERR_ALIGN = -4,     /* a tensor base is not aligned to its element size         */
   SPECDEC_ERR_WORKSPACE = -5, /* workspace NULL or smaller than specdec_workspace_size()  */
@@ -75,9 +76,10 @@ typedef enum {
 #define SPECDEC_TEMPERATURE_MIN 1e-6f     /* smallest non-zero temperature accepted       */
 
 /* Bytes of device workspace specdec_verify / specdec_verify_greedy need for these sizes
- * (a pure function of B, K, V; 0 for B == 0).  The workspace holds per-row partial
- * statistics and per-sequence sampling state; its contents need no initialisation and
- * are meaningless after the call.  Returns 0 for invalid sizes. */
+ * (a pure function of B, K, V; 0 for B == 0 or invalid sizes).  The workspace holds
+ * per-row partial statistics, per-sequence draw state and per-segment weight sums; it needs
+ * no initialisation and its contents are meaningless after the call.  Calls that overlap
+ * in time (different streams) need separate workspaces. */
 size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V);
 
 /* Batched rejection-sampling verify (sampled and greedy rows mixed by temperature).
@@ -123,10 +125,10 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
                                      int32_t* accept_len, int32_t* out_tokens, float* out_probs,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Measurement hook: HIP events (hipEvent_t, host handles) recorded on `stream` immediately
- * before and after the streaming logit-row kernel (the one that reads every target row).
- * Either may be NULL.  Passing opts == NULL to specdec_verify_ex is the same as
- * specdec_verify. */
+/* Measurement hook: HIP events (hipEvent_t, host handles) recorded by the dispatch of the
+ * streaming logit-row kernel (the one that reads every target row) when it starts and when it
+ * completes, so hipEventElapsedTime gives that kernel's own duration.  Either may be NULL.
+ * Passing opts == NULL to specdec_verify_ex is the same as specdec_verify. */
 typedef struct {
   void* hot_event_begin;
   void* hot_event_end;

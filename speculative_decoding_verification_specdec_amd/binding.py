@@ -106,7 +106,8 @@ def _outputs(B, K, device, out, want_probs):
 def _workspace(B, K, V, device, workspace):
     need = specdec_workspace_size(B, K, V)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        # Zero-filled once: the library's arrival counters start at zero and are left zero.
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
     return workspace, need
 
 

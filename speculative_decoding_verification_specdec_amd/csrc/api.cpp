@@ -18,8 +18,9 @@ specdec_status check_sizes(int32_t B, int32_t K, int32_t V, int32_t dtype) {
   if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_ERR_DTYPE;
   // B*(K+1)*V elements must be addressable with 64-bit signed offsets (always true for
   // int32 sizes); keep the chunked work count in range as well.
+  // Tile counts (rows x 8192-logit chunks) are indexed with 32-bit arithmetic on the device.
   const long long rows = static_cast<long long>(B) * (K + 1);
-  if (rows * specdec::num_chunks(V) > (1LL << 40)) return SPECDEC_ERR_SHAPE;
+  if (rows * specdec::num_chunks(V) >= (1LL << 31)) return SPECDEC_ERR_SHAPE;
   return SPECDEC_OK;
 }
 
@@ -41,9 +42,8 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
       misaligned(uniforms, 4) || misaligned(accept_len, 4) || misaligned(out_tokens, 4) ||
       misaligned(out_probs, 4) || misaligned(workspace, 16))
     return SPECDEC_ERR_ALIGN;
-  size_t off_p, off_s, off_c;
-  const size_t need = specdec::workspace_layout(B, K, V, &off_p, &off_s, &off_c);
-  if (workspace_bytes < need) return SPECDEC_ERR_WORKSPACE;
+  const specdec::WorkspaceLayout L = specdec::workspace_layout(B, K, V);
+  if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE;
 
   specdec::LaunchArgs a{};
   a.logits = target_logits;
@@ -62,9 +62,9 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.out_tokens = out_tokens;
   a.out_probs = out_probs;
   char* base = static_cast<char*>(workspace);
-  a.ws.partials = reinterpret_cast<specdec::RowPartial*>(base + off_p);
-  a.ws.states = reinterpret_cast<specdec::SeqState*>(base + off_s);
-  a.ws.sums = reinterpret_cast<specdec::ChunkSums*>(base + off_c);
+  a.ws.partials = reinterpret_cast<specdec::RowPartial*>(base + L.partials);
+  a.ws.states = reinterpret_cast<specdec::SeqState*>(base + L.states);
+  a.ws.segs = reinterpret_cast<specdec::SegSums*>(base + L.segs);
   a.stream = static_cast<hipStream_t>(stream);
   a.hot_begin = opts ? static_cast<hipEvent_t>(opts->hot_event_begin) : nullptr;
   a.hot_end = opts ? static_cast<hipEvent_t>(opts->hot_event_end) : nullptr;
@@ -77,8 +77,7 @@ extern "C" {
 
 size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V) {
   if (check_sizes(B, K, V, SPECDEC_F32) != SPECDEC_OK || B == 0) return 0;
-  size_t a, b, c;
-  return specdec::workspace_layout(B, K, V, &a, &b, &c);
+  return specdec::workspace_layout(B, K, V).total;
 }
 
 specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,

@@ -8,24 +8,26 @@
 
 namespace specdec {
 
-constexpr int kThreads = 256;     // 4 x wave64 per workgroup
-constexpr int kChunk = 8192;      // logits per row chunk (statistics and sampling passes)
-constexpr int kGroup = 8;         // consecutive tokens per thread step of the sampling scan
+constexpr int kThreads = 256;               // 4 x wave64 per workgroup
+constexpr int kChunk = 8192;                // logits per row chunk (one workgroup tile)
+constexpr int kGroup = 8;                   // consecutive tokens per thread in the draw passes
+constexpr int kSeg = kThreads * kGroup;     // 2048 tokens per draw segment
+constexpr int kSegPerChunk = kChunk / kSeg; // 4
 
-// Per (row, chunk) partial statistics of the streaming pass.
+// Per (row, 2048-token sub-chunk) partial statistics of the streaming pass.
 struct RowPartial {
-  float m;      // max logit in the chunk (-inf if none)
-  float s;      // sum of exp2((z - m) * c) over the chunk
+  float m;      // max logit in the sub-chunk (-inf if none)
+  float s;      // sum of exp2((z - m) * c) over the sub-chunk
   int32_t arg;  // lowest index attaining m (greedy rows only)
   int32_t pad;
 };
 
-// What the sampling passes must draw for one sequence.
+// What the draw pass must sample for one sequence.
 enum SampleMode : int32_t {
-  kNone = 0,          // nothing to draw (greedy, invalid, or already emitted)
-  kResidual = 1,      // max(0, p_j - q_j) for a model-draft row
-  kResidualOnehot = 2,// p_j with the rejected draft x_j removed (one-hot / n-gram row)
-  kBonus = 3,         // p_k (every draft accepted)
+  kNone = 0,            // nothing to draw (greedy, invalid, or already emitted)
+  kResidual = 1,        // max(0, p_j - q_j) for a model-draft row
+  kResidualOnehot = 2,  // p_j with the rejected draft x_j removed (one-hot / n-gram row)
+  kBonus = 3,           // p_k (every draft accepted)
 };
 
 struct SeqState {
@@ -39,22 +41,28 @@ struct SeqState {
   float pad1;
 };
 
-struct ChunkSums {
-  double w;       // sum of the draw's weights over the chunk
-  double e;       // sum of exp2((z - m) * c) over the chunk (fallback when the residual is empty)
+// Weight sums of one 2048-token draw segment.
+struct SegSums {
+  double w;       // the draw's weights
+  double e;       // exp2((z - m) * c), i.e. s * p (fallback when the residual is empty)
 };
 
+// Caller-provided device workspace (no initialisation needed; contents are meaningless
+// between calls).
 struct Workspace {
-  RowPartial* partials;  // [B*(K+1)*S]
+  RowPartial* partials;  // [B*(K+1)*S*4], 4 sub-chunks per chunk
   SeqState* states;      // [B]
-  ChunkSums* sums;       // [B*S]
+  SegSums* segs;         // [B*S*kSegPerChunk]
 };
 
 inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
-// Byte layout of the caller's workspace; returns the total (0 on overflow).
-size_t workspace_layout(int B, int K, int V, size_t* off_partials, size_t* off_states,
-                        size_t* off_sums);
+struct WorkspaceLayout {
+  size_t partials, states, segs, total;
+};
+
+// Byte layout of the caller's workspace for these sizes.
+WorkspaceLayout workspace_layout(int B, int K, int V);
 
 struct LaunchArgs {
   const void* logits;
@@ -72,7 +80,7 @@ struct LaunchArgs {
   float* out_probs;
   Workspace ws;
   hipStream_t stream;
-  hipEvent_t hot_begin;      // optional, recorded around the streaming row-statistics kernel
+  hipEvent_t hot_begin;      // optional, recorded around the streaming kernel
   hipEvent_t hot_end;
 };
 

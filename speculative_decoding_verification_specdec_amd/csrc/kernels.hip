@@ -6,24 +6,27 @@
 // the result is exactly the target model"; "Speculative decoding: el secretario que adelanta
 // lo que va a decir el jefe" (blog.lo0.es), section "El mecanismo desnudo".
 //
-// Four kernels, enqueued back to back on the caller's stream:
-//   1. row_stats     streams every used target logit row once (the HBM-bound pass) and
-//                    writes, per (row, 8192-logit chunk), the chunk max m, the sum of
-//                    exp2((z - m) * log2(e)/T) and, for greedy rows, the lowest argmax.
-//   2. accept        one wave64 per sequence: merges the chunk partials of its rows in chunk
-//                    order, gathers p_i(x_i) (fp64) and q_i(x_i), runs the accept tests as one
-//                    64-bit ballot, finds the first rejection and emits every token whose value
-//                    is already known (accepted drafts, greedy argmaxes).
-//   3. sample_sums   for each sequence that still needs a draw, the sum of the draw's weights
-//                    (residual max(0, p - q), p without x, or p) per chunk of its one row.
-//   4. sample_pick   one workgroup per sequence: picks the chunk holding u * total from the
-//                    chunk sums, then scans that chunk in ascending token order (per-thread
-//                    8-token groups, fp64 workgroup prefix scan) to the first running sum
-//                    above u * total.
-// All reductions combine in a fixed order, so results are bit-reproducible; no atomics.
+// Four kernels, enqueued back to back on the caller's stream.  They communicate only through
+// the workspace across kernel boundaries: no atomics, no inter-workgroup waiting.
+//   stats_kernel   one 256-thread workgroup per (used target row, 8192-logit chunk).  Issues
+//       the chunk's 16-byte loads first, then folds them into (max, sum of
+//       exp2((z - max) * log2(e)/T), lowest argmax) and writes the chunk partial.
+//   accept_kernel  one wave64 per sequence, lane i <-> target row i: merges row i's chunk
+//       partials in chunk order, gathers p_i(x_i) (fp64) and q_i(x_i), and a 64-bit ballot
+//       finds the first rejection.  Emits every token already known (accepted drafts, greedy
+//       argmaxes) and records what remains to be drawn.
+//   draw_sums_kernel  one workgroup per (sequence that needs a draw, chunk of the row to draw
+//       from): sums the draw's weights -- s * max(0, p - q), p without the rejected draft, or
+//       p -- over each 2048-token segment of the chunk.
+//   pick_kernel  one workgroup per sequence that needs a draw: scans the segment sums (fp64)
+//       to the segment holding u * total, then scans that one segment in ascending token
+//       order to the first running sum above u * total.
+// Every reduction combines in a fixed order, so results are bit-reproducible.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
+
+#include <hip/hip_ext.h>
 
 #include "kernels.h"
 
@@ -33,6 +36,8 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kTempMin = 1e-6f;
 constexpr int kWaves = kThreads / 64;
+constexpr int kSub = kChunk / kWaves;          // tokens per wave sub-chunk (2048)
+constexpr int kPerThread = kSub / 64;          // logits per lane per sub-chunk (32)
 
 __device__ __forceinline__ bool temp_valid(float T) {
   return T == 0.f || (T >= kTempMin && T <= FLT_MAX);
@@ -45,17 +50,25 @@ __device__ __forceinline__ float load_logit(const uint16_t* p, long long i) {
 }
 __device__ __forceinline__ float load_logit(const float* p, long long i) { return p[i]; }
 
-// 16-byte vector -> floats.
-__device__ __forceinline__ void unpack(const uint4& d, float (&o)[8], const uint16_t*) {
+// 16-byte vector -> floats (bf16: shift / mask into the upper half of a binary32).
+__device__ __forceinline__ void unpack(const uint4& d, float* o, const uint16_t*) {
   o[0] = __uint_as_float(d.x << 16); o[1] = __uint_as_float(d.x & 0xffff0000u);
   o[2] = __uint_as_float(d.y << 16); o[3] = __uint_as_float(d.y & 0xffff0000u);
   o[4] = __uint_as_float(d.z << 16); o[5] = __uint_as_float(d.z & 0xffff0000u);
   o[6] = __uint_as_float(d.w << 16); o[7] = __uint_as_float(d.w & 0xffff0000u);
 }
-__device__ __forceinline__ void unpack(const uint4& d, float (&o)[4], const float*) {
+__device__ __forceinline__ void unpack(const uint4& d, float* o, const float*) {
   o[0] = __uint_as_float(d.x); o[1] = __uint_as_float(d.y);
   o[2] = __uint_as_float(d.z); o[3] = __uint_as_float(d.w);
 }
+// 16-byte streaming load: every logit and draft probability is read once per call, so the
+// loads carry the nontemporal hint.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const void* p) {
+  const u32x4 t = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 template <typename LT> struct Vec;
 template <> struct Vec<uint16_t> {
   static constexpr int kPer = 8;
@@ -81,34 +94,10 @@ __device__ __forceinline__ Stat merge(const Stat& x, const Stat& y, float c) {
     r.a = min(x.a, y.a);
     return r;
   }
-  r.s = x.s * exp2f((x.m - r.m) * c) + y.s * exp2f((y.m - r.m) * c);
+  r.s = x.s * __builtin_amdgcn_exp2f((x.m - r.m) * c) +
+        y.s * __builtin_amdgcn_exp2f((y.m - r.m) * c);
   r.a = (y.m > x.m || (y.m == x.m && y.a < x.a)) ? y.a : x.a;
   return r;
-}
-
-// Fold a block of logits (in ascending index order) into the running statistics.  `idx(j)`
-// gives the token index of element j; it is only evaluated for greedy rows.
-template <int N, typename IdxFn>
-__device__ __forceinline__ void fold_block(const float (&x)[N], float c, bool want_arg, Stat& st,
-                                           IdxFn idx) {
-  float bm = x[0];
-#pragma unroll
-  for (int j = 1; j < N; ++j) bm = fmaxf(bm, x[j]);
-  if (bm > st.m) {  // strictly greater keeps the earlier (lower-index) maximum
-    st.s *= exp2f((st.m - bm) * c);
-    if (want_arg) {
-      int a = INT_MAX;
-#pragma unroll
-      for (int j = N - 1; j >= 0; --j)
-        if (x[j] == bm) a = idx(j);
-      st.a = a;
-    }
-    st.m = bm;
-  }
-  // A history of only -inf (or NaN) keeps the reference at 0 so -inf maps to exp2(-inf) = 0.
-  const float ref = (st.m == -INFINITY) ? 0.f : st.m;
-#pragma unroll
-  for (int j = 0; j < N; ++j) st.s += __builtin_amdgcn_exp2f((x[j] - ref) * c);
 }
 
 __device__ __forceinline__ Stat wave_reduce(Stat v, float c) {
@@ -123,82 +112,269 @@ __device__ __forceinline__ Stat wave_reduce(Stat v, float c) {
   return v;
 }
 
+// All-reduce of a Stat over each 16-lane row of the wave with DPP (quad_perm xor 1, xor 2,
+// then row_ror 4, 8): no LDS traffic.  Every lane of a row ends with its row's result; lane
+// 16k + 0 is read, so the merge order is fixed.
+template <int kCtrl>
+__device__ __forceinline__ Stat dpp_stat(const Stat& v) {
+  return Stat{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.m), kCtrl, 0xf, 0xf, false)),
+              __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.s), kCtrl, 0xf, 0xf, false)),
+              __builtin_amdgcn_update_dpp(0, v.a, kCtrl, 0xf, 0xf, false)};
+}
+
+__device__ __forceinline__ Stat row16_reduce(Stat v, float c) {
+  v = merge(v, dpp_stat<0xB1>(v), c);   // quad_perm [1,0,3,2]
+  v = merge(v, dpp_stat<0x4E>(v), c);   // quad_perm [2,3,0,1]
+  v = merge(v, dpp_stat<0x124>(v), c);  // row_ror:4
+  v = merge(v, dpp_stat<0x128>(v), c);  // row_ror:8
+  return v;
+}
+
 // ------------------------------------------------------------------------------------------
-// 1. Streaming row statistics.
+// Streaming statistics of one chunk: (max, sum of exp2((z - max) * c)) of the thread's
+// kPerThread logits.
 // ------------------------------------------------------------------------------------------
+struct MaxSum {
+  float m;
+  float s;
+};
+
+__device__ __forceinline__ MaxSum merge_ms(const MaxSum& x, const MaxSum& y, float c) {
+  const float m = fmaxf(x.m, y.m);
+  if (m == -INFINITY) return MaxSum{m, x.s + y.s};  // both empty: sums are 0 (NaN stays NaN)
+  return MaxSum{m, x.s * __builtin_amdgcn_exp2f((x.m - m) * c) +
+                       y.s * __builtin_amdgcn_exp2f((y.m - m) * c)};
+}
+
+__device__ __forceinline__ MaxSum fold_chunk(const float (&x)[kPerThread], float c) {
+  float bm = x[0];
+#pragma unroll
+  for (int j = 1; j < kPerThread; ++j) bm = fmaxf(bm, x[j]);
+  // exp2((x - ref) * c) as exp2(fma(x, c, -hi)) * exp2(-lo) with ref * c = hi + lo exactly:
+  // one fma per logit, and the exponent is exact up to the fma's single rounding.  An all
+  // -inf (or NaN) chunk keeps the reference at 0 so -inf maps to exp2(-inf) = 0; NaN and
+  // +inf logits make the sum NaN, which marks the row invalid.
+  const float ref = (bm == -INFINITY) ? 0.f : bm;
+  const float hi = ref * c;
+  const float lo = fmaf(ref, c, -hi);
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPerThread; j += 4) {
+    s0 += __builtin_amdgcn_exp2f(fmaf(x[j], c, -hi));
+    s1 += __builtin_amdgcn_exp2f(fmaf(x[j + 1], c, -hi));
+    s2 += __builtin_amdgcn_exp2f(fmaf(x[j + 2], c, -hi));
+    s3 += __builtin_amdgcn_exp2f(fmaf(x[j + 3], c, -hi));
+  }
+  return MaxSum{bm, ((s0 + s1) + (s2 + s3)) * __builtin_amdgcn_exp2f(-lo)};
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Load one lane's logits of the wave's sub-chunk [c0, c0 + n) (n <= kSub, possibly <= 0):
+// 16-byte vectors u * 64 + lane (scalar path: tokens u * 64 + lane), all issued before any
+// value is used.  Slots past n read as -inf.
 template <typename LT, bool kVec>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(
-    const LT* __restrict__ logits, const int32_t* __restrict__ num_draft,
-    const float* __restrict__ temperature, int B, int K, int V, int S, int greedy_all,
-    RowPartial* __restrict__ partials) {
-  __shared__ Stat red[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long total = static_cast<long long>(B) * (K + 1) * S;
-  for (long long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int s = static_cast<int>(w % S);
-    const long long r = w / S;
-    const int b = static_cast<int>(r / (K + 1)), i = static_cast<int>(r % (K + 1));
-    const int kb = num_draft ? num_draft[b] : K;
-    const float T = greedy_all ? 0.f : temperature[b];
-    if (kb < 0 || kb > K || i > kb || !temp_valid(T)) continue;  // padded or invalid: unread
-    const bool want_arg = (T == 0.f);
-    const float c = temp_scale(T);
-    const LT* row = logits + r * static_cast<long long>(V);
-    const int c0 = s * kChunk;
-    const int n = min(kChunk, V - c0);
-    Stat st{-INFINITY, 0.f, INT_MAX};
-    if constexpr (kVec) {
-      constexpr int P = Vec<LT>::kPer;
-      constexpr int U = 4;  // 16-byte loads in flight per thread
-      const uint4* vrow = reinterpret_cast<const uint4*>(row + c0);
-      const int nvec = n / P;
-      for (int v0 = 0; v0 < nvec; v0 += U * kThreads) {
-        uint4 d[U];
+__device__ __forceinline__ void load_sub(const LT* __restrict__ row, int c0, int n, int lane,
+                                         float (&x)[kPerThread]) {
+  if constexpr (kVec) {
+    constexpr int P = Vec<LT>::kPer;
+    constexpr int U = kPerThread / P;
+    const uint4* vrow = reinterpret_cast<const uint4*>(row + c0);
+    const int nvec = n / P;
+    uint4 d[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int vi = v0 + u * kThreads + tid;
-          constexpr uint32_t ni = Vec<LT>::kNegInf;
-          d[u] = vi < nvec ? vrow[vi] : make_uint4(ni, ni, ni, ni);
-        }
-        float x[U * P];
+    for (int u = 0; u < U; ++u) {
+      const int vi = u * 64 + lane;
+      constexpr uint32_t ni = Vec<LT>::kNegInf;
+      d[u] = vi < nvec ? stream_load(vrow + vi) : make_uint4(ni, ni, ni, ni);
+    }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float t[P];
-          unpack(d[u], t, static_cast<const LT*>(nullptr));
+    for (int u = 0; u < U; ++u) unpack(d[u], &x[u * P], static_cast<const LT*>(nullptr));
+  } else {
 #pragma unroll
-          for (int e = 0; e < P; ++e) x[u * P + e] = t[e];
-        }
-        fold_block(x, c, want_arg, st, [&](int j) {
-          return c0 + (v0 + (j / P) * kThreads + tid) * P + (j % P);
-        });
+    for (int j = 0; j < kPerThread; ++j) {
+      const int vi = j * 64 + lane;
+      x[j] = vi < n ? load_logit(row, c0 + vi) : -INFINITY;
+    }
+  }
+}
+
+template <typename LT, bool kVec>
+__device__ __forceinline__ int tok_of(int c0, int lane, int j) {
+  if constexpr (kVec) {
+    constexpr int P = Vec<LT>::kPer;
+    return c0 + ((j / P) * 64 + lane) * P + (j % P);
+  } else {
+    return c0 + j * 64 + lane;
+  }
+}
+
+__device__ void write_invalid(int b, int lane, int K, int32_t* accept_len, int32_t* out_tokens,
+                              float* out_probs, SeqState* states) {
+  const long long row0 = static_cast<long long>(b) * (K + 1);
+  if (lane <= K) {
+    out_tokens[row0 + lane] = -1;
+    if (out_probs) out_probs[row0 + lane] = 0.f;
+  }
+  if (lane == 0) {
+    accept_len[b] = -1;
+    states[b] = SeqState{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Accept scan of sequence b by one wave64 (lane i <-> target row i); kb and T are valid.
+template <typename LT>
+__device__ void accept_sequence(const LT* logits, const float* draft_probs,
+                                const uint8_t* onehot, const int32_t* proposed,
+                                const float* uniforms, int b, int kb, float T, int K, int V,
+                                int S, const RowPartial* partials, int32_t* accept_len,
+                                int32_t* out_tokens, float* out_probs, SeqState* states,
+                                int lane) {
+  const bool greedy = (T == 0.f);
+  const bool is_onehot = !greedy && onehot != nullptr && onehot[b] != 0;
+  const float c = temp_scale(T);
+  const long long row0 = static_cast<long long>(b) * (K + 1);
+  // Independent loads first: the draft id, its logit and q, the uniform.
+  const bool drafted = lane < kb;
+  const int x = drafted ? proposed[static_cast<long long>(b) * K + lane] : -1;
+  const bool x_ok = x >= 0 && x < V;
+  const float u = (drafted && !greedy) ? uniforms[row0 + lane] : 0.f;
+  const double zx = (drafted && x_ok) ? static_cast<double>(load_logit(logits, (row0 + lane) * V + x))
+                                      : 0.0;
+  const bool model_q = drafted && x_ok && !greedy && !is_onehot && draft_probs != nullptr;
+  const float qf = model_q ? draft_probs[(static_cast<long long>(b) * K + lane) * V + x] : 1.f;
+  // Row statistics: four rows per pass, sixteen lanes per row.  Lane l of a row merges the
+  // row's sub-chunk partials l, l + 16, ... in order, the row's lanes all-reduce with DPP, and
+  // lane i keeps row i's result (taken from the row's lane 0).
+  Stat st{-INFINITY, 0.f, INT_MAX};
+  const int nsub = S * kWaves;
+  const int per_lane = (nsub + 15) / 16;
+  for (int i0 = 0; i0 <= kb; i0 += 4) {
+    const int ri = i0 + (lane >> 4), sl = lane & 15;
+    Stat v{-INFINITY, 0.f, INT_MAX};
+    const RowPartial* P = partials + (row0 + ri) * nsub;
+    for (int t0 = 0; t0 < per_lane; t0 += 8) {
+      RowPartial pb[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int j = sl + 16 * (t0 + t);
+        pb[t] = (ri <= kb && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0};
       }
-    } else {
-      constexpr int U = 8;
-      for (int v0 = 0; v0 < n; v0 += U * kThreads) {
-        float x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int vi = v0 + u * kThreads + tid;
-          x[u] = vi < n ? load_logit(row, c0 + vi) : -INFINITY;
+      for (int t = 0; t < 8; ++t) v = merge(v, Stat{pb[t].m, pb[t].s, pb[t].arg}, c);
+    }
+    v = row16_reduce(v, c);
+    const int src = ((lane - i0) & 3) * 16;
+    const Stat got{__shfl(v.m, src, 64), __shfl(v.s, src, 64), __shfl(v.a, src, 64)};
+    if (lane >= i0 && lane < i0 + 4) st = got;
+  }
+  bool lane_ok = true;
+  double px = 0.0;
+  bool acc = true;
+  if (lane <= kb) {
+    lane_ok = st.s > 0.f;  // NaN / +inf logit -> NaN; all -inf -> 0
+    if (drafted) {
+      if (!x_ok) {
+        lane_ok = false;
+      } else {
+        px = exp2((zx - static_cast<double>(st.m)) * static_cast<double>(c)) /
+             static_cast<double>(st.s);
+        if (greedy) {
+          acc = (x == st.a);
+        } else {
+          if (!(u >= 0.f && u < 1.f)) lane_ok = false;
+          double qx = 1.0;  // one-hot drafter: q(x) = 1
+          if (!is_onehot) {
+            if (draft_probs == nullptr) lane_ok = false;
+            else if (!(qf >= 0.f && qf <= FLT_MAX)) lane_ok = false;
+            qx = qf;
+          }
+          acc = static_cast<double>(u) * qx < px;
         }
-        fold_block(x, c, want_arg, st, [&](int j) { return c0 + v0 + j * kThreads + tid; });
       }
     }
-    st = wave_reduce(st, c);
-    if (lane == 0) red[wave] = st;
-    __syncthreads();
-    if (tid == 0) {
-      Stat acc = red[0];
-#pragma unroll
-      for (int k = 1; k < kWaves; ++k) acc = merge(acc, red[k], c);
-      partials[w] = RowPartial{acc.m, acc.s, acc.a, 0};
+  }
+  if (!greedy && lane == 0) {
+    const float uk = uniforms[row0 + K];
+    if (!(uk >= 0.f && uk < 1.f)) lane_ok = false;
+  }
+  const bool ok = (__ballot(!lane_ok) == 0ull);
+  const unsigned long long rej = __ballot(lane < kb && !acc);
+  const int A = ok ? (rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb) : -1;
+
+  if (lane <= K) {
+    int tok = -1;
+    float prob = 0.f;
+    if (ok && lane < A) {
+      tok = x;
+      prob = static_cast<float>(px);
+    } else if (ok && lane == A && greedy) {
+      tok = st.a;                                    // argmax: exp2(0) / s
+      prob = static_cast<float>(1.0 / static_cast<double>(st.s));
     }
-    __syncthreads();
+    out_tokens[row0 + lane] = tok;                   // a sampled slot is filled by the draw
+    if (out_probs) out_probs[row0 + lane] = prob;
+  }
+  if (lane == 0) accept_len[b] = A;
+  if ((!ok || greedy) && lane == 0) states[b] = SeqState{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
+  if (ok && !greedy && lane == A) {
+    const int mode = (A == kb) ? kBonus : (is_onehot ? kResidualOnehot : kResidual);
+    states[b] = SeqState{mode, A, x, 0, c, st.m, st.s, 0.f};
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// 2. Accept scan: one wave64 per sequence, lane i <-> target row i.
+// Streaming row statistics.
+// ------------------------------------------------------------------------------------------
+template <typename LT, bool kVec>
+__global__ __launch_bounds__(kThreads) void stats_kernel(
+    const LT* __restrict__ logits, const int32_t* __restrict__ num_draft,
+    const float* __restrict__ temperature, int b0, int K, int V, int S, int greedy_all,
+    RowPartial* __restrict__ partials) {
+  // Grid: x = chunk, y = row within the sequence, z = sequence (offset by b0).  Each wave
+  // reduces its own 2048-token sub-chunk and writes its own partial: no LDS, no barrier.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = blockIdx.x, i = blockIdx.y, b = b0 + static_cast<int>(blockIdx.z);
+  if (num_draft != nullptr) {
+    const int kb = num_draft[b];
+    if (kb < 0 || kb > K || i > kb) return;  // padding (or an invalid count): never read
+  }
+  const long long r = static_cast<long long>(b) * (K + 1) + i;
+  const LT* row = logits + r * V;
+  const int c0 = s * kChunk + wave * kSub;
+  const int n = min(kSub, V - c0);
+  // The loads go out first; the row's temperature is only needed to fold them.
+  float x[kPerThread];
+  load_sub<LT, kVec>(row, c0, n, lane, x);
+  const float T = greedy_all ? 0.f : temperature[b];
+  const float c = temp_valid(T) ? temp_scale(T) : kLog2e;  // invalid rows: result unused
+  MaxSum st = fold_chunk(x, c);
+  const float lane_max = st.m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    st = merge_ms(st, MaxSum{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)}, c);
+  int arg = 0;
+  if (T == 0.f) {
+    // Greedy row: the lowest token index attaining the sub-chunk max.  Only lanes whose own
+    // max is that max search their registers.
+    int a = INT_MAX;
+    if (lane_max == st.m) {
+#pragma unroll
+      for (int j = kPerThread - 1; j >= 0; --j)
+        if (x[j] == st.m) a = tok_of<LT, kVec>(c0, lane, j);
+    }
+    arg = wave_min(a);
+  }
+  if (lane == 0)
+    partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, 0};
+}
+
+// ------------------------------------------------------------------------------------------
+// Accept scan: one wave64 per sequence.
 // ------------------------------------------------------------------------------------------
 template <typename LT>
 __global__ __launch_bounds__(64) void accept_kernel(
@@ -213,122 +389,50 @@ __global__ __launch_bounds__(64) void accept_kernel(
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     const int kb = num_draft ? num_draft[b] : K;
     const float T = greedy_all ? 0.f : temperature[b];
-    const bool greedy = (T == 0.f);
-    bool ok = kb >= 0 && kb <= K && temp_valid(T);
-    const bool is_onehot = ok && !greedy && onehot != nullptr && onehot[b] != 0;
-    const float c = temp_scale(T);
-    const long long row0 = static_cast<long long>(b) * (K + 1);
-
-    // Row statistics of row `lane` (merged over chunks in chunk order).
-    Stat st{-INFINITY, 0.f, INT_MAX};
-    bool lane_ok = true;
-    int x = -1;
-    double px = 0.0;
-    bool acc = true;
-    if (ok && lane <= kb) {
-      const RowPartial* P = partials + (row0 + lane) * S;
-      st = Stat{P[0].m, P[0].s, P[0].arg};
-      for (int j = 1; j < S; ++j) st = merge(st, Stat{P[j].m, P[j].s, P[j].arg}, c);
-      lane_ok = st.s > 0.f;  // NaN / +inf logit -> NaN; all -inf -> 0
-      if (lane < kb) {
-        x = proposed[static_cast<long long>(b) * K + lane];
-        if (x < 0 || x >= V) {
-          lane_ok = false;
-        } else {
-          const double zx = load_logit(logits, (row0 + lane) * V + x);
-          px = exp2((zx - static_cast<double>(st.m)) * static_cast<double>(c)) /
-               static_cast<double>(st.s);
-          if (greedy) {
-            acc = (x == st.a);
-          } else {
-            const float u = uniforms[row0 + lane];
-            if (!(u >= 0.f && u < 1.f)) lane_ok = false;
-            double qx = 1.0;  // one-hot drafter: q(x) = 1
-            if (!is_onehot) {
-              if (draft_probs == nullptr) {
-                lane_ok = false;
-              } else {
-                const float qf = draft_probs[(static_cast<long long>(b) * K + lane) * V + x];
-                if (!(qf >= 0.f && qf <= FLT_MAX)) lane_ok = false;
-                qx = qf;
-              }
-            }
-            acc = static_cast<double>(u) * qx < px;
-          }
-        }
-      }
+    if (kb < 0 || kb > K || !temp_valid(T)) {
+      write_invalid(b, lane, K, accept_len, out_tokens, out_probs, states);
+      continue;
     }
-    if (ok && !greedy && lane == 0) {
-      const float uk = uniforms[row0 + K];
-      if (!(uk >= 0.f && uk < 1.f)) lane_ok = false;
-    }
-    ok = ok && (__ballot(!lane_ok) == 0ull);
-    const unsigned long long rej = __ballot(lane < kb && !acc);
-    const int A = ok ? (rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb) : -1;
-
-    if (lane <= K) {
-      int tok = -1;
-      float prob = 0.f;
-      if (ok && lane < A) {
-        tok = x;
-        prob = static_cast<float>(px);
-      } else if (ok && lane == A && greedy) {
-        tok = st.a;                                    // argmax: exp2(0) / s
-        prob = static_cast<float>(1.0 / static_cast<double>(st.s));
-      }
-      out_tokens[row0 + lane] = tok;                   // the sampled slot is filled later
-      if (out_probs) out_probs[row0 + lane] = prob;
-    }
-    if (lane == 0) accept_len[b] = A;
-    if ((!ok || greedy) && lane == 0) states[b] = SeqState{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
-    if (ok && !greedy && lane == A) {
-      const int mode = (A == kb) ? kBonus : (is_onehot ? kResidualOnehot : kResidual);
-      states[b] = SeqState{mode, A, x, 0, c, st.m, st.s, 0.f};
-    }
+    accept_sequence<LT>(logits, draft_probs, onehot, proposed, uniforms, b, kb, T, K, V, S,
+                        partials, accept_len, out_tokens, out_probs, states, lane);
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// 3./4. Sampling passes.  Both compute a token's weight with the same code, so the chunk sums
-// of pass 3 and the scan of pass 4 see identical values.
+// Kernel B: draw weights per segment + the inverse-CDF pick of each completed sequence.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float draw_weight(float z, float q, int v, const SeqState& st,
-                                             bool plain, float* e_out) {
+                                             bool plain, float& e_out) {
   const float e = __builtin_amdgcn_exp2f((z - st.m) * st.c);
-  *e_out = e;
+  e_out = e;
   if (plain || st.mode == kBonus) return e;
   if (st.mode == kResidualOnehot) return v == st.excl ? 0.f : e;
   return fmaxf(0.f, fmaf(-st.s, q, e));  // s * max(0, p - q)
 }
 
-// Weights of the kGroup tokens [v0, v0 + cnt) (zeros past cnt).
+// Loads of the kGroup tokens [v0, v0 + cnt) (cnt <= 0: none); -inf / 0 past cnt.
 template <typename LT, bool kVec>
 __device__ __forceinline__ void load_group(const LT* __restrict__ z, const float* __restrict__ q,
-                                           int v0, int cnt, const SeqState& st, bool plain,
-                                           float (&w)[kGroup], float (&e)[kGroup]) {
-  float zv[kGroup], qv[kGroup];
-  if constexpr (kVec) {  // cnt == kGroup, 16-byte aligned
-    if constexpr (sizeof(LT) == 2) {
-      float t[8];
-      unpack(*reinterpret_cast<const uint4*>(z + v0), t, static_cast<const LT*>(nullptr));
+                                           int v0, int cnt, float (&zv)[kGroup],
+                                           float (&qv)[kGroup]) {
+  if constexpr (kVec) {  // cnt is kGroup or <= 0; 16-byte aligned
+    if (cnt > 0) {
+      if constexpr (sizeof(LT) == 2) {
+        unpack(stream_load(z + v0), zv, static_cast<const LT*>(nullptr));
+      } else {
+        unpack(stream_load(z + v0), zv, static_cast<const LT*>(nullptr));
+        unpack(stream_load(z + v0 + 4), zv + 4, static_cast<const LT*>(nullptr));
+      }
+      if (q != nullptr) {
+        unpack(stream_load(q + v0), qv, static_cast<const float*>(nullptr));
+        unpack(stream_load(q + v0 + 4), qv + 4, static_cast<const float*>(nullptr));
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) zv[j] = t[j];
-    } else {
-      float t0[4], t1[4];
-      unpack(*reinterpret_cast<const uint4*>(z + v0), t0, static_cast<const LT*>(nullptr));
-      unpack(*reinterpret_cast<const uint4*>(z + v0 + 4), t1, static_cast<const LT*>(nullptr));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { zv[j] = t0[j]; zv[4 + j] = t1[j]; }
-    }
-    if (q != nullptr) {
-      float t0[4], t1[4];
-      unpack(*reinterpret_cast<const uint4*>(q + v0), t0, static_cast<const float*>(nullptr));
-      unpack(*reinterpret_cast<const uint4*>(q + v0 + 4), t1, static_cast<const float*>(nullptr));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { qv[j] = t0[j]; qv[4 + j] = t1[j]; }
+        for (int j = 0; j < kGroup; ++j) qv[j] = 0.f;
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) qv[j] = 0.f;
+      for (int j = 0; j < kGroup; ++j) { zv[j] = -INFINITY; qv[j] = 0.f; }
     }
   } else {
 #pragma unroll
@@ -337,26 +441,51 @@ __device__ __forceinline__ void load_group(const LT* __restrict__ z, const float
       qv[j] = (q != nullptr && j < cnt) ? q[v0 + j] : 0.f;
     }
   }
+}
+
+// Weights of one group and their sums (sequential in token order, fp32).
+__device__ __forceinline__ void group_weights(const float (&zv)[kGroup], const float (&qv)[kGroup],
+                                              int v0, int cnt, const SeqState& st, bool plain,
+                                              float (&w)[kGroup], float& gw, float& ge) {
+  gw = 0.f;
+  ge = 0.f;
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) {
-    if (j < cnt) {
-      w[j] = draw_weight(zv[j], qv[j], v0 + j, st, plain, &e[j]);
-    } else {
-      w[j] = 0.f;
-      e[j] = 0.f;
-    }
+    float e = 0.f;
+    w[j] = j < cnt ? draw_weight(zv[j], qv[j], v0 + j, st, plain, e) : 0.f;
+    if (j >= cnt) e = 0.f;
+    gw += w[j];
+    ge += e;
   }
 }
 
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(v, off, 64);
+    if (lane >= off) v = y + v;
+  }
+  return v;
+}
+
 template <typename LT, bool kVec>
-__global__ __launch_bounds__(kThreads) void sample_sums_kernel(
+__global__ __launch_bounds__(kThreads) void draw_sums_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs, int B, int K, int V,
-    int S, const SeqState* __restrict__ states, ChunkSums* __restrict__ sums) {
-  __shared__ double redw[kWaves], rede[kWaves];
+    int S, const SeqState* __restrict__ states, SegSums* __restrict__ segs) {
+  // Wave w of the workgroup sums segment w of the chunk; lane l owns its groups l, l+64, ...
+  constexpr int kGroupsPerLane = kSeg / kGroup / 64;  // 4
+  constexpr int kZVec = kGroup * static_cast<int>(sizeof(LT)) / 16;  // 16-byte loads per group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long total = static_cast<long long>(B) * S;
-  for (long long wi = blockIdx.x; wi < total; wi += gridDim.x) {
-    const int b = static_cast<int>(wi / S), s = static_cast<int>(wi % S);
+  const unsigned total = static_cast<unsigned>(B) * static_cast<unsigned>(S);
+  for (unsigned wi = blockIdx.x; wi < total; wi += gridDim.x) {
+    const int b = static_cast<int>(wi / static_cast<unsigned>(S));
+    const int s = static_cast<int>(wi) - b * S;
     const SeqState st = states[b];
     if (st.mode == kNone) continue;
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
@@ -365,166 +494,176 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(
                          ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
                          : nullptr;
     const int c0 = s * kChunk, n = min(kChunk, V - c0);
-    const int ngroups = (n + kGroup - 1) / kGroup;
-    double tw = 0.0, te = 0.0;
-    for (int g = tid; g < ngroups; g += kThreads) {
-      float w[kGroup], e[kGroup];
-      load_group<LT, kVec>(z, q, c0 + g * kGroup, min(kGroup, n - g * kGroup), st, false, w, e);
-      float gw = 0.f, ge = 0.f;
+    const int seg0 = wave * kSeg;  // this wave's segment, relative to the chunk
+    double lw = 0.0, le = 0.0;
+    if constexpr (kVec) {
+      // All of the lane's 16-byte loads go out before any is unpacked.
+      uint4 zr[kGroupsPerLane][kZVec], qr[kGroupsPerLane][2];
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) { gw += w[j]; ge += e[j]; }
-      tw += gw;
-      te += ge;
-    }
+      for (int g = 0; g < kGroupsPerLane; ++g) {
+        const int v0 = c0 + seg0 + (g * 64 + lane) * kGroup;
+        const bool in = v0 < c0 + n;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      tw += __shfl_xor(tw, off, 64);
-      te += __shfl_xor(te, off, 64);
-    }
-    if (lane == 0) { redw[wave] = tw; rede[wave] = te; }
-    __syncthreads();
-    if (tid == 0) {
-      double a = redw[0], c = rede[0];
+        for (int h = 0; h < kZVec; ++h)
+          zr[g][h] = in ? stream_load(z + v0 + h * (16 / sizeof(LT))) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int k = 1; k < kWaves; ++k) { a += redw[k]; c += rede[k]; }
-      sums[wi] = ChunkSums{a, c};
+        for (int h = 0; h < 2; ++h)
+          qr[g][h] = (in && q != nullptr) ? stream_load(q + v0 + 4 * h) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < kGroupsPerLane; ++g) {
+        const int v0 = seg0 + (g * 64 + lane) * kGroup;
+        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+#pragma unroll
+        for (int h = 0; h < kZVec; ++h)
+          unpack(zr[g][h], zv + h * (16 / sizeof(LT)), static_cast<const LT*>(nullptr));
+        unpack(qr[g][0], qv, static_cast<const float*>(nullptr));
+        unpack(qr[g][1], qv + 4, static_cast<const float*>(nullptr));
+        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+        lw += gw;
+        le += ge;
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < kGroupsPerLane; ++g) {
+        const int v0 = seg0 + (g * 64 + lane) * kGroup;
+        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+        load_group<LT, false>(z, q, c0 + v0, min(kGroup, n - v0), zv, qv);
+        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+        lw += gw;
+        le += ge;
+      }
     }
-    __syncthreads();
+    lw = wave_sum(lw);
+    le = wave_sum(le);
+    if (lane == 0) segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
   }
 }
 
 template <typename LT, bool kVec>
-__global__ __launch_bounds__(kThreads) void sample_pick_kernel(
+__global__ __launch_bounds__(kThreads) void pick_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const float* __restrict__ uniforms, int B, int K, int V, int S,
-    const SeqState* __restrict__ states, const ChunkSums* __restrict__ sums,
+    const SeqState* __restrict__ states, const SegSums* __restrict__ all_segs,
     int32_t* __restrict__ out_tokens, float* __restrict__ out_probs) {
-  __shared__ double sh_t, sh_base;
-  __shared__ int sh_chunk, sh_plain, sh_last;
-  __shared__ double wtot[kWaves];
-  __shared__ int wfound[kWaves], wlast[kWaves];
+  __shared__ int sh_seg, sh_plain, sh_hit[kWaves], sh_lastpos[kWaves];
+  __shared__ float sh_zhit[kWaves], sh_zlast[kWaves];
+  __shared__ double sh_t, sh_base, sh_wtot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    const int nseg = S * kSegPerChunk;
+    const SegSums* segs = all_segs + static_cast<long long>(b) * nseg;
+    // The first 64 segment sums are fetched alongside the sequence's state.
+    SegSums first{0.0, 0.0};
+    if (wave == 0 && lane < nseg) first = segs[lane];
     const SeqState st = states[b];
     if (st.mode == kNone) continue;
-    const long long row0 = static_cast<long long>(b) * (K + 1);
-    if (tid == 0) {
-      // Chunk totals in chunk order (fp64); an empty residual falls back to p itself.
-      const ChunkSums* cs = sums + static_cast<long long>(b) * S;
-      double R = 0.0;
-      for (int s = 0; s < S; ++s) R += cs[s].w;
-      const int plain = !(R > 0.0);
-      if (plain) {
-        R = 0.0;
-        for (int s = 0; s < S; ++s) R += cs[s].e;
+    const long long row = static_cast<long long>(b) * (K + 1) + st.row;
+    const LT* z = logits + row * V;
+    // ---- The segment holding t = u * total (fp64 running sums in segment order). ----
+    if (wave == 0) {
+      // Pass 1: totals of both weight kinds, with the same scan arithmetic as pass 2.
+      double base_w = 0.0, base_e = 0.0;
+      for (int j0 = 0; j0 < nseg; j0 += 64) {
+        const int j = j0 + lane;
+        const SegSums sj = j0 == 0 ? first : (j < nseg ? segs[j] : SegSums{0.0, 0.0});
+        const double vw = sj.w, ve = sj.e;
+        const double iw = wave_inclusive_scan(vw, lane), ie = wave_inclusive_scan(ve, lane);
+        base_w += __shfl(iw, 63, 64);
+        base_e += __shfl(ie, 63, 64);
       }
-      const double t = static_cast<double>(uniforms[row0 + K]) * R;
-      double base = 0.0, base_last = 0.0;
-      int chunk = -1, last = -1;
-      for (int s = 0; s < S; ++s) {
-        const double ws = plain ? cs[s].e : cs[s].w;
-        if (ws > 0.0) {
-          if (base + ws > t) { chunk = s; break; }
-          last = s;
-          base_last = base;
+      const bool plain = !(base_w > 0.0);  // empty residual: draw from p itself
+      const double R = plain ? base_e : base_w;
+      const double t =
+          static_cast<double>(uniforms[static_cast<long long>(b) * (K + 1) + K]) * R;
+      // Pass 2: first segment whose running sum exceeds t.
+      double base = 0.0;
+      int seg = -1, lastpos = -1;
+      double base_at_seg = 0.0, base_at_last = 0.0;
+      for (int j0 = 0; j0 < nseg && seg < 0; j0 += 64) {
+        const int j = j0 + lane;
+        const SegSums sj = j0 == 0 ? first : (j < nseg ? segs[j] : SegSums{0.0, 0.0});
+        const double v = plain ? sj.e : sj.w;
+        const double inc = wave_inclusive_scan(v, lane);
+        const double exc = base + (inc - v);
+        const unsigned long long hit = __ballot(v > 0.0 && base + inc > t);
+        const unsigned long long pos = __ballot(v > 0.0);
+        if (hit) {
+          const int l = __ffsll(static_cast<long long>(hit)) - 1;
+          seg = j0 + l;
+          base_at_seg = __shfl(exc, l, 64);
+        } else if (pos) {
+          const int l = 63 - __clzll(static_cast<long long>(pos));
+          lastpos = j0 + l;
+          base_at_last = __shfl(exc, l, 64);
         }
-        base += ws;
+        base += __shfl(inc, 63, 64);
       }
-      if (chunk < 0) { chunk = last; base = base_last; }
-      if (chunk < 0) { chunk = 0; base = 0.0; }  // no positive chunk sum (cannot happen for a valid row)
-      sh_t = t;
-      sh_base = base;
-      sh_chunk = chunk;
-      sh_plain = plain;
+      if (seg < 0) { seg = lastpos >= 0 ? lastpos : 0; base_at_seg = base_at_last; }
+      if (lane == 0) { sh_seg = seg; sh_plain = plain; sh_t = t; sh_base = base_at_seg; }
     }
     __syncthreads();
-    const double t = sh_t;
+    // ---- Scan the chosen segment in ascending token order. ----
+    const int seg = sh_seg;
     const bool plain = sh_plain != 0;
-    const int chunk = sh_chunk;
-    const long long row = row0 + st.row;
-    const LT* z = logits + row * V;
-    const float* q = (st.mode == kResidual && !plain)
-                         ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
-                         : nullptr;
-    const int c0 = chunk * kChunk, n = min(kChunk, V - c0);
-    const int ngroups = (n + kGroup - 1) / kGroup;
-    double base = sh_base;
-    int result = -1, last_pos = -1;
-    for (int g0 = 0; g0 < ngroups; g0 += kThreads) {
-      const int g = g0 + tid;
-      float w[kGroup], e[kGroup];
-      float gsum = 0.f;
-      if (g < ngroups) {
-        load_group<LT, kVec>(z, q, c0 + g * kGroup, min(kGroup, n - g * kGroup), st, plain, w, e);
+    const double t = sh_t;
+    const int sc = seg / kSegPerChunk, sg = seg % kSegPerChunk;
+    const int cc0 = sc * kChunk, cn = min(kChunk, V - cc0);
+    const int v0 = sg * kSeg + tid * kGroup;
+    const int cnt = min(kGroup, cn - v0);
+    const float* qs = (st.mode == kResidual && !plain)
+                          ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
+                          : nullptr;
+    float zg[kGroup], qg[kGroup], w[kGroup], gw, ge;
+    load_group<LT, kVec>(z, qs, cc0 + v0, cnt, zg, qg);
+    group_weights(zg, qg, cc0 + v0, cnt, st, plain, w, gw, ge);
+    const double inc = wave_inclusive_scan(static_cast<double>(gw), lane);
+    if (lane == 63) sh_wtot[wave] = inc;
+    __syncthreads();
+    double before = sh_base;
+    for (int k = 0; k < wave; ++k) before += sh_wtot[k];
+    before += inc - static_cast<double>(gw);
+    int hit = -1, lastpos = -1;
+    float zhit = 0.f, zlast = 0.f, run = 0.f;
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-          gsum += w[j];
-          if (w[j] > 0.f) last_pos = c0 + g * kGroup + j;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) w[j] = 0.f;
+    for (int j = 0; j < kGroup; ++j) {
+      run += w[j];
+      if (w[j] > 0.f) {
+        lastpos = cc0 + v0 + j;
+        zlast = zg[j];
+        if (hit < 0 && before + static_cast<double>(run) > t) { hit = cc0 + v0 + j; zhit = zg[j]; }
       }
-      // Inclusive scan of the group sums over the workgroup (fp64, ascending thread order).
-      double inc = gsum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(inc, off, 64);
-        if (lane >= off) inc = y + inc;
-      }
-      double exc = __shfl_up(inc, 1, 64);
-      if (lane == 0) exc = 0.0;
-      if (lane == 63) wtot[wave] = inc;
-      __syncthreads();
-      double before = base;
-      for (int k = 0; k < wave; ++k) before += wtot[k];
-      before += exc;
-      // First token of this group whose running sum exceeds t.
-      int hit = -1;
-      if (g < ngroups) {
-        float run = 0.f;
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-          run += w[j];
-          if (hit < 0 && w[j] > 0.f && before + static_cast<double>(run) > t)
-            hit = c0 + g * kGroup + j;
-        }
-      }
-      // Lowest hit in the workgroup.
-      const unsigned long long hm = __ballot(hit >= 0);
-      const int wl = hm ? __shfl(hit, __ffsll(static_cast<long long>(hm)) - 1, 64) : -1;
-      if (lane == 0) wfound[wave] = wl;
-      __syncthreads();
-      int found = -1;
-      for (int k = 0; k < kWaves; ++k)
-        if (found < 0 && wfound[k] >= 0) found = wfound[k];
-      double iter_total = 0.0;
-      for (int k = 0; k < kWaves; ++k) iter_total += wtot[k];
-      __syncthreads();
-      if (found >= 0) { result = found; break; }
-      base += iter_total;
     }
-    if (result < 0) {
-      // Rounding left u * total at the very top of the chunk: take its last positive token.
-      int lp = last_pos;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, 64));
-      if (lane == 0) wlast[wave] = lp;
-      __syncthreads();
-      if (tid == 0) {
-        int m = -1;
-        for (int k = 0; k < kWaves; ++k) m = max(m, wlast[k]);
-        sh_last = m;
-      }
-      __syncthreads();
-      result = sh_last >= 0 ? sh_last : c0;
+    const unsigned long long hm = __ballot(hit >= 0);
+    const unsigned long long pm = __ballot(lastpos >= 0);
+    const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 0;
+    const int ll = pm ? 63 - __clzll(static_cast<long long>(pm)) : 0;
+    const int wave_hit = hm ? __shfl(hit, hl, 64) : -1;
+    const float wave_zhit = __shfl(zhit, hl, 64);
+    const int wave_last = pm ? __shfl(lastpos, ll, 64) : -1;
+    const float wave_zlast = __shfl(zlast, ll, 64);
+    if (lane == 0) {
+      sh_hit[wave] = wave_hit; sh_zhit[wave] = wave_zhit;
+      sh_lastpos[wave] = wave_last; sh_zlast[wave] = wave_zlast;
     }
+    __syncthreads();
     if (tid == 0) {
-      const double zy = load_logit(z, result);
-      const double p = exp2((zy - static_cast<double>(st.m)) * static_cast<double>(st.c)) /
-                       static_cast<double>(st.s);
-      out_tokens[row0 + st.row] = result;
-      if (out_probs) out_probs[row0 + st.row] = static_cast<float>(p);
+      int y = -1, lp = -1;
+      float zy = 0.f, zl = 0.f;
+      for (int k = 0; k < kWaves; ++k) {
+        if (y < 0 && sh_hit[k] >= 0) { y = sh_hit[k]; zy = sh_zhit[k]; }
+        if (sh_lastpos[k] >= 0) { lp = sh_lastpos[k]; zl = sh_zlast[k]; }
+      }
+      // Rounding left t at the very top of the segment: take its last positive token.
+      if (y < 0) {
+        y = lp >= 0 ? lp : cc0 + sg * kSeg;
+        zy = lp >= 0 ? zl : load_logit(z, y);
+      }
+      const double p = exp2((static_cast<double>(zy) - static_cast<double>(st.m)) *
+                            static_cast<double>(st.c)) / static_cast<double>(st.s);
+      const long long slot = static_cast<long long>(b) * (K + 1) + st.row;
+      out_tokens[slot] = y;
+      if (out_probs) out_probs[slot] = static_cast<float>(p);
     }
     __syncthreads();
   }
@@ -542,39 +681,45 @@ hipError_t launch_typed(const LaunchArgs& a) {
   const int S = num_chunks(a.V);
   const bool vec_stats = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
                          ((static_cast<long long>(a.V) * sizeof(LT)) % 16 == 0);
-  const bool vec_sample = vec_stats && (a.V % kGroup == 0) &&
-                          (a.draft_probs == nullptr ||
-                           reinterpret_cast<uintptr_t>(a.draft_probs) % 16 == 0);
-  const long long rows = static_cast<long long>(a.B) * (a.K + 1);
+  const bool vec_draw = vec_stats && (a.V % kGroup == 0) &&
+                        (a.draft_probs == nullptr ||
+                         reinterpret_cast<uintptr_t>(a.draft_probs) % 16 == 0);
   hipError_t err;
-  if (a.hot_begin && (err = hipEventRecord(a.hot_begin, a.stream)) != hipSuccess) return err;
-  if (vec_stats)
-    row_stats_kernel<LT, true><<<grid_for(rows * S), kThreads, 0, a.stream>>>(
-        logits, a.num_draft, a.temperature, a.B, a.K, a.V, S, a.greedy_all, a.ws.partials);
-  else
-    row_stats_kernel<LT, false><<<grid_for(rows * S), kThreads, 0, a.stream>>>(
-        logits, a.num_draft, a.temperature, a.B, a.K, a.V, S, a.greedy_all, a.ws.partials);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (a.hot_end && (err = hipEventRecord(a.hot_end, a.stream)) != hipSuccess) return err;
+  // The streaming kernel: grid (chunk, row within sequence, sequence), at most 65535 sequences
+  // per launch.  With measurement events, the dispatches record them (first start, last end).
+  auto stats = vec_stats ? stats_kernel<LT, true> : stats_kernel<LT, false>;
+  constexpr int kMaxZ = 65535;
+  for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
+    const dim3 grid(S, a.K + 1, min(kMaxZ, a.B - b0));
+    hipEvent_t ev0 = b0 == 0 ? a.hot_begin : nullptr;
+    hipEvent_t ev1 = b0 + kMaxZ >= a.B ? a.hot_end : nullptr;
+    if (ev0 || ev1)
+      hipExtLaunchKernelGGL(stats, grid, dim3(kThreads), 0, a.stream, ev0, ev1, 0, logits,
+                            a.num_draft, a.temperature, b0, a.K, a.V, S, a.greedy_all,
+                            a.ws.partials);
+    else
+      stats<<<grid, kThreads, 0, a.stream>>>(logits, a.num_draft, a.temperature, b0, a.K, a.V,
+                                             S, a.greedy_all, a.ws.partials);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   accept_kernel<LT><<<grid_for(a.B), 64, 0, a.stream>>>(
       logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms, a.B,
       a.K, a.V, S, a.greedy_all, a.ws.partials, a.accept_len, a.out_tokens, a.out_probs,
       a.ws.states);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.greedy_all) return hipSuccess;
-  if (vec_sample) {
-    sample_sums_kernel<LT, true><<<grid_for(static_cast<long long>(a.B) * S), kThreads, 0,
-                                  a.stream>>>(logits, a.draft_probs, a.B, a.K, a.V, S,
-                                              a.ws.states, a.ws.sums);
-    sample_pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.sums,
+  const long long draw_tiles = static_cast<long long>(a.B) * S;
+  if (vec_draw) {
+    draw_sums_kernel<LT, true><<<grid_for(draw_tiles), kThreads, 0, a.stream>>>(
+        logits, a.draft_probs, a.B, a.K, a.V, S, a.ws.states, a.ws.segs);
+    pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
+        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
         a.out_tokens, a.out_probs);
   } else {
-    sample_sums_kernel<LT, false><<<grid_for(static_cast<long long>(a.B) * S), kThreads, 0,
-                                   a.stream>>>(logits, a.draft_probs, a.B, a.K, a.V, S,
-                                               a.ws.states, a.ws.sums);
-    sample_pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.sums,
+    draw_sums_kernel<LT, false><<<grid_for(draw_tiles), kThreads, 0, a.stream>>>(
+        logits, a.draft_probs, a.B, a.K, a.V, S, a.ws.states, a.ws.segs);
+    pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
+        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
         a.out_tokens, a.out_probs);
   }
   return hipGetLastError();
@@ -582,19 +727,20 @@ hipError_t launch_typed(const LaunchArgs& a) {
 
 }  // namespace
 
-size_t workspace_layout(int B, int K, int V, size_t* off_partials, size_t* off_states,
-                        size_t* off_sums) {
+WorkspaceLayout workspace_layout(int B, int K, int V) {
   auto align16 = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
   const size_t S = static_cast<size_t>(num_chunks(V));
   const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(K + 1);
+  WorkspaceLayout L;
   size_t off = 0;
-  *off_partials = off;
-  off = align16(off + rows * S * sizeof(RowPartial));
-  *off_states = off;
+  L.partials = off;
+  off = align16(off + rows * S * kWaves * sizeof(RowPartial));
+  L.states = off;
   off = align16(off + static_cast<size_t>(B) * sizeof(SeqState));
-  *off_sums = off;
-  off = align16(off + static_cast<size_t>(B) * S * sizeof(ChunkSums));
-  return off;
+  L.segs = off;
+  off = align16(off + static_cast<size_t>(B) * S * kSegPerChunk * sizeof(SegSums));
+  L.total = off;
+  return L;
 }
 
 hipError_t launch_verify(const LaunchArgs& a) {

@@ -159,3 +159,23 @@ def test_empty_batch():
                                    torch.empty((0, 6), dtype=torch.float32, device=DEV))
     torch.cuda.synchronize()
     assert acc.numel() == 0 and tok.shape == (0, 6)
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """One zero-filled workspace serves consecutive calls of different shapes: every call
+    leaves its arrival counters at zero again."""
+    from speculative_decoding_verification_specdec_amd import specdec_workspace_size
+    big = gen.ragged_mixed(B=80, V=20000, seed=61)
+    small = gen.batch64(B=12, V=9000, seed=62)
+    need = max(specdec_workspace_size(x.B, x.K, x.V) for x in (big, small))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for inp in (big, small, big, small):
+        d = inputs_to_device(inp, DEV)
+        acc, tok, prb = specdec_verify(d["logits"], d["draft_probs"], d["proposed"],
+                                       d["temperature"], d["uniforms"],
+                                       draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
+                                       workspace=ws)
+        torch.cuda.synchronize()
+        rep = compare(inp, oracle.verify(inp), acc.cpu().numpy(), tok.cpu().numpy(),
+                      prb.cpu().numpy())
+        assert rep["mismatch"] == 0, rep["details"]
