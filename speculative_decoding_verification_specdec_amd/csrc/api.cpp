@@ -63,6 +63,7 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.out_probs = out_probs;
   char* base = static_cast<char*>(workspace);
   a.ws.partials = reinterpret_cast<specdec::RowPartial*>(base + L.partials);
+  a.ws.gathers = reinterpret_cast<specdec::Gather*>(base + L.gathers);
   a.ws.states = reinterpret_cast<specdec::SeqState*>(base + L.states);
   a.ws.segs = reinterpret_cast<specdec::SegSums*>(base + L.segs);
   a.stream = static_cast<hipStream_t>(stream);

@@ -41,6 +41,15 @@ struct SeqState {
   float pad1;
 };
 
+// One drafted slot's gathered inputs, recorded by the streaming kernel: the proposed id x_i,
+// the target logit z_i[x_i] and the drafter probability q_i(x_i).
+struct Gather {
+  float z;
+  float q;
+  int32_t x;
+  int32_t pad;
+};
+
 // Weight sums of one 2048-token draw segment.
 struct SegSums {
   double w;       // the draw's weights
@@ -51,6 +60,7 @@ struct SegSums {
 // between calls).
 struct Workspace {
   RowPartial* partials;  // [B*(K+1)*S*4], 4 sub-chunks per chunk
+  Gather* gathers;       // [B*K]
   SeqState* states;      // [B]
   SegSums* segs;         // [B*S*kSegPerChunk]
 };
@@ -58,7 +68,7 @@ struct Workspace {
 inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
 struct WorkspaceLayout {
-  size_t partials, states, segs, total;
+  size_t partials, gathers, states, segs, total;
 };
 
 // Byte layout of the caller's workspace for these sizes.

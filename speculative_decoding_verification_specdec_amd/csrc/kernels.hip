@@ -6,18 +6,18 @@
 // the result is exactly the target model"; "Speculative decoding: el secretario que adelanta
 // lo que va a decir el jefe" (blog.lo0.es), section "El mecanismo desnudo".
 //
-// Four kernels, enqueued back to back on the caller's stream.  They communicate only through
+// Three kernels, enqueued back to back on the caller's stream.  They communicate only through
 // the workspace across kernel boundaries: no atomics, no inter-workgroup waiting.
 //   stats_kernel   one 256-thread workgroup per (used target row, 8192-logit chunk).  Issues
 //       the chunk's 16-byte loads first, then folds them into (max, sum of
 //       exp2((z - max) * log2(e)/T), lowest argmax) and writes the chunk partial.
-//   accept_kernel  one wave64 per sequence, lane i <-> target row i: merges row i's chunk
-//       partials in chunk order, gathers p_i(x_i) (fp64) and q_i(x_i), and a 64-bit ballot
-//       finds the first rejection.  Emits every token already known (accepted drafts, greedy
-//       argmaxes) and records what remains to be drawn.
-//   draw_sums_kernel  one workgroup per (sequence that needs a draw, chunk of the row to draw
-//       from): sums the draw's weights -- s * max(0, p - q), p without the rejected draft, or
-//       p -- over each 2048-token segment of the chunk.
+//   accept_draw_kernel  one workgroup per (chunk of the row to draw from, sequence).  Wave 0
+//       runs the sequence's accept scan (lane i <-> target row i: row i's sub-chunk partials
+//       merged by 16 lanes with a DPP all-reduce, p_i(x_i) in fp64, q_i(x_i) gathered, a 64-bit
+//       ballot finds the first rejection); the chunk-0 workgroup emits every token already
+//       known (accepted drafts, greedy argmaxes) and records what remains to be drawn.  Then the
+//       workgroup sums the draw's weights -- s * max(0, p - q), p without the rejected draft,
+//       or p -- over each 2048-token segment of its chunk.
 //   pick_kernel  one workgroup per sequence that needs a draw: scans the segment sums (fp64)
 //       to the segment holding u * total, then scans that one segment in ascending token
 //       order to the first running sum above u * total.
@@ -213,65 +213,69 @@ __device__ __forceinline__ int tok_of(int c0, int lane, int j) {
   }
 }
 
-__device__ void write_invalid(int b, int lane, int K, int32_t* accept_len, int32_t* out_tokens,
-                              float* out_probs, SeqState* states) {
+// Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count
+// and temperature (an invalid pair poisons the sequence).  Every load that needs neither of
+// them goes out first: the drafted ids with their gathered logit and q (recorded by the
+// streaming kernel), the uniforms, and all K + 1 rows' sub-chunk partials.  Returns what remains
+// to be drawn (the same value in every lane); with `write`, also emits the known tokens,
+// accept_len and the draw state.
+__device__ __forceinline__ SeqState accept_sequence(const uint8_t* onehot, const float* uniforms,
+                                    const Gather* gathers, bool have_q, int b, int kb_raw,
+                                    float T, int K, int V, int S, const RowPartial* partials,
+                                    int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                                    SeqState* states, bool write, int lane) {
   const long long row0 = static_cast<long long>(b) * (K + 1);
-  if (lane <= K) {
-    out_tokens[row0 + lane] = -1;
-    if (out_probs) out_probs[row0 + lane] = 0.f;
-  }
-  if (lane == 0) {
-    accept_len[b] = -1;
-    states[b] = SeqState{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// Accept scan of sequence b by one wave64 (lane i <-> target row i); kb and T are valid.
-template <typename LT>
-__device__ void accept_sequence(const LT* logits, const float* draft_probs,
-                                const uint8_t* onehot, const int32_t* proposed,
-                                const float* uniforms, int b, int kb, float T, int K, int V,
-                                int S, const RowPartial* partials, int32_t* accept_len,
-                                int32_t* out_tokens, float* out_probs, SeqState* states,
-                                int lane) {
+  const Gather g = lane < K ? gathers[static_cast<long long>(b) * K + lane]
+                            : Gather{0.f, 0.f, -1, 0};
+  const float u = (uniforms != nullptr && lane < K) ? uniforms[row0 + lane] : 0.f;
+  const float uk = (uniforms != nullptr && lane == 0) ? uniforms[row0 + K] : 0.f;
+  const bool onehot_row = onehot != nullptr && onehot[b] != 0;
+  const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
+  const int kb = seq_ok ? kb_raw : 0;
   const bool greedy = (T == 0.f);
-  const bool is_onehot = !greedy && onehot != nullptr && onehot[b] != 0;
-  const float c = temp_scale(T);
-  const long long row0 = static_cast<long long>(b) * (K + 1);
-  // Independent loads first: the draft id, its logit and q, the uniform.
-  const bool drafted = lane < kb;
-  const int x = drafted ? proposed[static_cast<long long>(b) * K + lane] : -1;
-  const bool x_ok = x >= 0 && x < V;
-  const float u = (drafted && !greedy) ? uniforms[row0 + lane] : 0.f;
-  const double zx = (drafted && x_ok) ? static_cast<double>(load_logit(logits, (row0 + lane) * V + x))
-                                      : 0.0;
-  const bool model_q = drafted && x_ok && !greedy && !is_onehot && draft_probs != nullptr;
-  const float qf = model_q ? draft_probs[(static_cast<long long>(b) * K + lane) * V + x] : 1.f;
-  // Row statistics: four rows per pass, sixteen lanes per row.  Lane l of a row merges the
-  // row's sub-chunk partials l, l + 16, ... in order, the row's lanes all-reduce with DPP, and
-  // lane i keeps row i's result (taken from the row's lane 0).
+  const bool is_onehot = !greedy && onehot_row;
+  const float c = seq_ok ? temp_scale(T) : kLog2e;
+
+  // Row statistics: four rows per pass, sixteen lanes per row, two passes' loads in flight
+  // at a time.  Lane l of a row merges the row's sub-chunk partials l, l + 16, ... in order,
+  // the row's lanes all-reduce with DPP, and lane i keeps row i's result (from the row's lane 0).
+  // Rows past k_b are merged too (their partials are stale) and ignored.
   Stat st{-INFINITY, 0.f, INT_MAX};
   const int nsub = S * kWaves;
   const int per_lane = (nsub + 15) / 16;
-  for (int i0 = 0; i0 <= kb; i0 += 4) {
-    const int ri = i0 + (lane >> 4), sl = lane & 15;
-    Stat v{-INFINITY, 0.f, INT_MAX};
-    const RowPartial* P = partials + (row0 + ri) * nsub;
-    for (int t0 = 0; t0 < per_lane; t0 += 8) {
-      RowPartial pb[8];
+  const int sl = lane & 15;
+  for (int i0 = 0; i0 <= K; i0 += 8) {
+    Stat v[2] = {Stat{-INFINITY, 0.f, INT_MAX}, Stat{-INFINITY, 0.f, INT_MAX}};
+    for (int t0 = 0; t0 < per_lane; t0 += 4) {
+      RowPartial pb[2][4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int j = sl + 16 * (t0 + t);
-        pb[t] = (ri <= kb && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0};
+      for (int h = 0; h < 2; ++h) {
+        const int ri = i0 + 4 * h + (lane >> 4);
+        const RowPartial* P = partials + (row0 + ri) * nsub;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = sl + 16 * (t0 + t);
+          pb[h][t] = (ri <= K && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0};
+        }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v = merge(v, Stat{pb[t].m, pb[t].s, pb[t].arg}, c);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[h] = merge(v[h], Stat{pb[h][t].m, pb[h][t].s, pb[h][t].arg}, c);
     }
-    v = row16_reduce(v, c);
-    const int src = ((lane - i0) & 3) * 16;
-    const Stat got{__shfl(v.m, src, 64), __shfl(v.s, src, 64), __shfl(v.a, src, 64)};
-    if (lane >= i0 && lane < i0 + 4) st = got;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const Stat red = row16_reduce(v[h], c);
+      const int base = i0 + 4 * h;
+      const int src = ((lane - base) & 3) * 16;
+      const Stat got{__shfl(red.m, src, 64), __shfl(red.s, src, 64), __shfl(red.a, src, 64)};
+      if (lane >= base && lane < base + 4) st = got;
+    }
   }
+
+  const bool drafted = lane < kb;
+  const int x = g.x;
+  const bool x_ok = x >= 0 && x < V;
   bool lane_ok = true;
   double px = 0.0;
   bool acc = true;
@@ -281,50 +285,54 @@ __device__ void accept_sequence(const LT* logits, const float* draft_probs,
       if (!x_ok) {
         lane_ok = false;
       } else {
-        px = exp2((zx - static_cast<double>(st.m)) * static_cast<double>(c)) /
-             static_cast<double>(st.s);
+        px = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
+                  static_cast<double>(c)) / static_cast<double>(st.s);
         if (greedy) {
           acc = (x == st.a);
         } else {
           if (!(u >= 0.f && u < 1.f)) lane_ok = false;
           double qx = 1.0;  // one-hot drafter: q(x) = 1
           if (!is_onehot) {
-            if (draft_probs == nullptr) lane_ok = false;
-            else if (!(qf >= 0.f && qf <= FLT_MAX)) lane_ok = false;
-            qx = qf;
+            if (!have_q) lane_ok = false;
+            else if (!(g.q >= 0.f && g.q <= FLT_MAX)) lane_ok = false;
+            qx = g.q;
           }
           acc = static_cast<double>(u) * qx < px;
         }
       }
     }
   }
-  if (!greedy && lane == 0) {
-    const float uk = uniforms[row0 + K];
-    if (!(uk >= 0.f && uk < 1.f)) lane_ok = false;
-  }
-  const bool ok = (__ballot(!lane_ok) == 0ull);
+  if (!greedy && lane == 0 && !(uk >= 0.f && uk < 1.f)) lane_ok = false;
+  const bool ok = seq_ok && (__ballot(!lane_ok) == 0ull);
   const unsigned long long rej = __ballot(lane < kb && !acc);
   const int A = ok ? (rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb) : -1;
 
-  if (lane <= K) {
-    int tok = -1;
-    float prob = 0.f;
-    if (ok && lane < A) {
-      tok = x;
-      prob = static_cast<float>(px);
-    } else if (ok && lane == A && greedy) {
-      tok = st.a;                                    // argmax: exp2(0) / s
-      prob = static_cast<float>(1.0 / static_cast<double>(st.s));
-    }
-    out_tokens[row0 + lane] = tok;                   // a sampled slot is filled by the draw
-    if (out_probs) out_probs[row0 + lane] = prob;
-  }
-  if (lane == 0) accept_len[b] = A;
-  if ((!ok || greedy) && lane == 0) states[b] = SeqState{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
-  if (ok && !greedy && lane == A) {
+  SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
+  if (ok && !greedy) {  // A is wave-uniform: lane A's row is the one to draw from
     const int mode = (A == kb) ? kBonus : (is_onehot ? kResidualOnehot : kResidual);
-    states[b] = SeqState{mode, A, x, 0, c, st.m, st.s, 0.f};
+    out = SeqState{mode, A, __shfl(x, A, 64), 0, c, __shfl(st.m, A, 64), __shfl(st.s, A, 64),
+                   0.f};
   }
+  if (write) {
+    if (lane <= K) {
+      int tok = -1;
+      float prob = 0.f;
+      if (ok && lane < A) {
+        tok = x;
+        prob = static_cast<float>(px);
+      } else if (ok && lane == A && greedy) {
+        tok = st.a;                                  // argmax: exp2(0) / s
+        prob = static_cast<float>(1.0 / static_cast<double>(st.s));
+      }
+      out_tokens[row0 + lane] = tok;                 // a sampled slot is filled by the draw
+      if (out_probs) out_probs[row0 + lane] = prob;
+    }
+    if (lane == 0) {
+      accept_len[b] = A;
+      states[b] = out;
+    }
+  }
+  return out;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -332,15 +340,17 @@ __device__ void accept_sequence(const LT* logits, const float* draft_probs,
 // ------------------------------------------------------------------------------------------
 template <typename LT, bool kVec>
 __global__ __launch_bounds__(kThreads) void stats_kernel(
-    const LT* __restrict__ logits, const int32_t* __restrict__ num_draft,
+    const LT* __restrict__ logits, const float* __restrict__ draft_probs,
+    const int32_t* __restrict__ proposed, const int32_t* __restrict__ num_draft,
     const float* __restrict__ temperature, int b0, int K, int V, int S, int greedy_all,
-    RowPartial* __restrict__ partials) {
+    RowPartial* __restrict__ partials, Gather* __restrict__ gathers) {
   // Grid: x = chunk, y = row within the sequence, z = sequence (offset by b0).  Each wave
   // reduces its own 2048-token sub-chunk and writes its own partial: no LDS, no barrier.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = blockIdx.x, i = blockIdx.y, b = b0 + static_cast<int>(blockIdx.z);
+  int kb = K;
   if (num_draft != nullptr) {
-    const int kb = num_draft[b];
+    kb = num_draft[b];
     if (kb < 0 || kb > K || i > kb) return;  // padding (or an invalid count): never read
   }
   const long long r = static_cast<long long>(b) * (K + 1) + i;
@@ -351,6 +361,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   float x[kPerThread];
   load_sub<LT, kVec>(row, c0, n, lane, x);
   const float T = greedy_all ? 0.f : temperature[b];
+  if (s == 0 && threadIdx.x == 0 && i < kb) {
+    // The accept scan's gathers for drafted slot i, recorded while the stream is in flight.
+    const long long slot = static_cast<long long>(b) * K + i;
+    const int xi = proposed[slot];
+    Gather gi{0.f, 0.f, xi, 0};
+    if (xi >= 0 && xi < V) {
+      gi.z = load_logit(row, xi);
+      if (draft_probs != nullptr && T != 0.f) gi.q = draft_probs[slot * V + xi];
+    }
+    gathers[slot] = gi;
+  }
   const float c = temp_valid(T) ? temp_scale(T) : kLog2e;  // invalid rows: result unused
   MaxSum st = fold_chunk(x, c);
   const float lane_max = st.m;
@@ -371,31 +392,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   }
   if (lane == 0)
     partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, 0};
-}
-
-// ------------------------------------------------------------------------------------------
-// Accept scan: one wave64 per sequence.
-// ------------------------------------------------------------------------------------------
-template <typename LT>
-__global__ __launch_bounds__(64) void accept_kernel(
-    const LT* __restrict__ logits, const float* __restrict__ draft_probs,
-    const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
-    const int32_t* __restrict__ num_draft, const float* __restrict__ temperature,
-    const float* __restrict__ uniforms, int B, int K, int V, int S, int greedy_all,
-    const RowPartial* __restrict__ partials, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ out_tokens, float* __restrict__ out_probs,
-    SeqState* __restrict__ states) {
-  const int lane = threadIdx.x;
-  for (int b = blockIdx.x; b < B; b += gridDim.x) {
-    const int kb = num_draft ? num_draft[b] : K;
-    const float T = greedy_all ? 0.f : temperature[b];
-    if (kb < 0 || kb > K || !temp_valid(T)) {
-      write_invalid(b, lane, K, accept_len, out_tokens, out_probs, states);
-      continue;
-    }
-    accept_sequence<LT>(logits, draft_probs, onehot, proposed, uniforms, b, kb, T, K, V, S,
-                        partials, accept_len, out_tokens, out_probs, states, lane);
-  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -474,70 +470,87 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
   return v;
 }
 
+// ------------------------------------------------------------------------------------------
+// Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
+// by b0).  Wave 0 of every workgroup runs its sequence's accept scan (the partials it reads are
+// L2-resident); the chunk-0 workgroup also writes the scan's outputs and the draw state.  Then
+// wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns groups l,
+// l + 64, ...), in fp64.
+// ------------------------------------------------------------------------------------------
 template <typename LT, bool kVec>
-__global__ __launch_bounds__(kThreads) void draw_sums_kernel(
-    const LT* __restrict__ logits, const float* __restrict__ draft_probs, int B, int K, int V,
-    int S, const SeqState* __restrict__ states, SegSums* __restrict__ segs) {
-  // Wave w of the workgroup sums segment w of the chunk; lane l owns its groups l, l+64, ...
+__global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
+    const LT* __restrict__ logits, const float* __restrict__ draft_probs,
+    const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
+    const int32_t* __restrict__ num_draft, const float* __restrict__ temperature,
+    const float* __restrict__ uniforms, int b0, int K, int V, int S, int greedy_all,
+    const RowPartial* __restrict__ partials, const Gather* __restrict__ gathers,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs) {
   constexpr int kGroupsPerLane = kSeg / kGroup / 64;  // 4
   constexpr int kZVec = kGroup * static_cast<int>(sizeof(LT)) / 16;  // 16-byte loads per group
+  __shared__ SeqState sh_st;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned total = static_cast<unsigned>(B) * static_cast<unsigned>(S);
-  for (unsigned wi = blockIdx.x; wi < total; wi += gridDim.x) {
-    const int b = static_cast<int>(wi / static_cast<unsigned>(S));
-    const int s = static_cast<int>(wi) - b * S;
-    const SeqState st = states[b];
-    if (st.mode == kNone) continue;
-    const long long row = static_cast<long long>(b) * (K + 1) + st.row;
-    const LT* z = logits + row * V;
-    const float* q = st.mode == kResidual
-                         ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
-                         : nullptr;
-    const int c0 = s * kChunk, n = min(kChunk, V - c0);
-    const int seg0 = wave * kSeg;  // this wave's segment, relative to the chunk
-    double lw = 0.0, le = 0.0;
-    if constexpr (kVec) {
-      // All of the lane's 16-byte loads go out before any is unpacked.
-      uint4 zr[kGroupsPerLane][kZVec], qr[kGroupsPerLane][2];
-#pragma unroll
-      for (int g = 0; g < kGroupsPerLane; ++g) {
-        const int v0 = c0 + seg0 + (g * 64 + lane) * kGroup;
-        const bool in = v0 < c0 + n;
-#pragma unroll
-        for (int h = 0; h < kZVec; ++h)
-          zr[g][h] = in ? stream_load(z + v0 + h * (16 / sizeof(LT))) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          qr[g][h] = (in && q != nullptr) ? stream_load(q + v0 + 4 * h) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int g = 0; g < kGroupsPerLane; ++g) {
-        const int v0 = seg0 + (g * 64 + lane) * kGroup;
-        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
-#pragma unroll
-        for (int h = 0; h < kZVec; ++h)
-          unpack(zr[g][h], zv + h * (16 / sizeof(LT)), static_cast<const LT*>(nullptr));
-        unpack(qr[g][0], qv, static_cast<const float*>(nullptr));
-        unpack(qr[g][1], qv + 4, static_cast<const float*>(nullptr));
-        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
-        lw += gw;
-        le += ge;
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < kGroupsPerLane; ++g) {
-        const int v0 = seg0 + (g * 64 + lane) * kGroup;
-        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
-        load_group<LT, false>(z, q, c0 + v0, min(kGroup, n - v0), zv, qv);
-        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
-        lw += gw;
-        le += ge;
-      }
-    }
-    lw = wave_sum(lw);
-    le = wave_sum(le);
-    if (lane == 0) segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
+  const int s = blockIdx.x, b = b0 + static_cast<int>(blockIdx.y);
+  if (wave == 0) {
+    const int kb = num_draft ? num_draft[b] : K;
+    const float T = greedy_all ? 0.f : temperature[b];
+    const SeqState st = accept_sequence(onehot, uniforms, gathers, draft_probs != nullptr, b, kb,
+                                        T, K, V, S, partials, accept_len, out_tokens, out_probs,
+                                        states, s == 0, lane);
+    if (lane == 0) sh_st = st;
   }
+  __syncthreads();
+  const SeqState st = sh_st;
+  if (st.mode == kNone) return;
+  const long long row = static_cast<long long>(b) * (K + 1) + st.row;
+  const LT* z = logits + row * V;
+  const float* q = st.mode == kResidual
+                       ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
+                       : nullptr;
+  const int c0 = s * kChunk, n = min(kChunk, V - c0);
+  const int seg0 = wave * kSeg;  // this wave's segment, relative to the chunk
+  double lw = 0.0, le = 0.0;
+  if constexpr (kVec) {
+    // All of the lane's 16-byte loads go out before any is unpacked.
+    uint4 zr[kGroupsPerLane][kZVec], qr[kGroupsPerLane][2];
+#pragma unroll
+    for (int g = 0; g < kGroupsPerLane; ++g) {
+      const int v0 = c0 + seg0 + (g * 64 + lane) * kGroup;
+      const bool in = v0 < c0 + n;
+#pragma unroll
+      for (int h = 0; h < kZVec; ++h)
+        zr[g][h] = in ? stream_load(z + v0 + h * (16 / sizeof(LT))) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        qr[g][h] = (in && q != nullptr) ? stream_load(q + v0 + 4 * h) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < kGroupsPerLane; ++g) {
+      const int v0 = seg0 + (g * 64 + lane) * kGroup;
+      float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+#pragma unroll
+      for (int h = 0; h < kZVec; ++h)
+        unpack(zr[g][h], zv + h * (16 / sizeof(LT)), static_cast<const LT*>(nullptr));
+      unpack(qr[g][0], qv, static_cast<const float*>(nullptr));
+      unpack(qr[g][1], qv + 4, static_cast<const float*>(nullptr));
+      group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+      lw += gw;
+      le += ge;
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kGroupsPerLane; ++g) {
+      const int v0 = seg0 + (g * 64 + lane) * kGroup;
+      float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+      load_group<LT, false>(z, q, c0 + v0, min(kGroup, n - v0), zv, qv);
+      group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+      lw += gw;
+      le += ge;
+    }
+  }
+  lw = wave_sum(lw);
+  le = wave_sum(le);
+  if (lane == 0) segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
 }
 
 template <typename LT, bool kVec>
@@ -670,6 +683,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
 }
 
 constexpr long long kMaxGrid = 1 << 20;
+constexpr int kMaxZ = 65535;  // largest grid y / z extent
 
 inline unsigned grid_for(long long work) {
   return static_cast<unsigned>(work < 1 ? 1 : (work < kMaxGrid ? work : kMaxGrid));
@@ -688,40 +702,41 @@ hipError_t launch_typed(const LaunchArgs& a) {
   // The streaming kernel: grid (chunk, row within sequence, sequence), at most 65535 sequences
   // per launch.  With measurement events, the dispatches record them (first start, last end).
   auto stats = vec_stats ? stats_kernel<LT, true> : stats_kernel<LT, false>;
-  constexpr int kMaxZ = 65535;
   for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
     const dim3 grid(S, a.K + 1, min(kMaxZ, a.B - b0));
     hipEvent_t ev0 = b0 == 0 ? a.hot_begin : nullptr;
     hipEvent_t ev1 = b0 + kMaxZ >= a.B ? a.hot_end : nullptr;
     if (ev0 || ev1)
       hipExtLaunchKernelGGL(stats, grid, dim3(kThreads), 0, a.stream, ev0, ev1, 0, logits,
-                            a.num_draft, a.temperature, b0, a.K, a.V, S, a.greedy_all,
-                            a.ws.partials);
+                            a.draft_probs, a.proposed, a.num_draft, a.temperature, b0, a.K, a.V,
+                            S, a.greedy_all, a.ws.partials, a.ws.gathers);
     else
-      stats<<<grid, kThreads, 0, a.stream>>>(logits, a.num_draft, a.temperature, b0, a.K, a.V,
-                                             S, a.greedy_all, a.ws.partials);
+      stats<<<grid, kThreads, 0, a.stream>>>(logits, a.draft_probs, a.proposed, a.num_draft,
+                                             a.temperature, b0, a.K, a.V, S, a.greedy_all,
+                                             a.ws.partials, a.ws.gathers);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  accept_kernel<LT><<<grid_for(a.B), 64, 0, a.stream>>>(
-      logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms, a.B,
-      a.K, a.V, S, a.greedy_all, a.ws.partials, a.accept_len, a.out_tokens, a.out_probs,
-      a.ws.states);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // Accept scan + draw sums: one workgroup per (chunk, sequence); greedy-only calls need just
+  // the chunk-0 workgroups (no draw).
+  auto accept_draw = vec_draw ? accept_draw_kernel<LT, true> : accept_draw_kernel<LT, false>;
+  const int gx = a.greedy_all ? 1 : S;
+  for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
+    const dim3 grid(gx, min(kMaxZ, a.B - b0));
+    accept_draw<<<grid, kThreads, 0, a.stream>>>(
+        logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms, b0,
+        a.K, a.V, S, a.greedy_all, a.ws.partials, a.ws.gathers, a.accept_len, a.out_tokens,
+        a.out_probs, a.ws.states, a.ws.segs);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (a.greedy_all) return hipSuccess;
-  const long long draw_tiles = static_cast<long long>(a.B) * S;
-  if (vec_draw) {
-    draw_sums_kernel<LT, true><<<grid_for(draw_tiles), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.B, a.K, a.V, S, a.ws.states, a.ws.segs);
+  if (vec_draw)
     pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
         a.out_tokens, a.out_probs);
-  } else {
-    draw_sums_kernel<LT, false><<<grid_for(draw_tiles), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.B, a.K, a.V, S, a.ws.states, a.ws.segs);
+  else
     pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
         a.out_tokens, a.out_probs);
-  }
   return hipGetLastError();
 }
 
@@ -735,6 +750,8 @@ WorkspaceLayout workspace_layout(int B, int K, int V) {
   size_t off = 0;
   L.partials = off;
   off = align16(off + rows * S * kWaves * sizeof(RowPartial));
+  L.gathers = off;
+  off = align16(off + static_cast<size_t>(B) * static_cast<size_t>(K) * sizeof(Gather));
   L.states = off;
   off = align16(off + static_cast<size_t>(B) * sizeof(SeqState));
   L.segs = off;
