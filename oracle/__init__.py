@@ -4,7 +4,8 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import 
 package; the library and its binding never do.
 """
 from .verify_oracle import OracleOut, TEMPERATURE_MIN, inverse_cdf, logit_row, target_probs, verify, verify_row
+from .ngram_oracle import ngram_propose, propose_one
 from . import closed_forms
 
 __all__ = ["OracleOut", "TEMPERATURE_MIN", "inverse_cdf", "logit_row", "target_probs", "verify",
-           "verify_row", "closed_forms"]
+           "verify_row", "closed_forms", "ngram_propose", "propose_one"]
