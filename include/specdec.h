@@ -144,6 +144,39 @@ specdec_status specdec_verify_ex(const void* target_logits, int32_t logits_dtype
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  const specdec_options* opts);
 
+/* ---------------------------------------------------------------------------------------
+ * N-gram (prompt-lookup) drafter: the model-free proposer of
+ *   - "Decodificação especulativa explicada" (gsantana.dev), section "A família de
+ *     rascunhos", prompt lookup / n-gram drafting;
+ *   - "ch15 · Speculative Decoding" (snowch.github.io), section "What proposes the tokens";
+ *   - longest match first, after the longest-prefix match in "Speculative decoding: el
+ *     secretario que adelanta lo que va a decir el jefe" (blog.lo0.es), section "Las cinco
+ *     familias modernas".
+ * For history h = tokens[b, 0..L) (L = lengths[b]): for n = min(n_max, L-1) down to n_min,
+ * find the earliest p with h[p..p+n) == h[L-n..L) and p + n <= L - 1; the first n that has one
+ * proposes h[p+n .. min(p+n+K, L)), so 1 <= num_draft[b] <= K.  No occurrence at any n:
+ * num_draft[b] = 0.  L outside [0, capacity]: num_draft[b] = -1.  Unused proposed slots hold
+ * -1.  The rows are one-hot drafts: verify them with draft_onehot[b] = 1.
+ *
+ * tokens      [B, capacity]  int32 histories; slots >= L may be loaded but are ignored.
+ * lengths     [B]            int32 history lengths L.
+ * n_min,n_max                1 <= n_min <= n_max <= SPECDEC_NGRAM_MAX_N.
+ * K                          0 <= K <= SPECDEC_MAX_K proposals per sequence.
+ * proposed    [B, K]   out   int32 (may be NULL when K == 0).
+ * num_draft   [B]      out   int32 (the verify step's num_draft).
+ * workspace                  device scratch of >= specdec_ngram_workspace_size(B, capacity)
+ *                            bytes, 16-byte aligned; no initialisation needed.
+ * Returns SPECDEC_ERR_SHAPE for out-of-range sizes or n_min / n_max, otherwise as for
+ * specdec_verify. */
+#define SPECDEC_NGRAM_MAX_N 32
+
+size_t specdec_ngram_workspace_size(int32_t B, int32_t capacity);
+
+specdec_status specdec_ngram_propose(const int32_t* tokens, const int32_t* lengths, int32_t B,
+                                     int32_t capacity, int32_t n_min, int32_t n_max, int32_t K,
+                                     int32_t* proposed, int32_t* num_draft, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* specdec_status_string(int32_t status);
 

@@ -53,6 +53,10 @@ def load_library():
     lib.specdec_verify_greedy.restype = i32
     lib.specdec_workspace_size.argtypes = [i32, i32, i32]
     lib.specdec_workspace_size.restype = sz
+    lib.specdec_ngram_workspace_size.argtypes = [i32, i32]
+    lib.specdec_ngram_workspace_size.restype = sz
+    lib.specdec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.specdec_ngram_propose.restype = i32
     lib.specdec_status_string.argtypes = [i32]
     lib.specdec_status_string.restype = ctypes.c_char_p
     lib.specdec_version.argtypes = []
@@ -106,8 +110,8 @@ def _outputs(B, K, device, out, want_probs):
 def _workspace(B, K, V, device, workspace):
     need = specdec_workspace_size(B, K, V)
     if workspace is None:
-        # Zero-filled once: the library's arrival counters start at zero and are left zero.
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
+        # The library needs no initialised workspace.
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     return workspace, need
 
 
@@ -191,6 +195,37 @@ def specdec_verify_greedy(target_logits: torch.Tensor, proposed: torch.Tensor | 
                                        ws.numel(), _stream_handle(stream))
     _raise(status, "specdec_verify_greedy")
     return acc, tok, prb
+
+
+def specdec_ngram_workspace_size(B: int, capacity: int) -> int:
+    return int(load_library().specdec_ngram_workspace_size(int(B), int(capacity)))
+
+
+def specdec_ngram_propose(tokens: torch.Tensor, lengths: torch.Tensor, K: int, *, n_min: int = 1,
+                          n_max: int = 4, out=None, workspace=None, stream=None):
+    """N-gram drafter.  tokens [B, capacity] int32 histories, lengths [B] int32.  Returns
+    (proposed [B, K] int32, num_draft [B] int32), enqueued on ``stream`` without synchronising."""
+    lib = load_library()
+    if tokens.dim() != 2:
+        raise SpecdecError("tokens must be [B, capacity]")
+    B, cap = (int(s) for s in tokens.shape)
+    dev = tokens.device
+    _check(tokens, "tokens", torch.int32, (B, cap), dev)
+    _check(lengths, "lengths", torch.int32, (B,), dev)
+    if out is None:
+        out = (torch.empty((B, K), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    proposed, num_draft = out
+    _check(proposed, "proposed", torch.int32, (B, K), dev)
+    _check(num_draft, "num_draft", torch.int32, (B,), dev)
+    need = specdec_ngram_workspace_size(B, cap)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    status = lib.specdec_ngram_propose(_ptr(tokens), _ptr(lengths), B, cap, int(n_min), int(n_max),
+                                       int(K), _ptr(proposed) if K > 0 else None, _ptr(num_draft),
+                                       _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _raise(status, "specdec_ngram_propose")
+    return proposed, num_draft
 
 
 def inputs_to_device(inp, device) -> dict:

@@ -72,9 +72,51 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   return specdec::launch_verify(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
+specdec_status check_ngram_sizes(int32_t B, int32_t capacity, int32_t n_min, int32_t n_max,
+                                 int32_t K) {
+  if (B < 0 || capacity < 1 || K < 0 || K > SPECDEC_MAX_K) return SPECDEC_ERR_SHAPE;
+  if (n_min < 1 || n_max < n_min || n_max > SPECDEC_NGRAM_MAX_N) return SPECDEC_ERR_SHAPE;
+  if (static_cast<long long>(B) * specdec::ngram_tiles(capacity) >= (1LL << 31))
+    return SPECDEC_ERR_SHAPE;
+  return SPECDEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t specdec_ngram_workspace_size(int32_t B, int32_t capacity) {
+  if (check_ngram_sizes(B, capacity, 1, 1, 0) != SPECDEC_OK || B == 0) return 0;
+  return static_cast<size_t>(B) * specdec::ngram_tiles(capacity) * sizeof(unsigned long long);
+}
+
+specdec_status specdec_ngram_propose(const int32_t* tokens, const int32_t* lengths, int32_t B,
+                                     int32_t capacity, int32_t n_min, int32_t n_max, int32_t K,
+                                     int32_t* proposed, int32_t* num_draft, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const specdec_status st = check_ngram_sizes(B, capacity, n_min, n_max, K);
+  if (st != SPECDEC_OK) return st;
+  if (B == 0) return SPECDEC_OK;
+  if (!tokens || !lengths || !num_draft || !workspace || (K > 0 && !proposed))
+    return SPECDEC_ERR_NULL;
+  if (misaligned(tokens, 4) || misaligned(lengths, 4) || misaligned(proposed, 4) ||
+      misaligned(num_draft, 4) || misaligned(workspace, 16))
+    return SPECDEC_ERR_ALIGN;
+  if (workspace_bytes < specdec_ngram_workspace_size(B, capacity)) return SPECDEC_ERR_WORKSPACE;
+  specdec::NgramArgs a{};
+  a.tokens = tokens;
+  a.lengths = lengths;
+  a.B = B;
+  a.capacity = capacity;
+  a.n_min = n_min;
+  a.n_max = n_max;
+  a.K = K;
+  a.proposed = proposed;
+  a.num_draft = num_draft;
+  a.partials = static_cast<unsigned long long*>(workspace);
+  a.stream = static_cast<hipStream_t>(stream);
+  return specdec::launch_ngram(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
 
 size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V) {
   if (check_sizes(B, K, V, SPECDEC_F32) != SPECDEC_OK || B == 0) return 0;
@@ -120,7 +162,7 @@ const char* specdec_status_string(int32_t status) {
   switch (status) {
     case SPECDEC_OK: return "ok";
     case SPECDEC_ERR_NULL: return "a required pointer is NULL";
-    case SPECDEC_ERR_SHAPE: return "invalid sizes (B, K, V)";
+    case SPECDEC_ERR_SHAPE: return "invalid sizes or parameters";
     case SPECDEC_ERR_DTYPE: return "unsupported logits dtype";
     case SPECDEC_ERR_ALIGN: return "a tensor is not aligned to its element size";
     case SPECDEC_ERR_WORKSPACE: return "workspace too small";

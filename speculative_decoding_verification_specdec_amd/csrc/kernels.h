@@ -96,4 +96,22 @@ struct LaunchArgs {
 
 hipError_t launch_verify(const LaunchArgs& a);
 
+// ---- n-gram drafter (ngram.hip) ----
+constexpr int kNgramTile = 4096;   // candidate positions per workgroup
+constexpr int kNgramMaxN = 32;     // longest suffix tried
+
+inline int ngram_tiles(int capacity) { return (capacity + kNgramTile - 1) / kNgramTile; }
+
+struct NgramArgs {
+  const int32_t* tokens;     // [B, capacity]
+  const int32_t* lengths;    // [B]
+  int B, capacity, n_min, n_max, K;
+  int32_t* proposed;         // [B, K] (may be null when K == 0)
+  int32_t* num_draft;        // [B]
+  unsigned long long* partials;  // workspace [B * ngram_tiles(capacity)]
+  hipStream_t stream;
+};
+
+hipError_t launch_ngram(const NgramArgs& a);
+
 }  // namespace specdec

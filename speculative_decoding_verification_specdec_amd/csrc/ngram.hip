@@ -1,0 +1,160 @@
+// gfx950 kernels of the n-gram (prompt-lookup) drafter.
+//
+// The drafter is the model-free one the pages describe: find where the most recent tokens of
+// the sequence appeared earlier in it and propose what followed there ("Decodificação
+// especulativa explicada", gsantana.dev, section "A família de rascunhos", prompt lookup; "ch15 ·
+// Speculative Decoding", snowch.github.io, section "What proposes the tokens"; longest match
+// first after the longest-prefix match in "Speculative decoding: el secretario...",
+// blog.lo0.es, section "Las cinco familias modernas").
+//
+// For history h[0..L) and a follower position e in [1, L-1], let m(e) be the length of the
+// longest common run h[e-j] == h[L-j], j = 1, 2, ..., capped at min(n_max, e).  The n-token
+// suffix occurs at p = e - n (with at least one follower) iff m(e) >= n, so the longest suffix
+// that occurs is N = max_e m(e) and its earliest occurrence ends at the smallest e with
+// m(e) = N.  Both fall out of one max-reduction of the key (m(e) << 32) | (2^32 - 1 - e).
+//
+// Two kernels, no atomics:
+//   ngram_match_kernel  one 256-thread workgroup per (4096-position tile, sequence): the tile
+//       and a 32-token halo are staged in LDS with 16-byte loads, each thread extends the
+//       match of 16 positions (consecutive threads on consecutive positions), and the
+//       workgroup's best key goes to the workspace.
+//   ngram_emit_kernel   one wave per sequence: max of the tile keys, then the proposal is
+//       copied from the history.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace specdec {
+namespace {
+
+constexpr int kNgThreads = 256;
+constexpr int kNgPer = kNgramTile / kNgThreads;  // 16 positions per thread
+constexpr int kNgHalo = kNgramMaxN;              // tokens staged before the tile
+
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned lo = __shfl_xor(static_cast<unsigned>(v), off, 64);
+    const unsigned hi = __shfl_xor(static_cast<unsigned>(v >> 32), off, 64);
+    v = max_u64(v, (static_cast<unsigned long long>(hi) << 32) | lo);
+  }
+  return v;
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ lengths, int capacity,
+    int n_min, int n_max, int ntiles, unsigned long long* __restrict__ partials) {
+  __shared__ int sh_tok[kNgHalo + kNgramTile];  // sh_tok[i] = h[t0 - kNgHalo + i]
+  __shared__ int sh_suf[kNgramMaxN + 1];        // sh_suf[j] = h[L - j]
+  __shared__ unsigned long long sh_best[kNgThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = static_cast<int>(blockIdx.x / ntiles), tile = static_cast<int>(blockIdx.x % ntiles);
+  const int L = lengths[b];
+  const int t0 = tile * kNgramTile;
+  unsigned long long* out = partials + static_cast<long long>(b) * ntiles + tile;
+  const int nmax = min(n_max, L - 1);
+  // Invalid length, nothing long enough to match, or no follower position in this tile.
+  if (L < 0 || L > capacity || nmax < n_min || t0 > L - 1) {
+    if (tid == 0) *out = 0ull;
+    return;
+  }
+  const int32_t* h = tokens + static_cast<long long>(b) * capacity;
+  if (tid >= 1 && tid <= nmax) sh_suf[tid] = h[L - tid];
+  // Stage h[t0 - kNgHalo, t0 + kNgramTile) where it lies in [0, L); other slots are never
+  // compared (every compared index e - j lies in [0, L - 2]).
+  const int i0 = t0 - kNgHalo;
+  if constexpr (kVec) {
+    constexpr int kVecs = (kNgHalo + kNgramTile) / 4;
+    const int4* hv = reinterpret_cast<const int4*>(h);
+    for (int v = tid; v < kVecs; v += kNgThreads) {
+      const int idx = i0 + 4 * v;  // a multiple of 4; idx < L <= capacity keeps idx + 3 in the row
+      int4 d = make_int4(0, 0, 0, 0);
+      if (idx >= 0 && idx < L) d = hv[idx / 4];
+      sh_tok[4 * v] = d.x;
+      sh_tok[4 * v + 1] = d.y;
+      sh_tok[4 * v + 2] = d.z;
+      sh_tok[4 * v + 3] = d.w;
+    }
+  } else {
+    for (int i = tid; i < kNgHalo + kNgramTile; i += kNgThreads) {
+      const int idx = i0 + i;
+      sh_tok[i] = (idx >= 0 && idx < L) ? h[idx] : 0;
+    }
+  }
+  __syncthreads();
+  unsigned long long best = 0ull;
+#pragma unroll 4
+  for (int r = 0; r < kNgPer; ++r) {
+    const int e = t0 + r * kNgThreads + tid;
+    if (e < 1 || e > L - 1) continue;
+    const int base = kNgHalo + (e - t0);
+    const int jmax = min(nmax, e);
+    int J = 0;
+    while (J < jmax && sh_tok[base - J - 1] == sh_suf[J + 1]) ++J;
+    if (J >= n_min)
+      best = max_u64(best, (static_cast<unsigned long long>(J) << 32) |
+                               (0xffffffffull - static_cast<unsigned>(e)));
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) sh_best[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long v = sh_best[0];
+    for (int w = 1; w < kNgThreads / 64; ++w) v = max_u64(v, sh_best[w]);
+    *out = v;
+  }
+}
+
+__global__ __launch_bounds__(kNgThreads) void ngram_emit_kernel(
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ lengths, int B, int capacity,
+    int K, int ntiles, const unsigned long long* __restrict__ partials,
+    int32_t* __restrict__ proposed, int32_t* __restrict__ num_draft) {
+  const int lane = threadIdx.x & 63;
+  const int b = static_cast<int>(blockIdx.x) * (kNgThreads / 64) + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int L = lengths[b];
+  const bool valid = L >= 0 && L <= capacity;
+  unsigned long long key = 0ull;
+  if (valid) {
+    const unsigned long long* p = partials + static_cast<long long>(b) * ntiles;
+    for (int t = lane; t < ntiles; t += 64) key = max_u64(key, p[t]);
+    key = wave_max_u64(key);
+  }
+  int cnt = 0, e = 0;
+  if (key != 0ull) {
+    e = static_cast<int>(0xffffffffull - (key & 0xffffffffull));
+    cnt = min(K, L - e);
+  }
+  if (lane < K) {
+    const int32_t* h = tokens + static_cast<long long>(b) * capacity;
+    proposed[static_cast<long long>(b) * K + lane] = lane < cnt ? h[e + lane] : -1;
+  }
+  if (lane == 0) num_draft[b] = valid ? cnt : -1;
+}
+
+}  // namespace
+
+hipError_t launch_ngram(const NgramArgs& a) {
+  if (a.B == 0) return hipSuccess;
+  const int ntiles = ngram_tiles(a.capacity);
+  const bool vec = (reinterpret_cast<uintptr_t>(a.tokens) % 16 == 0) && (a.capacity % 4 == 0);
+  const unsigned grid1 = static_cast<unsigned>(static_cast<long long>(a.B) * ntiles);
+  if (vec)
+    ngram_match_kernel<true><<<grid1, kNgThreads, 0, a.stream>>>(
+        a.tokens, a.lengths, a.capacity, a.n_min, a.n_max, ntiles, a.partials);
+  else
+    ngram_match_kernel<false><<<grid1, kNgThreads, 0, a.stream>>>(
+        a.tokens, a.lengths, a.capacity, a.n_min, a.n_max, ntiles, a.partials);
+  const unsigned grid2 = static_cast<unsigned>((a.B + kNgThreads / 64 - 1) / (kNgThreads / 64));
+  ngram_emit_kernel<<<grid2, kNgThreads, 0, a.stream>>>(a.tokens, a.lengths, a.B, a.capacity,
+                                                        a.K, ntiles, a.partials, a.proposed,
+                                                        a.num_draft);
+  return hipGetLastError();
+}
+
+}  // namespace specdec

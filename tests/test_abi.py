@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("specdec_verify", "specdec_verify_greedy", "specdec_verify_ex",
-              "specdec_workspace_size", "specdec_status_string", "specdec_version"):
+              "specdec_workspace_size", "specdec_status_string", "specdec_version",
+              "specdec_ngram_propose", "specdec_ngram_workspace_size"):
         assert n in names
 
 
@@ -85,3 +86,35 @@ def test_greedy_entry_point_errors(lib):
     assert g(FAKE, 1, FAKE, None, 4, 3, 64, FAKE, FAKE, None, FAKE, 16, None) == -5
     assert g(FAKE, 1, None, None, 4, 3, 64, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
     assert g(FAKE + 1, 1, FAKE, None, 4, 3, 64, FAKE, FAKE, None, FAKE, 1 << 20, None) == -4
+
+
+def _ngram(lib, **kw):
+    a = dict(tok=FAKE, lens=FAKE, B=4, cap=100, n_min=1, n_max=4, K=5, prop=FAKE, nd=FAKE,
+             ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.specdec_ngram_propose(a["tok"], a["lens"], a["B"], a["cap"], a["n_min"],
+                                     a["n_max"], a["K"], a["prop"], a["nd"], a["ws"], a["wsb"],
+                                     a["stream"])
+
+
+def test_ngram_workspace_size(lib):
+    assert lib.specdec_ngram_workspace_size(0, 100) == 0
+    assert lib.specdec_ngram_workspace_size(3, 0) == 0
+    assert lib.specdec_ngram_workspace_size(3, 4096) == 3 * 8
+    assert lib.specdec_ngram_workspace_size(3, 4097) == 3 * 2 * 8
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -2), (dict(cap=0), -2), (dict(K=-1), -2), (dict(K=64), -2),
+    (dict(n_min=0), -2), (dict(n_min=3, n_max=2), -2), (dict(n_max=33), -2),
+    (dict(tok=None), -1), (dict(lens=None), -1), (dict(nd=None), -1), (dict(ws=None), -1),
+    (dict(prop=None), -1),
+    (dict(tok=FAKE + 2), -4), (dict(prop=FAKE + 1), -4), (dict(ws=FAKE + 4), -4),
+    (dict(wsb=4), -5),
+])
+def test_ngram_host_side_errors(lib, kw, status):
+    assert _ngram(lib, **kw) == status
+
+
+def test_ngram_empty_batch_and_k0(lib):
+    assert _ngram(lib, B=0, tok=None, lens=None, nd=None, ws=None, prop=None) == 0
