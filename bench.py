@@ -121,6 +121,96 @@ def algorithmic_bytes(inp, acc_np):
     return logits, logits + small + draft_rows
 
 
+def time_replayed(calls, steps, stream):
+    """Mean µs per call of ``calls`` (rotated) replayed from one HIP graph of ``steps`` calls,
+    bracketed by synchronisation and events, after one untimed replay."""
+    import torch
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def bench_ngram(dev, stream, steps=200, replicas=20):
+    """The n-gram drafter on 512 histories of 4096-8192 tokens (V = 128256, n = 4..1, K = 8):
+    history tokens scanned per second and the algorithmic bytes (4 per history token read,
+    plus the proposals) against the HBM peak.  ``replicas`` copies (~340 MB) rotate so the
+    Infinity Cache cannot hold them."""
+    import numpy as np
+    import torch
+    from speculative_decoding_verification_specdec_amd import (specdec_ngram_propose,
+                                                               specdec_ngram_workspace_size)
+    from speculative_decoding_verification_specdec_amd.contexts import ngram_workload
+    h = ngram_workload()
+    K, n_min, n_max = 8, 1, 4
+    ws = torch.empty(specdec_ngram_workspace_size(h.B, h.capacity), dtype=torch.uint8, device=dev)
+    out = (torch.empty((h.B, K), dtype=torch.int32, device=dev),
+           torch.empty(h.B, dtype=torch.int32, device=dev))
+    calls = []
+    for _ in range(replicas):
+        t = torch.from_numpy(h.tokens).to(dev)
+        ln = torch.from_numpy(h.lengths).to(dev)
+        calls.append(lambda t=t, ln=ln: specdec_ngram_propose(t, ln, K, n_min=n_min, n_max=n_max,
+                                                              out=out, workspace=ws))
+    us = time_replayed(calls, steps, stream)
+    nd = out[1].cpu().numpy()
+    toks = float(h.lengths.astype(np.int64).sum())
+    nbytes = 4.0 * toks + 4.0 * h.B + 4.0 * h.B * (K + 1)
+    return {
+        "workload": "512 token histories, length U{4096..8192}, V=128256, half the segments "
+                    "copied from earlier in the history; n = 4..1, K = 8",
+        "us_per_call": us, "history_tokens_per_s": toks / (us * 1e-6),
+        "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
+        "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "sequences_proposing": int((nd > 0).sum()),
+    }
+
+
+def bench_commit(dev, stream, steps=400):
+    """The commit step on the ragged batch's shape: B = 512 sequences, K = 8, accept lengths
+    U{0..8}, histories of capacity 8192 with lengths U{4096..8000}, both cache lengths rolled
+    back, the packed stream and offsets written.  Latency-bound (a few KB move)."""
+    import numpy as np
+    import torch
+    from speculative_decoding_verification_specdec_amd import specdec_commit
+    B, K, cap = 512, 8, 8192
+    rng = np.random.default_rng(21)
+    acc = torch.from_numpy(rng.integers(0, K + 1, size=B).astype(np.int32)).to(dev)
+    out = torch.from_numpy(rng.integers(0, 128256, size=(B, K + 1)).astype(np.int32)).to(dev)
+    seq0 = rng.integers(4096, 8001, size=B).astype(np.int32)
+    tokens = torch.zeros((B, cap), dtype=torch.int32, device=dev)
+    seq = torch.from_numpy(seq0).to(dev)
+    tkv = torch.from_numpy(seq0 + K).to(dev)
+    dkv = torch.from_numpy(seq0 + K - 1).to(dev)
+    packed = (torch.empty(B * (K + 1), dtype=torch.int32, device=dev),
+              torch.empty(B + 1, dtype=torch.int32, device=dev))
+    base = torch.from_numpy(seq0).to(dev)
+
+    def call():
+        # Lengths are reset by a device copy first so every call commits the same round.
+        seq.copy_(base)
+        specdec_commit(acc, out, seq, tokens=tokens, target_kv_len=tkv, draft_kv_len=dkv,
+                       out=packed)
+    us = time_replayed([call], steps, stream)
+    return {"workload": "B=512, K=8, accept lengths U{0..8}, history capacity 8192",
+            "us_per_call_including_length_reset_copy": us,
+            "sequences_per_s": B / (us * 1e-6)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +219,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the drafter / commit / match-mode / telemetry measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -277,6 +369,11 @@ def main():
             "rejected_sequences": int((acc_np < K).sum()),
         },
     }
+    if not args.no_next_rows:
+        print("[bench] n-gram drafter", file=sys.stderr, flush=True)
+        res["next_rows"] = {"ngram_propose": bench_ngram(dev, stream)}
+        print("[bench] commit", file=sys.stderr, flush=True)
+        res["next_rows"]["commit"] = bench_commit(dev, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

@@ -177,6 +177,37 @@ specdec_status specdec_ngram_propose(const int32_t* tokens, const int32_t* lengt
                                      int32_t* proposed, int32_t* num_draft, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Commit of a verified round: cache rollback and ragged compaction.  The step after verify in
+ *   - "Decodificação especulativa explicada" (gsantana.dev), section "O ciclo de rascunho e
+ *     verificação": the target's cache entries past the first rejection are dropped by
+ *     truncating or moving a pointer back, and the drafter's cache is rolled back the same way;
+ *   - "ch15 · Speculative Decoding" (snowch.github.io), section "The build";
+ *   - "Speculative decoding: el secretario..." (blog.lo0.es), section "Pitfalls
+ *     operacionales": each sequence accepts a different number of tokens per round.
+ * For sequence b with A = accept_len[b] and L = seq_len[b] (tokens before the round), the
+ * round emits n_b = A + 1 tokens out_tokens[b, 0..A]:
+ *   tokens[b, L .. L+A] = out_tokens[b, 0..A];  seq_len[b] = L + A + 1;
+ *   target_kv_len[b] = min(target_kv_len[b], L + A);  draft_kv_len[b] likewise
+ *   (only the entries of the L prefix tokens and the A accepted drafts can be kept);
+ *   packed_offsets[b] = n_0 + ... + n_{b-1}, packed_offsets[B] = the total, and
+ *   packed_tokens[packed_offsets[b] + i] = out_tokens[b, i].
+ * A sequence with A outside [0, K], L < 0, or L + A + 1 > capacity commits nothing: n_b = 0
+ * and its lengths are left unchanged.
+ *
+ * accept_len      [B]        int32, from specdec_verify.
+ * out_tokens      [B, K+1]   int32, from specdec_verify.
+ * tokens          [B, capacity] int32 histories, appended in place; NULL = no history.
+ * seq_len         [B]        int32 in/out.
+ * target_kv_len   [B]        int32 in/out, or NULL.   draft_kv_len [B] likewise.
+ * packed_tokens   [B*(K+1)]  int32 out, or NULL.      packed_offsets [B+1] int32 out, or NULL.
+ * Needs no workspace.  SPECDEC_ERR_SHAPE: B < 0, K outside [0, SPECDEC_MAX_K], capacity < 1,
+ * or B*(K+1) >= 2^31. */
+specdec_status specdec_commit(const int32_t* accept_len, const int32_t* out_tokens, int32_t B,
+                              int32_t K, int32_t* tokens, int32_t capacity, int32_t* seq_len,
+                              int32_t* target_kv_len, int32_t* draft_kv_len,
+                              int32_t* packed_tokens, int32_t* packed_offsets, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* specdec_status_string(int32_t status);
 

@@ -7,8 +7,9 @@ raises if the library is missing.
 """
 from .binding import (SpecdecError, specdec_verify, specdec_verify_greedy, specdec_workspace_size,
                       specdec_status_string, library_path, load_library,
-                      inputs_to_device, specdec_ngram_propose, specdec_ngram_workspace_size)
+                      inputs_to_device, specdec_ngram_propose, specdec_ngram_workspace_size,
+                      specdec_commit)
 
 __all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_workspace_size",
            "specdec_status_string", "library_path", "load_library", "inputs_to_device",
-           "specdec_ngram_propose", "specdec_ngram_workspace_size"]
+           "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit"]

@@ -57,6 +57,8 @@ def load_library():
     lib.specdec_ngram_workspace_size.restype = sz
     lib.specdec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.specdec_ngram_propose.restype = i32
+    lib.specdec_commit.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.specdec_commit.restype = i32
     lib.specdec_status_string.argtypes = [i32]
     lib.specdec_status_string.restype = ctypes.c_char_p
     lib.specdec_version.argtypes = []
@@ -226,6 +228,49 @@ def specdec_ngram_propose(tokens: torch.Tensor, lengths: torch.Tensor, K: int, *
                                        _ptr(workspace), workspace.numel(), _stream_handle(stream))
     _raise(status, "specdec_ngram_propose")
     return proposed, num_draft
+
+
+def specdec_commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, seq_len: torch.Tensor, *,
+                   tokens: torch.Tensor | None = None, capacity: int | None = None,
+                   target_kv_len: torch.Tensor | None = None,
+                   draft_kv_len: torch.Tensor | None = None, packed: bool = True, out=None,
+                   stream=None):
+    """Commit a verified round in place: append the emitted tokens to ``tokens`` [B, capacity]
+    (optional), advance ``seq_len`` [B], roll ``target_kv_len`` / ``draft_kv_len`` [B] back
+    (optional), and with ``packed`` return (packed_tokens [B*(K+1)], packed_offsets [B+1]);
+    otherwise return None.  ``capacity`` defaults to tokens.shape[1]."""
+    lib = load_library()
+    if out_tokens.dim() != 2:
+        raise SpecdecError("out_tokens must be [B, K+1]")
+    B, K1 = (int(s) for s in out_tokens.shape)
+    dev = out_tokens.device
+    _check(accept_len, "accept_len", torch.int32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, K1), dev)
+    _check(seq_len, "seq_len", torch.int32, (B,), dev)
+    if tokens is not None:
+        if tokens.dim() != 2:
+            raise SpecdecError("tokens must be [B, capacity]")
+        _check(tokens, "tokens", torch.int32, (B, int(tokens.shape[1])), dev)
+        cap = int(tokens.shape[1])
+        if capacity is not None and int(capacity) != cap:
+            raise SpecdecError("capacity differs from tokens.shape[1]")
+    elif capacity is None:
+        raise SpecdecError("capacity is required when no history tensor is given")
+    else:
+        cap = int(capacity)
+    _check(target_kv_len, "target_kv_len", torch.int32, (B,), dev, optional=True)
+    _check(draft_kv_len, "draft_kv_len", torch.int32, (B,), dev, optional=True)
+    pk = off = None
+    if packed:
+        if out is None:
+            out = (torch.empty(max(B * K1, 1), dtype=torch.int32, device=dev),
+                   torch.empty(B + 1, dtype=torch.int32, device=dev))
+        pk, off = out
+    status = lib.specdec_commit(_ptr(accept_len), _ptr(out_tokens), B, K1 - 1, _ptr(tokens), cap,
+                                _ptr(seq_len), _ptr(target_kv_len), _ptr(draft_kv_len), _ptr(pk),
+                                _ptr(off), _stream_handle(stream))
+    _raise(status, "specdec_commit")
+    return (pk, off) if packed else None
 
 
 def inputs_to_device(inp, device) -> dict:

@@ -158,6 +158,33 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
              stream, nullptr, true);
 }
 
+specdec_status specdec_commit(const int32_t* accept_len, const int32_t* out_tokens, int32_t B,
+                              int32_t K, int32_t* tokens, int32_t capacity, int32_t* seq_len,
+                              int32_t* target_kv_len, int32_t* draft_kv_len,
+                              int32_t* packed_tokens, int32_t* packed_offsets, void* stream) {
+  if (B < 0 || K < 0 || K > SPECDEC_MAX_K || capacity < 1) return SPECDEC_ERR_SHAPE;
+  if (static_cast<long long>(B) * (K + 1) >= (1LL << 31)) return SPECDEC_ERR_SHAPE;
+  if (B > 0 && (!accept_len || !out_tokens || !seq_len)) return SPECDEC_ERR_NULL;
+  if (misaligned(accept_len, 4) || misaligned(out_tokens, 4) || misaligned(tokens, 4) ||
+      misaligned(seq_len, 4) || misaligned(target_kv_len, 4) || misaligned(draft_kv_len, 4) ||
+      misaligned(packed_tokens, 4) || misaligned(packed_offsets, 4))
+    return SPECDEC_ERR_ALIGN;
+  specdec::CommitArgs a{};
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.B = B;
+  a.K = K;
+  a.capacity = capacity;
+  a.tokens = tokens;
+  a.seq_len = seq_len;
+  a.target_kv = target_kv_len;
+  a.draft_kv = draft_kv_len;
+  a.packed = packed_tokens;
+  a.offsets = packed_offsets;
+  a.stream = static_cast<hipStream_t>(stream);
+  return specdec::launch_commit(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
 const char* specdec_status_string(int32_t status) {
   switch (status) {
     case SPECDEC_OK: return "ok";

@@ -1,0 +1,86 @@
+// gfx950 kernel of the post-verify commit: cache rollback and ragged compaction.
+//
+// After the verify step each sequence keeps its A accepted drafts plus the correction or bonus
+// token, so its history grows by A + 1 tokens and every cache entry past the first L + A tokens
+// is dropped by moving the cache length back ("Decodificação especulativa explicada",
+// gsantana.dev, section "O ciclo de rascunho e verificação": truncate the cache or move a
+// pointer back, for the target and the drafter alike; "ch15 · Speculative Decoding",
+// snowch.github.io, section "The build").  The emitted tokens of the whole batch are also packed
+// into one ragged stream with exclusive-prefix-sum offsets, since every sequence accepts a
+// different number ("Speculative decoding: el secretario...", blog.lo0.es, section "Pitfalls
+// operacionales", continuous batching).
+//
+// One 1024-thread workgroup: thread t owns sequences [t*per, (t+1)*per); their emitted counts
+// are summed, scanned across the workgroup (wave shuffles, then the 16 wave totals in LDS),
+// and each thread writes its sequences' offsets, tokens and lengths.  No atomics.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace specdec {
+namespace {
+
+constexpr int kCmThreads = 1024;
+constexpr int kCmWaves = kCmThreads / 64;
+
+// Tokens sequence b commits: A + 1, or 0 for an invalid row / length / overflow.
+__device__ __forceinline__ int emitted_count(int A, int L, int K, int capacity) {
+  if (A < 0 || A > K || L < 0) return 0;
+  if (static_cast<long long>(L) + A + 1 > capacity) return 0;
+  return A + 1;
+}
+
+__global__ __launch_bounds__(kCmThreads) void commit_kernel(
+    const int32_t* __restrict__ accept_len, const int32_t* __restrict__ out_tokens, int B, int K,
+    int capacity, int32_t* __restrict__ tokens, int32_t* __restrict__ seq_len,
+    int32_t* __restrict__ target_kv, int32_t* __restrict__ draft_kv,
+    int32_t* __restrict__ packed, int32_t* __restrict__ offsets) {
+  __shared__ int sh_wave[kCmWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (B + kCmThreads - 1) / kCmThreads;
+  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += emitted_count(accept_len[b], seq_len[b], K, capacity);
+  // Exclusive scan of the per-thread counts over the workgroup.
+  int inc = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) sh_wave[wave] = inc;
+  __syncthreads();
+  int base = inc - local;
+  for (int w = 0; w < wave; ++w) base += sh_wave[w];
+  for (int b = b0; b < b1; ++b) {
+    const int A = accept_len[b], L = seq_len[b];
+    const int em = emitted_count(A, L, K, capacity);
+    if (offsets) offsets[b] = base;
+    if (em > 0) {
+      const int32_t* src = out_tokens + static_cast<long long>(b) * (K + 1);
+      int32_t* dst = tokens ? tokens + static_cast<long long>(b) * capacity + L : nullptr;
+      for (int i = 0; i < em; ++i) {
+        const int32_t t = src[i];
+        if (dst) dst[i] = t;
+        if (packed) packed[base + i] = t;
+      }
+      seq_len[b] = L + em;
+      if (target_kv) target_kv[b] = min(target_kv[b], L + A);
+      if (draft_kv) draft_kv[b] = min(draft_kv[b], L + A);
+    }
+    base += em;
+  }
+  if (tid == kCmThreads - 1 && offsets) offsets[B] = base;
+}
+
+}  // namespace
+
+hipError_t launch_commit(const CommitArgs& a) {
+  if (a.B == 0 && !a.offsets) return hipSuccess;  // B == 0 still writes offsets[0] = 0
+  commit_kernel<<<1, kCmThreads, 0, a.stream>>>(a.accept_len, a.out_tokens, a.B, a.K,
+                                                a.capacity, a.tokens, a.seq_len, a.target_kv,
+                                                a.draft_kv, a.packed, a.offsets);
+  return hipGetLastError();
+}
+
+}  // namespace specdec

@@ -114,4 +114,20 @@ struct NgramArgs {
 
 hipError_t launch_ngram(const NgramArgs& a);
 
+// ---- commit: rollback and ragged compaction (commit.hip) ----
+struct CommitArgs {
+  const int32_t* accept_len;   // [B]
+  const int32_t* out_tokens;   // [B, K+1]
+  int B, K, capacity;
+  int32_t* tokens;             // [B, capacity] history, or null
+  int32_t* seq_len;            // [B] in/out
+  int32_t* target_kv;          // [B] in/out, or null
+  int32_t* draft_kv;           // [B] in/out, or null
+  int32_t* packed;             // [B*(K+1)] out, or null
+  int32_t* offsets;            // [B+1] out, or null
+  hipStream_t stream;
+};
+
+hipError_t launch_commit(const CommitArgs& a);
+
 }  // namespace specdec

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("specdec_verify", "specdec_verify_greedy", "specdec_verify_ex",
               "specdec_workspace_size", "specdec_status_string", "specdec_version",
-              "specdec_ngram_propose", "specdec_ngram_workspace_size"):
+              "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit"):
         assert n in names
 
 
@@ -118,3 +118,25 @@ def test_ngram_host_side_errors(lib, kw, status):
 
 def test_ngram_empty_batch_and_k0(lib):
     assert _ngram(lib, B=0, tok=None, lens=None, nd=None, ws=None, prop=None) == 0
+
+
+def _commit(lib, **kw):
+    a = dict(acc=FAKE, out=FAKE, B=4, K=3, tok=FAKE, cap=100, sl=FAKE, tkv=None, dkv=None,
+             pk=FAKE, off=FAKE, stream=None)
+    a.update(kw)
+    return lib.specdec_commit(a["acc"], a["out"], a["B"], a["K"], a["tok"], a["cap"], a["sl"],
+                              a["tkv"], a["dkv"], a["pk"], a["off"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -2), (dict(K=-1), -2), (dict(K=64), -2), (dict(cap=0), -2),
+    (dict(acc=None), -1), (dict(out=None), -1), (dict(sl=None), -1),
+    (dict(acc=FAKE + 1), -4), (dict(tok=FAKE + 2), -4), (dict(tkv=FAKE + 3), -4),
+    (dict(off=FAKE + 2), -4),
+])
+def test_commit_host_side_errors(lib, kw, status):
+    assert _commit(lib, **kw) == status
+
+
+def test_commit_empty_batch_without_offsets(lib):
+    assert _commit(lib, B=0, acc=None, out=None, sl=None, tok=None, pk=None, off=None) == 0

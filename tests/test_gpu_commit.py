@@ -1,0 +1,122 @@
+"""GPU parity of the commit step (rollback + ragged compaction) against its CPU oracle, and the
+whole speculative loop on the GPU -- n-gram drafter, greedy verify, commit -- against plain
+greedy decoding of the same toy target.  Integer work: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_verification_specdec_amd import (specdec_commit, specdec_ngram_propose,
+                                                           specdec_verify_greedy)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def t(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def random_round(B, K, cap, seed):
+    rng = np.random.default_rng(seed)
+    acc = rng.integers(-1, K + 1, size=B)
+    out = rng.integers(0, 128256, size=(B, K + 1))
+    for b in range(B):                      # slots past A hold -1, as the verify step writes
+        out[b, max(acc[b], -1) + 1:] = -1
+    seq = rng.integers(0, cap + 1, size=B)
+    seq[: min(B, 3)] = [cap, cap - 1, 0][: min(B, 3)]
+    hist = rng.integers(0, 128256, size=(B, cap))
+    tkv = seq + rng.integers(-2, K + 1, size=B)
+    dkv = seq + rng.integers(-2, K, size=B)
+    return acc, out, seq, hist, tkv, dkv
+
+
+@pytest.mark.parametrize("B,K,cap", [(1, 1, 8), (7, 5, 40), (512, 8, 256), (1024, 3, 64),
+                                     (3000, 8, 128)])
+def test_commit_matches_oracle(B, K, cap):
+    print(f"\n[case] commit B={B} K={K} cap={cap}", flush=True)
+    acc, out, seq, hist, tkv, dkv = random_round(B, K, cap, seed=B + K)
+    tok_d, seq_d, tkv_d, dkv_d = t(hist), t(seq), t(tkv), t(dkv)
+    pk, off = specdec_commit(t(acc), t(out), seq_d, tokens=tok_d, target_kv_len=tkv_d,
+                             draft_kv_len=dkv_d)
+    torch.cuda.synchronize()
+    r_tok, r_seq, r_tkv, r_dkv, r_em, r_off, r_pk = oracle.commit(acc, out, hist, seq, cap, tkv, dkv)
+    assert np.array_equal(tok_d.cpu().numpy(), r_tok)
+    assert np.array_equal(seq_d.cpu().numpy(), r_seq)
+    assert np.array_equal(tkv_d.cpu().numpy(), r_tkv)
+    assert np.array_equal(dkv_d.cpu().numpy(), r_dkv)
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(pk.cpu().numpy()[: r_off[-1]], r_pk)
+
+
+def test_commit_optional_outputs_and_empty_batch():
+    acc, out, seq, hist, tkv, dkv = random_round(50, 4, 30, seed=5)
+    seq_d = t(seq)
+    assert specdec_commit(t(acc), t(out), seq_d, capacity=30, packed=False) is None
+    torch.cuda.synchronize()
+    _, r_seq, *_ = oracle.commit(acc, out, None, seq, 30)
+    assert np.array_equal(seq_d.cpu().numpy(), r_seq)
+    e = torch.empty(0, dtype=torch.int32, device=DEV)
+    pk, off = specdec_commit(e, e.view(0, 4), e, capacity=10)
+    torch.cuda.synchronize()
+    assert off.cpu().tolist() == [0]
+
+
+class ToyTarget:
+    """Next-token logits as a fixed function of the last two tokens (small vocabulary)."""
+
+    def __init__(self, V=16, seed=0):
+        self.V = V
+        self.W = np.random.default_rng(seed).standard_normal((V, V, V)).astype(np.float32) * 3
+
+    def logits(self, hist):
+        a = hist[-2] if len(hist) > 1 else 0
+        return self.W[a, hist[-1]]
+
+
+@pytest.mark.parametrize("B,K,n_max", [(8, 4, 3), (5, 8, 2)])
+def test_speculative_loop_on_gpu_reproduces_greedy_decoding(B, K, n_max):
+    print(f"\n[case] loop B={B} K={K} n_max={n_max}", flush=True)
+    models = [ToyTarget(seed=s) for s in range(B)]
+    prompts = [list(np.random.default_rng(100 + s).integers(0, 16, size=6)) for s in range(B)]
+    n_new = 50
+    cap = 6 + (n_new + 1) * (K + 1)   # finished sequences keep growing until all are done
+    want = []
+    for m, p in zip(models, prompts):
+        h = list(p)
+        for _ in range(n_new):
+            h.append(int(np.argmax(m.logits(h))))
+        want.append(h)
+    hist = np.full((B, cap), -1, dtype=np.int32)
+    for b, p in enumerate(prompts):
+        hist[b, :6] = p
+    hist_d, seq_d = t(hist), t(np.full(B, 6))
+    tkv_d = t(np.full(B, 5))      # cache entries for all but the last token
+    rounds = 0
+    while True:
+        seq = seq_d.cpu().numpy()
+        if (seq >= 6 + n_new).all():
+            break
+        prop_d, nd_d = specdec_ngram_propose(hist_d, seq_d, K, n_min=1, n_max=n_max)
+        prop, nd = prop_d.cpu().numpy(), nd_d.cpu().numpy()
+        h = hist_d.cpu().numpy()
+        rows = np.zeros((B, K + 1, 16), dtype=np.float32)   # the target pass (host toy model)
+        for b in range(B):
+            ctx = list(h[b, :seq[b]])
+            for i in range(nd[b] + 1):
+                rows[b, i] = models[b].logits(ctx + [int(x) for x in prop[b, :i]])
+        acc, tok, _ = specdec_verify_greedy(torch.from_numpy(rows).to(DEV),
+                                            t(np.where(prop >= 0, prop, 0)), num_draft=nd_d,
+                                            want_probs=False)
+        tkv_d += t(nd + 1)         # the target pass wrote the last token's and k drafts' entries
+        specdec_commit(acc, tok, seq_d, tokens=hist_d, target_kv_len=tkv_d, packed=False)
+        torch.cuda.synchronize()
+        a = acc.cpu().numpy()
+        assert ((a >= 0) & (a <= nd)).all()
+        assert (tkv_d.cpu().numpy() == seq_d.cpu().numpy() - 1).all()
+        rounds += 1
+        assert rounds < 200
+    h = hist_d.cpu().numpy()
+    for b in range(B):
+        assert h[b, :6 + n_new].tolist() == want[b][:6 + n_new]
+    assert rounds < n_new
