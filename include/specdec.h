@@ -144,6 +144,22 @@ specdec_status specdec_verify_ex(const void* target_logits, int32_t logits_dtype
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  const specdec_options* opts);
 
+/* Sample-and-match verify: the simpler exact scheme of "Decodificação especulativa
+ * explicada" (gsantana.dev), section "A regra de amostragem por rejeição" (the paragraph after
+ * the biased fallback).  Position i < k_b draws y_i ~ p_i by the inverse CDF above with
+ * uniforms[b, i]; the draft x_i is kept while y_i == x_i; the first y_i != x_i is emitted and
+ * ends the round (A = i); if all k_b are kept the bonus y_k ~ p_k is drawn with
+ * uniforms[b, K] (A = k_b).  Every emitted token is a draw from p; a draft survives with
+ * probability sum_x p(x) q(x), below the rejection rule's sum_x min(p(x), q(x)).  No draft
+ * distribution is read.  Greedy rows, data errors, outputs and workspace are as for
+ * specdec_verify (without the q conditions); a sequence's draft_onehot flag is irrelevant. */
+specdec_status specdec_verify_match(const void* target_logits, int32_t logits_dtype,
+                                    const int32_t* proposed, const int32_t* num_draft,
+                                    const float* temperature, const float* uniforms,
+                                    int32_t B, int32_t K, int32_t V,
+                                    int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * N-gram (prompt-lookup) drafter: the model-free proposer of
  *   - "Decodificação especulativa explicada" (gsantana.dev), section "A família de

@@ -8,8 +8,9 @@ raises if the library is missing.
 from .binding import (SpecdecError, specdec_verify, specdec_verify_greedy, specdec_workspace_size,
                       specdec_status_string, library_path, load_library,
                       inputs_to_device, specdec_ngram_propose, specdec_ngram_workspace_size,
-                      specdec_commit)
+                      specdec_commit, specdec_verify_match)
 
 __all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_workspace_size",
            "specdec_status_string", "library_path", "load_library", "inputs_to_device",
-           "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit"]
+           "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit",
+           "specdec_verify_match"]

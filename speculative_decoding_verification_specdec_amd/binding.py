@@ -51,6 +51,9 @@ def load_library():
     lib.specdec_verify_ex.restype = i32
     lib.specdec_verify_greedy.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.specdec_verify_greedy.restype = i32
+    lib.specdec_verify_match.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp,
+                                         sz, vp]
+    lib.specdec_verify_match.restype = i32
     lib.specdec_workspace_size.argtypes = [i32, i32, i32]
     lib.specdec_workspace_size.restype = sz
     lib.specdec_ngram_workspace_size.argtypes = [i32, i32]
@@ -196,6 +199,40 @@ def specdec_verify_greedy(target_logits: torch.Tensor, proposed: torch.Tensor | 
                                        B, K, V, _ptr(acc), _ptr(tok), _ptr(prb), _ptr(ws),
                                        ws.numel(), _stream_handle(stream))
     _raise(status, "specdec_verify_greedy")
+    return acc, tok, prb
+
+
+def specdec_verify_match(target_logits: torch.Tensor, proposed: torch.Tensor | None,
+                         temperature: torch.Tensor, uniforms: torch.Tensor, *,
+                         num_draft: torch.Tensor | None = None, out=None, workspace=None,
+                         want_probs: bool = True, stream=None):
+    """Sample-and-match verify (no draft distribution).  Shapes as for specdec_verify.  Returns
+    (accept_len, out_tokens, out_probs or None)."""
+    lib = load_library()
+    if target_logits.dim() != 3:
+        raise SpecdecError("target_logits must be [B, K+1, V]")
+    B, K1, V = (int(s) for s in target_logits.shape)
+    K = K1 - 1
+    dev = target_logits.device
+    if target_logits.dtype == torch.bfloat16:
+        dt = SPECDEC_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = SPECDEC_F32
+    else:
+        raise SpecdecError(f"target_logits dtype {target_logits.dtype} is not bf16/fp32")
+    if not target_logits.is_contiguous():
+        raise SpecdecError("target_logits must be contiguous")
+    _check(proposed, "proposed", torch.int32, (B, K), dev, optional=(K == 0))
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
+    acc, tok, prb = _outputs(B, K, dev, out, want_probs)
+    ws, need = _workspace(B, K, V, dev, workspace)
+    status = lib.specdec_verify_match(_ptr(target_logits), dt, _ptr(proposed), _ptr(num_draft),
+                                      _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc),
+                                      _ptr(tok), _ptr(prb), _ptr(ws), ws.numel(),
+                                      _stream_handle(stream))
+    _raise(status, "specdec_verify_match")
     return acc, tok, prb
 
 

@@ -29,7 +29,7 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
                    const int32_t* num_draft, const float* temperature, const float* uniforms,
                    int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
                    float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
-                   const specdec_options* opts, bool greedy_all) {
+                   const specdec_options* opts, bool greedy_all, bool match = false) {
   specdec_status st = check_sizes(B, K, V, logits_dtype);
   if (st != SPECDEC_OK) return st;
   if (B == 0) return SPECDEC_OK;
@@ -58,6 +58,7 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.K = K;
   a.V = V;
   a.greedy_all = greedy_all ? 1 : 0;
+  a.match = match ? 1 : 0;
   a.accept_len = accept_len;
   a.out_tokens = out_tokens;
   a.out_probs = out_probs;
@@ -156,6 +157,17 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
   return run(target_logits, logits_dtype, nullptr, nullptr, proposed, num_draft, nullptr,
              nullptr, B, K, V, accept_len, out_tokens, out_probs, workspace, workspace_bytes,
              stream, nullptr, true);
+}
+
+specdec_status specdec_verify_match(const void* target_logits, int32_t logits_dtype,
+                                    const int32_t* proposed, const int32_t* num_draft,
+                                    const float* temperature, const float* uniforms, int32_t B,
+                                    int32_t K, int32_t V, int32_t* accept_len,
+                                    int32_t* out_tokens, float* out_probs, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return run(target_logits, logits_dtype, nullptr, nullptr, proposed, num_draft, temperature,
+             uniforms, B, K, V, accept_len, out_tokens, out_probs, workspace, workspace_bytes,
+             stream, nullptr, false, true);
 }
 
 specdec_status specdec_commit(const int32_t* accept_len, const int32_t* out_tokens, int32_t B,

@@ -19,7 +19,7 @@ struct RowPartial {
   float m;      // max logit in the sub-chunk (-inf if none)
   float s;      // sum of exp2((z - m) * c) over the sub-chunk
   int32_t arg;  // lowest index attaining m (greedy rows only)
-  int32_t pad;
+  float pre;    // match mode: the same sum over the tokens below the drafted id x_i
 };
 
 // What the draw pass must sample for one sequence.
@@ -34,7 +34,7 @@ struct SeqState {
   int32_t mode;   // SampleMode
   int32_t row;    // target row j the draw is taken from
   int32_t excl;   // x_j for kResidualOnehot
-  int32_t pad0;
+  int32_t ucol;   // uniforms column of the draw (K; in match mode the mismatching position)
   float c;        // log2(e) / T
   float m;        // max of row j
   float s;        // sum_v exp2((z_j[v] - m) * c) of row j
@@ -85,6 +85,7 @@ struct LaunchArgs {
   const float* uniforms;
   int B, K, V;
   int greedy_all;            // 1: every row is temperature 0 (no q, T, u read)
+  int match;                 // 1: sample-and-match mode (q never read)
   int32_t* accept_len;
   int32_t* out_tokens;
   float* out_probs;

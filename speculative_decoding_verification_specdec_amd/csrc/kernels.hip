@@ -168,6 +168,50 @@ __device__ __forceinline__ MaxSum fold_chunk(const float (&x)[kPerThread], float
   return MaxSum{bm, ((s0 + s1) + (s2 + s3)) * __builtin_amdgcn_exp2f(-lo)};
 }
 
+// Match mode: (max, sum, sum below the drafted id) of the thread's logits, with the masked
+// sum taken in the same order and against the same reference as the whole sum.
+struct MaxSumPre {
+  float m;
+  float s;
+  float p;
+};
+
+__device__ __forceinline__ MaxSumPre merge_msp(const MaxSumPre& x, const MaxSumPre& y, float c) {
+  const float m = fmaxf(x.m, y.m);
+  if (m == -INFINITY) return MaxSumPre{m, x.s + y.s, x.p + y.p};
+  const float fx = __builtin_amdgcn_exp2f((x.m - m) * c), fy = __builtin_amdgcn_exp2f((y.m - m) * c);
+  return MaxSumPre{m, x.s * fx + y.s * fy, x.p * fx + y.p * fy};
+}
+
+template <typename LT, bool kVec>
+__device__ __forceinline__ int tok_of(int c0, int lane, int j);
+
+template <typename LT, bool kVec>
+__device__ __forceinline__ MaxSumPre fold_chunk_pre(const float (&x)[kPerThread], float c, int c0,
+                                                    int lane, int xid) {
+  float bm = x[0];
+#pragma unroll
+  for (int j = 1; j < kPerThread; ++j) bm = fmaxf(bm, x[j]);
+  const float ref = (bm == -INFINITY) ? 0.f : bm;
+  const float hi = ref * c;
+  const float lo = fmaf(ref, c, -hi);
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPerThread; j += 4) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(x[j], c, -hi));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(x[j + 1], c, -hi));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(x[j + 2], c, -hi));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(x[j + 3], c, -hi));
+    s0 += e0; s1 += e1; s2 += e2; s3 += e3;
+    p0 += tok_of<LT, kVec>(c0, lane, j) < xid ? e0 : 0.f;
+    p1 += tok_of<LT, kVec>(c0, lane, j + 1) < xid ? e1 : 0.f;
+    p2 += tok_of<LT, kVec>(c0, lane, j + 2) < xid ? e2 : 0.f;
+    p3 += tok_of<LT, kVec>(c0, lane, j + 3) < xid ? e3 : 0.f;
+  }
+  const float f = __builtin_amdgcn_exp2f(-lo);
+  return MaxSumPre{bm, ((s0 + s1) + (s2 + s3)) * f, ((p0 + p1) + (p2 + p3)) * f};
+}
+
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
@@ -255,7 +299,7 @@ __device__ __forceinline__ SeqState accept_sequence(const uint8_t* onehot, const
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int j = sl + 16 * (t0 + t);
-          pb[h][t] = (ri <= K && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0};
+          pb[h][t] = (ri <= K && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0.f};
         }
       }
 #pragma unroll
@@ -310,7 +354,7 @@ __device__ __forceinline__ SeqState accept_sequence(const uint8_t* onehot, const
   SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
   if (ok && !greedy) {  // A is wave-uniform: lane A's row is the one to draw from
     const int mode = (A == kb) ? kBonus : (is_onehot ? kResidualOnehot : kResidual);
-    out = SeqState{mode, A, __shfl(x, A, 64), 0, c, __shfl(st.m, A, 64), __shfl(st.s, A, 64),
+    out = SeqState{mode, A, __shfl(x, A, 64), K, c, __shfl(st.m, A, 64), __shfl(st.s, A, 64),
                    0.f};
   }
   if (write) {
@@ -336,9 +380,159 @@ __device__ __forceinline__ SeqState accept_sequence(const uint8_t* onehot, const
 }
 
 // ------------------------------------------------------------------------------------------
+// Match mode ("Decodificação especulativa explicada", section "A regra de amostragem por
+// rejeição", the simpler exact scheme): position i draws y_i from p_i with u[b, i] (the bonus
+// position with u[b, K]) and the draft is kept while y_i == x_i.  The inverse-CDF draw picks x_i
+// exactly when its interval [C(x_i - 1), C(x_i)) of the running sum holds t = u * total, so the
+// scan decides every position from the row's total S_i, the sum P_i below x_i and x_i's own
+// weight -- no pass over the row.  Only the first mismatching position (or the bonus) is then
+// drawn by the draw kernels, as a plain sample of p with its own uniform column.
+// ------------------------------------------------------------------------------------------
+struct StatD {
+  float m;
+  double s;  // sum of exp2((z - m) * c)
+  double p;  // the same sum below the drafted id
+};
+
+__device__ __forceinline__ StatD merge_d(const StatD& x, const StatD& y, float c) {
+  const float m = fmaxf(x.m, y.m);
+  if (m == -INFINITY) return StatD{m, x.s + y.s, x.p + y.p};
+  const double fx = __builtin_amdgcn_exp2f((x.m - m) * c);
+  const double fy = __builtin_amdgcn_exp2f((y.m - m) * c);
+  return StatD{m, x.s * fx + y.s * fy, x.p * fx + y.p * fy};
+}
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, 0xf, 0xf,
+                                             false);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ StatD dpp_statd(const StatD& v) {
+  return StatD{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.m), kCtrl, 0xf, 0xf,
+                                                          false)),
+               dpp_d<kCtrl>(v.s), dpp_d<kCtrl>(v.p)};
+}
+
+__device__ __forceinline__ StatD row16_reduce_d(StatD v, float c) {
+  v = merge_d(v, dpp_statd<0xB1>(v), c);
+  v = merge_d(v, dpp_statd<0x4E>(v), c);
+  v = merge_d(v, dpp_statd<0x124>(v), c);
+  v = merge_d(v, dpp_statd<0x128>(v), c);
+  return v;
+}
+
+__device__ __forceinline__ double shfl_d(double v, int src) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __shfl(static_cast<int>(bits), src, 64);
+  const int hi = __shfl(static_cast<int>(bits >> 32), src, 64);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+// The match-mode scan of one sampled sequence (greedy and invalid-count sequences take the
+// rejection-rule scan, which treats them identically).  Same layout and outputs as
+// accept_sequence.
+__device__ __forceinline__ SeqState accept_sequence_match(const float* uniforms,
+                                    const Gather* gathers, int b, int kb_raw, float T, int K,
+                                    int V, int S, const RowPartial* partials,
+                                    int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                                    SeqState* states, bool write, int lane) {
+  const long long row0 = static_cast<long long>(b) * (K + 1);
+  const Gather g = lane < K ? gathers[static_cast<long long>(b) * K + lane]
+                            : Gather{0.f, 0.f, -1, 0};
+  const float u = lane < K ? uniforms[row0 + lane] : 0.f;
+  const float uk = lane == 0 ? uniforms[row0 + K] : 0.f;
+  const bool seq_ok = temp_valid(T);  // T != 0 and k_b in range here
+  const int kb = kb_raw;
+  const float c = seq_ok ? temp_scale(T) : kLog2e;
+
+  // Row sums in fp64 (fp32 partials, fp32 rescale factors), sixteen lanes per row.
+  StatD st{-INFINITY, 0.0, 0.0};
+  const int nsub = S * kWaves;
+  const int per_lane = (nsub + 15) / 16;
+  const int sl = lane & 15;
+  for (int i0 = 0; i0 <= K; i0 += 8) {
+    StatD v[2] = {StatD{-INFINITY, 0.0, 0.0}, StatD{-INFINITY, 0.0, 0.0}};
+    for (int t0 = 0; t0 < per_lane; t0 += 4) {
+      RowPartial pb[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ri = i0 + 4 * h + (lane >> 4);
+        const RowPartial* P = partials + (row0 + ri) * nsub;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = sl + 16 * (t0 + t);
+          pb[h][t] = (ri <= K && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0.f};
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          v[h] = merge_d(v[h], StatD{pb[h][t].m, pb[h][t].s, pb[h][t].pre}, c);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const StatD red = row16_reduce_d(v[h], c);
+      const int base = i0 + 4 * h;
+      const int src = ((lane - base) & 3) * 16;
+      const StatD got{__shfl(red.m, src, 64), shfl_d(red.s, src), shfl_d(red.p, src)};
+      if (lane >= base && lane < base + 4) st = got;
+    }
+  }
+
+  const bool drafted = lane < kb;
+  const int x = g.x;
+  bool lane_ok = true, keep = true;
+  double px = 0.0;
+  if (lane <= kb) {
+    lane_ok = st.s > 0.0;  // NaN / +inf logit -> NaN; all -inf -> 0
+    if (drafted) {
+      if (!(x >= 0 && x < V) || !(u >= 0.f && u < 1.f)) {
+        lane_ok = false;
+      } else {
+        // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
+        const double ex = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
+                               static_cast<double>(c));
+        const double t = static_cast<double>(u) * st.s;
+        keep = st.p <= t && t < st.p + ex;
+        px = ex / st.s;
+      }
+    }
+  }
+  if (lane == 0 && !(uk >= 0.f && uk < 1.f)) lane_ok = false;
+  const bool ok = seq_ok && (__ballot(!lane_ok) == 0ull);
+  const unsigned long long rej = __ballot(lane < kb && !keep);
+  const int A = ok ? (rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb) : -1;
+
+  SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
+  if (ok)  // a plain draw of p_A with u[b, A] (mismatch) or u[b, K] (bonus)
+    out = SeqState{kBonus, A, -1, A < kb ? A : K, c, __shfl(st.m, A, 64),
+                   static_cast<float>(shfl_d(st.s, A)), 0.f};
+  if (write) {
+    if (lane <= K) {
+      const bool kept = ok && lane < A;
+      out_tokens[row0 + lane] = kept ? x : -1;     // slot A is filled by the draw
+      if (out_probs) out_probs[row0 + lane] = kept ? static_cast<float>(px) : 0.f;
+    }
+    if (lane == 0) {
+      accept_len[b] = A;
+      states[b] = out;
+    }
+  }
+  return out;
+}
+
+// ------------------------------------------------------------------------------------------
 // Streaming row statistics.
 // ------------------------------------------------------------------------------------------
-template <typename LT, bool kVec>
+template <typename LT, bool kVec, bool kMatch>
 __global__ __launch_bounds__(kThreads) void stats_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const int32_t* __restrict__ proposed, const int32_t* __restrict__ num_draft,
@@ -373,11 +567,34 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     gathers[slot] = gi;
   }
   const float c = temp_valid(T) ? temp_scale(T) : kLog2e;  // invalid rows: result unused
-  MaxSum st = fold_chunk(x, c);
-  const float lane_max = st.m;
+  // Match mode also needs, per drafted sampled row, the sum below the drafted id x_i: only the
+  // sub-chunk that contains x_i takes the masked sum; below x_i it is the whole sum.
+  float pre = 0.f, lane_max;
+  MaxSum st;
+  bool have_pre = false;
+  int xi = -1;
+  if constexpr (kMatch) {
+    xi = (i < kb && T != 0.f) ? proposed[static_cast<long long>(b) * K + i] : -1;
+    if (xi >= c0 && xi < c0 + n) {
+      MaxSumPre sp = fold_chunk_pre<LT, kVec>(x, c, c0, lane, xi);
+      lane_max = sp.m;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
-    st = merge_ms(st, MaxSum{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)}, c);
+      for (int off = 32; off >= 1; off >>= 1)
+        sp = merge_msp(sp, MaxSumPre{__shfl_xor(sp.m, off, 64), __shfl_xor(sp.s, off, 64),
+                                     __shfl_xor(sp.p, off, 64)}, c);
+      st = MaxSum{sp.m, sp.s};
+      pre = sp.p;
+      have_pre = true;
+    }
+  }
+  if (!have_pre) {
+    st = fold_chunk(x, c);
+    lane_max = st.m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+      st = merge_ms(st, MaxSum{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)}, c);
+    if constexpr (kMatch) pre = xi >= c0 + n ? st.s : 0.f;
+  }
   int arg = 0;
   if (T == 0.f) {
     // Greedy row: the lowest token index attaining the sub-chunk max.  Only lanes whose own
@@ -391,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     arg = wave_min(a);
   }
   if (lane == 0)
-    partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, 0};
+    partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, pre};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -477,7 +694,7 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
 // wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns groups l,
 // l + 64, ...), in fp64.
 // ------------------------------------------------------------------------------------------
-template <typename LT, bool kVec>
+template <typename LT, bool kVec, bool kMatch>
 __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
@@ -494,9 +711,14 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
   if (wave == 0) {
     const int kb = num_draft ? num_draft[b] : K;
     const float T = greedy_all ? 0.f : temperature[b];
-    const SeqState st = accept_sequence(onehot, uniforms, gathers, draft_probs != nullptr, b, kb,
-                                        T, K, V, S, partials, accept_len, out_tokens, out_probs,
-                                        states, s == 0, lane);
+    SeqState st;
+    if (kMatch && T != 0.f && kb >= 0 && kb <= K)
+      st = accept_sequence_match(uniforms, gathers, b, kb, T, K, V, S, partials, accept_len,
+                                 out_tokens, out_probs, states, s == 0, lane);
+    else
+      st = accept_sequence(kMatch ? nullptr : onehot, uniforms, gathers,
+                           draft_probs != nullptr, b, kb, T, K, V, S, partials, accept_len,
+                           out_tokens, out_probs, states, s == 0, lane);
     if (lane == 0) sh_st = st;
   }
   __syncthreads();
@@ -588,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
       const bool plain = !(base_w > 0.0);  // empty residual: draw from p itself
       const double R = plain ? base_e : base_w;
       const double t =
-          static_cast<double>(uniforms[static_cast<long long>(b) * (K + 1) + K]) * R;
+          static_cast<double>(uniforms[static_cast<long long>(b) * (K + 1) + st.ucol]) * R;
       // Pass 2: first segment whose running sum exceeds t.
       double base = 0.0;
       int seg = -1, lastpos = -1;
@@ -701,7 +923,9 @@ hipError_t launch_typed(const LaunchArgs& a) {
   hipError_t err;
   // The streaming kernel: grid (chunk, row within sequence, sequence), at most 65535 sequences
   // per launch.  With measurement events, the dispatches record them (first start, last end).
-  auto stats = vec_stats ? stats_kernel<LT, true> : stats_kernel<LT, false>;
+  const bool match = a.match && !a.greedy_all;
+  auto stats = match ? (vec_stats ? stats_kernel<LT, true, true> : stats_kernel<LT, false, true>)
+                     : (vec_stats ? stats_kernel<LT, true, false> : stats_kernel<LT, false, false>);
   for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
     const dim3 grid(S, a.K + 1, min(kMaxZ, a.B - b0));
     hipEvent_t ev0 = b0 == 0 ? a.hot_begin : nullptr;
@@ -718,7 +942,10 @@ hipError_t launch_typed(const LaunchArgs& a) {
   }
   // Accept scan + draw sums: one workgroup per (chunk, sequence); greedy-only calls need just
   // the chunk-0 workgroups (no draw).
-  auto accept_draw = vec_draw ? accept_draw_kernel<LT, true> : accept_draw_kernel<LT, false>;
+  auto accept_draw = match ? (vec_draw ? accept_draw_kernel<LT, true, true>
+                                        : accept_draw_kernel<LT, false, true>)
+                           : (vec_draw ? accept_draw_kernel<LT, true, false>
+                                       : accept_draw_kernel<LT, false, false>);
   const int gx = a.greedy_all ? 1 : S;
   for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
     const dim3 grid(gx, min(kMaxZ, a.B - b0));
