@@ -224,6 +224,53 @@ specdec_status specdec_commit(const int32_t* accept_len, const int32_t* out_toke
                               int32_t* target_kv_len, int32_t* draft_kv_len,
                               int32_t* packed_tokens, int32_t* packed_offsets, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Acceptance telemetry and the per-route draft length.  The pages advise recording the
+ * acceptance rate per route and choosing the draft length from it:
+ *   - "Decodificação especulativa explicada" (gsantana.dev), sections "Quanto mais rápido: a
+ *     matemática" (E[tokens per pass] = (1 - a^(k+1)) / (1 - a), speedup = E / (k c + 1)),
+ *     "A tabela de speedup" (the best k per a and c) and "Checagem de realidade em produção"
+ *     (record acceptance per route);
+ *   - "Speculative decoding: el secretario..." (blog.lo0.es), sections "La matemática que
+ *     importa: techo y speedup" and "Pitfalls operacionales" (tune the length dynamically).
+ *
+ * Counters: int64 [n_routes][SPECDEC_TELEMETRY_ROW], per route the fields
+ *   0 rounds (valid rows)   1 drafted sum k_b   2 accepted sum A_b   3 emitted sum (A_b + 1)
+ *   4 rounds with A_b = k_b   5 rounds with A_b < k_b (one rejected position each)
+ *   6 invalid rows   7 reserved (0)   8 + a: rounds with A_b = a (a = 0..63).
+ * A row is invalid when accept_len < 0, k_b is outside [0, K] or A_b > k_b; rows whose route id
+ * is outside [0, n_routes) are not counted. */
+#define SPECDEC_TELEMETRY_FIELDS 8
+#define SPECDEC_TELEMETRY_ROW 72
+#define SPECDEC_TELEMETRY_MAX_ROUTES 64
+
+/* Adds one verified batch to the DEVICE counters (stream-ordered; the caller zeroes them once).
+ * accept_len [B] int32 (from a verify call); num_draft [B] int32 or NULL (= K); route [B] int32
+ * or NULL (= route 0); 1 <= n_routes <= SPECDEC_TELEMETRY_MAX_ROUTES.  Integer sums: the result
+ * does not depend on the order.  Calls that overlap on the same counters race. */
+specdec_status specdec_telemetry_update(const int32_t* accept_len, const int32_t* num_draft,
+                                        const int32_t* route, int32_t B, int32_t K,
+                                        int32_t n_routes, int64_t* counters, void* stream);
+
+/* Host arithmetic on HOST copies of the counters.  specdec_alpha_estimate: accepted /
+ * (accepted + rejected positions), the maximum-likelihood per-token rate (NaN without
+ * observations).  specdec_expected_tokens / specdec_speedup: the formulas above (NaN outside
+ * alpha in [0, 1], k >= 0, c >= 0).  specdec_choose_k: the k in [k_min, k_max] with the largest
+ * speedup (the smaller k on ties), -1 for invalid arguments.  specdec_plan_k: k_table[r] for each
+ * route (k_default for a route without observations). */
+double specdec_alpha_estimate(const int64_t* route_counters);
+double specdec_expected_tokens(double alpha, int32_t k);
+double specdec_speedup(double alpha, int32_t k, double c);
+int32_t specdec_choose_k(double alpha, double c, int32_t k_min, int32_t k_max);
+specdec_status specdec_plan_k(const int64_t* counters, int32_t n_routes, double c, int32_t k_min,
+                              int32_t k_max, int32_t k_default, int32_t* k_table);
+
+/* Applies a plan on the DEVICE: num_draft[b] = min(num_draft[b], max(0, k_table[route[b]])) for
+ * rows with num_draft[b] >= 0 and a route id in [0, n_routes) (route NULL = route 0).  The
+ * proposals past the new count are simply not verified. */
+specdec_status specdec_apply_k(int32_t* num_draft, const int32_t* route, const int32_t* k_table,
+                               int32_t B, int32_t n_routes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* specdec_status_string(int32_t status);
 

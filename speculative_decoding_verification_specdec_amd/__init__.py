@@ -8,9 +8,11 @@ raises if the library is missing.
 from .binding import (SpecdecError, specdec_verify, specdec_verify_greedy, specdec_workspace_size,
                       specdec_status_string, library_path, load_library,
                       inputs_to_device, specdec_ngram_propose, specdec_ngram_workspace_size,
-                      specdec_commit, specdec_verify_match)
+                      specdec_commit, specdec_verify_match, specdec_telemetry_update,
+                      specdec_apply_k, specdec_plan_k, telemetry_counters)
 
 __all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_workspace_size",
            "specdec_status_string", "library_path", "load_library", "inputs_to_device",
            "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit",
-           "specdec_verify_match"]
+           "specdec_verify_match", "specdec_telemetry_update", "specdec_apply_k",
+           "specdec_plan_k", "telemetry_counters"]

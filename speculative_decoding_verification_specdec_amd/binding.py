@@ -62,6 +62,21 @@ def load_library():
     lib.specdec_ngram_propose.restype = i32
     lib.specdec_commit.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.specdec_commit.restype = i32
+    lib.specdec_telemetry_update.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.specdec_telemetry_update.restype = i32
+    lib.specdec_apply_k.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.specdec_apply_k.restype = i32
+    f64 = ctypes.c_double
+    lib.specdec_alpha_estimate.argtypes = [vp]
+    lib.specdec_alpha_estimate.restype = f64
+    lib.specdec_expected_tokens.argtypes = [f64, i32]
+    lib.specdec_expected_tokens.restype = f64
+    lib.specdec_speedup.argtypes = [f64, i32, f64]
+    lib.specdec_speedup.restype = f64
+    lib.specdec_choose_k.argtypes = [f64, f64, i32, i32]
+    lib.specdec_choose_k.restype = i32
+    lib.specdec_plan_k.argtypes = [vp, i32, f64, i32, i32, i32, vp]
+    lib.specdec_plan_k.restype = i32
     lib.specdec_status_string.argtypes = [i32]
     lib.specdec_status_string.restype = ctypes.c_char_p
     lib.specdec_version.argtypes = []
@@ -308,6 +323,61 @@ def specdec_commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, seq_len: 
                                 _ptr(off), _stream_handle(stream))
     _raise(status, "specdec_commit")
     return (pk, off) if packed else None
+
+
+TELEMETRY_ROW = 72
+TELEMETRY_MAX_ROUTES = 64
+
+
+def telemetry_counters(n_routes: int, device) -> torch.Tensor:
+    """Zeroed device counters [n_routes, 72] int64 for specdec_telemetry_update."""
+    return torch.zeros((n_routes, TELEMETRY_ROW), dtype=torch.int64, device=device)
+
+
+def specdec_telemetry_update(counters: torch.Tensor, accept_len: torch.Tensor, *,
+                             num_draft: torch.Tensor | None = None,
+                             route: torch.Tensor | None = None, K: int, stream=None):
+    """Add one verified batch to the device counters [n_routes, 72] int64 (in place)."""
+    lib = load_library()
+    B = int(accept_len.shape[0])
+    dev = accept_len.device
+    n_routes = int(counters.shape[0])
+    _check(counters, "counters", torch.int64, (n_routes, TELEMETRY_ROW), dev)
+    _check(accept_len, "accept_len", torch.int32, (B,), dev)
+    _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
+    _check(route, "route", torch.int32, (B,), dev, optional=True)
+    status = lib.specdec_telemetry_update(_ptr(accept_len), _ptr(num_draft), _ptr(route), B,
+                                          int(K), n_routes, _ptr(counters), _stream_handle(stream))
+    _raise(status, "specdec_telemetry_update")
+    return counters
+
+
+def specdec_apply_k(num_draft: torch.Tensor, k_table: torch.Tensor, *,
+                    route: torch.Tensor | None = None, stream=None):
+    """Clamp num_draft [B] (in place) to k_table [n_routes] of each sequence's route."""
+    lib = load_library()
+    B = int(num_draft.shape[0])
+    dev = num_draft.device
+    _check(num_draft, "num_draft", torch.int32, (B,), dev)
+    _check(k_table, "k_table", torch.int32, (int(k_table.shape[0]),), dev)
+    _check(route, "route", torch.int32, (B,), dev, optional=True)
+    status = lib.specdec_apply_k(_ptr(num_draft), _ptr(route), _ptr(k_table), B,
+                                 int(k_table.shape[0]), _stream_handle(stream))
+    _raise(status, "specdec_apply_k")
+    return num_draft
+
+
+def specdec_plan_k(counters_host, c: float, k_min: int, k_max: int, k_default: int):
+    """Host planner: counters (host int64 [n_routes, 72], numpy or CPU tensor) -> k per route
+    (numpy int32), through the library's host arithmetic."""
+    import numpy as np
+    cnt = np.ascontiguousarray(np.asarray(counters_host, dtype=np.int64))
+    n_routes = cnt.shape[0]
+    out = np.empty(n_routes, dtype=np.int32)
+    status = load_library().specdec_plan_k(cnt.ctypes.data, n_routes, float(c), int(k_min),
+                                           int(k_max), int(k_default), out.ctypes.data)
+    _raise(status, "specdec_plan_k")
+    return out
 
 
 def inputs_to_device(inp, device) -> dict:

@@ -131,4 +131,16 @@ struct CommitArgs {
 
 hipError_t launch_commit(const CommitArgs& a);
 
+// ---- acceptance telemetry and per-route draft length (telemetry.hip) ----
+constexpr int kTelemetryFields = 8;
+constexpr int kTelemetryBins = 64;
+constexpr int kTelemetryRow = kTelemetryFields + kTelemetryBins;
+constexpr int kTelemetryMaxRoutes = 64;
+
+hipError_t launch_telemetry(const int32_t* accept_len, const int32_t* num_draft,
+                            const int32_t* route, int B, int K, int n_routes,
+                            long long* counters, hipStream_t stream);
+hipError_t launch_apply_k(int32_t* num_draft, const int32_t* route, const int32_t* k_table,
+                          int B, int n_routes, hipStream_t stream);
+
 }  // namespace specdec

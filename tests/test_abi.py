@@ -27,7 +27,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("specdec_verify", "specdec_verify_greedy", "specdec_verify_ex",
               "specdec_workspace_size", "specdec_status_string", "specdec_version",
-              "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit"):
+              "specdec_ngram_propose", "specdec_ngram_workspace_size", "specdec_commit",
+              "specdec_verify_match", "specdec_telemetry_update", "specdec_apply_k",
+              "specdec_plan_k", "specdec_choose_k"):
         assert n in names
 
 
@@ -140,3 +142,68 @@ def test_commit_host_side_errors(lib, kw, status):
 
 def test_commit_empty_batch_without_offsets(lib):
     assert _commit(lib, B=0, acc=None, out=None, sl=None, tok=None, pk=None, off=None) == 0
+
+
+# ---- host arithmetic of the telemetry plan (no GPU needed): against the oracle ----
+
+def test_host_plan_functions_match_the_oracle(lib):
+    import json
+    import numpy as np
+    from oracle import closed_forms
+    from oracle.telemetry_oracle import ROW, choose_k, plan_k
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "page1_speedup_tables.json")))
+    lo, hi = g["best_k_search_range"]
+    for c_str, tab in g["tables"].items():
+        for alpha, (k_best, _) in zip(g["alphas"], tab["best"]):
+            assert lib.specdec_choose_k(alpha, float(c_str), lo, hi) == k_best
+    for alpha in np.linspace(0.0, 1.0, 21):
+        for k in (0, 1, 5, 8, 63):
+            assert lib.specdec_expected_tokens(alpha, k) == pytest.approx(
+                closed_forms.expected_tokens(alpha, k), rel=1e-12)
+            assert lib.specdec_speedup(alpha, k, 0.07) == pytest.approx(
+                closed_forms.speedup(alpha, k, 0.07), rel=1e-12)
+            assert lib.specdec_choose_k(alpha, 0.07, 0, k) == choose_k(alpha, 0.07, 0, k)
+    rng = np.random.default_rng(4)
+    cnt = np.zeros((9, ROW), dtype=np.int64)
+    cnt[:, 2] = rng.integers(0, 5000, size=9)
+    cnt[:, 5] = rng.integers(0, 5000, size=9)
+    cnt[3, [2, 5]] = 0                                    # a route with no observations
+    out = np.empty(9, dtype=np.int32)
+    assert lib.specdec_plan_k(cnt.ctypes.data, 9, 0.1, 1, 12, 4, out.ctypes.data) == 0
+    assert out.tolist() == plan_k(cnt, 0.1, 1, 12, 4).tolist()
+    assert np.isnan(lib.specdec_alpha_estimate(cnt[3].ctypes.data))
+    assert lib.specdec_alpha_estimate(cnt[0].ctypes.data) == cnt[0, 2] / (cnt[0, 2] + cnt[0, 5])
+
+
+def test_host_plan_argument_errors(lib):
+    import numpy as np
+    assert lib.specdec_choose_k(1.5, 0.1, 1, 5) == -1
+    assert lib.specdec_choose_k(0.5, -0.1, 1, 5) == -1
+    assert lib.specdec_choose_k(0.5, 0.1, 5, 4) == -1
+    assert lib.specdec_choose_k(0.5, 0.1, 1, 64) == -1
+    cnt = np.zeros((2, 72), dtype=np.int64)
+    out = np.empty(2, dtype=np.int32)
+    assert lib.specdec_plan_k(cnt.ctypes.data, 0, 0.1, 1, 5, 3, out.ctypes.data) == -2
+    assert lib.specdec_plan_k(None, 2, 0.1, 1, 5, 3, out.ctypes.data) == -1
+    assert lib.specdec_plan_k(cnt.ctypes.data, 2, 0.1, 1, 5, 64, out.ctypes.data) == -2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -2), (dict(K=64), -2), (dict(n=0), -2), (dict(n=65), -2),
+    (dict(acc=None), -1), (dict(cnt=None), -1),
+    (dict(acc=FAKE + 1), -4), (dict(cnt=FAKE + 4), -4), (dict(route=FAKE + 2), -4),
+])
+def test_telemetry_host_side_errors(lib, kw, status):
+    a = dict(acc=FAKE, nd=None, route=None, B=4, K=5, n=2, cnt=FAKE)
+    a.update(kw)
+    assert lib.specdec_telemetry_update(a["acc"], a["nd"], a["route"], a["B"], a["K"], a["n"],
+                                        a["cnt"], None) == status
+
+
+def test_apply_k_host_side_errors(lib):
+    assert lib.specdec_apply_k(FAKE, None, FAKE, -1, 2, None) == -2
+    assert lib.specdec_apply_k(FAKE, None, FAKE, 4, 0, None) == -2
+    assert lib.specdec_apply_k(None, None, FAKE, 4, 2, None) == -1
+    assert lib.specdec_apply_k(FAKE + 1, None, FAKE, 4, 2, None) == -4
+    assert lib.specdec_apply_k(None, None, None, 0, 2, None) == 0
