@@ -145,7 +145,7 @@ def time_replayed(calls, steps, stream):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
-def bench_ngram(dev, stream, steps=200, replicas=20):
+def bench_ngram(dev, stream, steps=200, replicas=20, long=False):
     """The n-gram drafter on 512 histories of 4096-8192 tokens (V = 128256, n = 4..1, K = 8):
     history tokens scanned per second and the algorithmic bytes (4 per history token read,
     plus the proposals) against the HBM peak.  ``replicas`` copies (~340 MB) rotate so the
@@ -154,8 +154,11 @@ def bench_ngram(dev, stream, steps=200, replicas=20):
     import torch
     from speculative_decoding_verification_specdec_amd import (specdec_ngram_propose,
                                                                specdec_ngram_workspace_size)
-    from speculative_decoding_verification_specdec_amd.contexts import ngram_workload
-    h = ngram_workload()
+    from speculative_decoding_verification_specdec_amd.contexts import (ngram_long_workload,
+                                                                        ngram_workload)
+    h = ngram_long_workload() if long else ngram_workload()
+    if long:
+        replicas = 4        # 4 x 67 MB of histories
     K, n_min, n_max = 8, 1, 4
     ws = torch.empty(specdec_ngram_workspace_size(h.B, h.capacity), dtype=torch.uint8, device=dev)
     out = (torch.empty((h.B, K), dtype=torch.int32, device=dev),
@@ -171,8 +174,9 @@ def bench_ngram(dev, stream, steps=200, replicas=20):
     toks = float(h.lengths.astype(np.int64).sum())
     nbytes = 4.0 * toks + 4.0 * h.B + 4.0 * h.B * (K + 1)
     return {
-        "workload": "512 token histories, length U{4096..8192}, V=128256, half the segments "
-                    "copied from earlier in the history; n = 4..1, K = 8",
+        "workload": (f"{h.B} token histories, length U{{{h.capacity // 2}..{h.capacity}}}, "
+                     "V=128256, half the segments copied from earlier in the history; "
+                     "n = 4..1, K = 8"),
         "us_per_call": us, "history_tokens_per_s": toks / (us * 1e-6),
         "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
         "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -209,6 +213,59 @@ def bench_commit(dev, stream, steps=400):
     return {"workload": "B=512, K=8, accept lengths U{0..8}, history capacity 8192",
             "us_per_call_including_length_reset_copy": us,
             "sequences_per_s": B / (us * 1e-6)}
+
+
+def bench_match(dev, stream, steps=300, replicas=6):
+    """Sample-and-match verify on the same B=64, k=5, V=128256 bf16 batch: verified draft
+    positions per second and the algorithmic bytes (every used logit row once, ids, uniforms,
+    outputs; no draft row is read) against the HBM peak."""
+    import torch
+    from speculative_decoding_verification_specdec_amd import (inputs_to_device,
+                                                               specdec_verify_match,
+                                                               specdec_workspace_size)
+    from speculative_decoding_verification_specdec_amd.inputs import batch64
+    inp = batch64()
+    B, K, V = inp.B, inp.K, inp.V
+    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    out = (torch.empty(B, dtype=torch.int32, device=dev),
+           torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+           torch.empty((B, K + 1), dtype=torch.float32, device=dev))
+    calls = []
+    for _ in range(replicas):
+        d = inputs_to_device(inp, dev)
+        calls.append(lambda d=d: specdec_verify_match(d["logits"], d["proposed"], d["temperature"],
+                                                      d["uniforms"], out=out, workspace=ws))
+    us = time_replayed(calls, steps, stream)
+    acc = out[0].cpu().numpy()
+    kb = inp.draft_counts()
+    positions = int(kb.sum())
+    nbytes = float(((kb + 1) * V * 2).sum() + (4 * kb + 4 * (kb + 1) + 4 + 8 * (kb + 1) + 4).sum())
+    return {"workload": "batch64 (B=64, k=5, V=128256, bf16), sample-and-match verify",
+            "us_per_call": us, "verified_positions_per_s": positions / (us * 1e-6),
+            "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mean_accept_len": float(acc.mean())}
+
+
+def bench_telemetry(dev, stream, steps=400):
+    """Telemetry update of a B=512, K=8 batch into 4 routes, and applying a 4-route plan."""
+    import numpy as np
+    import torch
+    from speculative_decoding_verification_specdec_amd import (specdec_apply_k,
+                                                               specdec_telemetry_update,
+                                                               telemetry_counters)
+    B, K = 512, 8
+    rng = np.random.default_rng(22)
+    nd = torch.from_numpy(rng.integers(1, K + 1, size=B).astype(np.int32)).to(dev)
+    acc = torch.from_numpy((rng.random(B) * (nd.cpu().numpy() + 1)).astype(np.int32)).to(dev)
+    route = torch.from_numpy(rng.integers(0, 4, size=B).astype(np.int32)).to(dev)
+    cnt = telemetry_counters(4, dev)
+    table = torch.tensor([3, 5, 8, 2], dtype=torch.int32, device=dev)
+    nd2 = nd.clone()
+    us_t = time_replayed([lambda: specdec_telemetry_update(cnt, acc, num_draft=nd, route=route,
+                                                           K=K)], steps, stream)
+    us_a = time_replayed([lambda: specdec_apply_k(nd2, table, route=route)], steps, stream)
+    return {"workload": "B=512, K=8, 4 routes", "update_us": us_t, "apply_k_us": us_a}
 
 
 def main():
@@ -371,9 +428,14 @@ def main():
     }
     if not args.no_next_rows:
         print("[bench] n-gram drafter", file=sys.stderr, flush=True)
-        res["next_rows"] = {"ngram_propose": bench_ngram(dev, stream)}
+        res["next_rows"] = {"ngram_propose": bench_ngram(dev, stream),
+                            "ngram_propose_long": bench_ngram(dev, stream, long=True)}
         print("[bench] commit", file=sys.stderr, flush=True)
         res["next_rows"]["commit"] = bench_commit(dev, stream)
+        print("[bench] sample-and-match verify", file=sys.stderr, flush=True)
+        res["next_rows"]["verify_match"] = bench_match(dev, stream)
+        print("[bench] telemetry", file=sys.stderr, flush=True)
+        res["next_rows"]["telemetry"] = bench_telemetry(dev, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

@@ -67,8 +67,11 @@ def make_histories(B: int, capacity: int, V: int, *, seed: int,
             seg = min(seg, L - n)
             if n > 0 and rc.random() < copy_frac:
                 src = int(rc.integers(0, n))
-                for j in range(seg):              # token by token: overlapping copies repeat
-                    h[n + j] = h[src + j]
+                if src + seg <= n:
+                    h[n:n + seg] = h[src:src + seg]
+                else:
+                    for j in range(seg):          # token by token: an overlapping copy repeats
+                        h[n + j] = h[src + j]
             else:
                 h[n:n + seg] = rt.integers(0, V, size=seg)
             n += seg
@@ -92,3 +95,10 @@ def ngram_workload(B: int = 512, capacity: int = 8192, V: int = 128256, seed: in
     """Drafting workload: 512 histories of 4096-8192 tokens over a 128256-token vocabulary, half
     of the segments copied from earlier in the same history (the ragged batch's n-gram rows)."""
     return make_histories(B, capacity, V, seed=seed, name="ngram_histories")
+
+
+def ngram_long_workload(B: int = 256, capacity: int = 65536, V: int = 128256,
+                        seed: int = 7) -> Histories:
+    """Long histories: 256 histories of 32768-65536 tokens (the same copy structure), a size at
+    which the drafter's pass over the history is bandwidth-bound rather than latency-bound."""
+    return make_histories(B, capacity, V, seed=seed, name="ngram_long_histories")

@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kCmThreads = 1024;
 constexpr int kCmWaves = kCmThreads / 64;
+constexpr int kPre = 9;  // tokens per sequence prefetched before the scan
 
 // Tokens sequence b commits: A + 1, or 0 for an invalid row / length / overflow.
 __device__ __forceinline__ int emitted_count(int A, int L, int K, int capacity) {
@@ -39,6 +40,14 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (B + kCmThreads - 1) / kCmThreads;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  // With one sequence per thread (B <= 1024) its first kPre emitted tokens are loaded together
+  // with the lengths, so the copies after the scan wait on no further load.
+  int32_t pre[kPre];
+  if (per == 1 && b0 < b1) {
+    const int32_t* src = out_tokens + static_cast<long long>(b0) * (K + 1);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) pre[i] = i <= K ? src[i] : 0;
+  }
   int local = 0;
   for (int b = b0; b < b1; ++b) local += emitted_count(accept_len[b], seq_len[b], K, capacity);
   // Exclusive scan of the per-thread counts over the workgroup.
@@ -60,7 +69,14 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
       const int32_t* src = out_tokens + static_cast<long long>(b) * (K + 1);
       int32_t* dst = tokens ? tokens + static_cast<long long>(b) * capacity + L : nullptr;
       for (int i = 0; i < em; ++i) {
-        const int32_t t = src[i];
+        int32_t t;
+        if (per == 1 && i < kPre) {
+#pragma unroll
+          for (int j = 0; j < kPre; ++j)  // register array: select without dynamic indexing
+            if (j == i) t = pre[j];
+        } else {
+          t = src[i];
+        }
         if (dst) dst[i] = t;
         if (packed) packed[base + i] = t;
       }

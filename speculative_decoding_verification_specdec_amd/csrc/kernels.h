@@ -98,7 +98,7 @@ struct LaunchArgs {
 hipError_t launch_verify(const LaunchArgs& a);
 
 // ---- n-gram drafter (ngram.hip) ----
-constexpr int kNgramTile = 4096;   // candidate positions per workgroup
+constexpr int kNgramTile = 8192;   // candidate positions per workgroup
 constexpr int kNgramMaxN = 32;     // longest suffix tried
 
 inline int ngram_tiles(int capacity) { return (capacity + kNgramTile - 1) / kNgramTile; }

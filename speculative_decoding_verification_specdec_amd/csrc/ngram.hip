@@ -13,13 +13,12 @@
 // that occurs is N = max_e m(e) and its earliest occurrence ends at the smallest e with
 // m(e) = N.  Both fall out of one max-reduction of the key (m(e) << 32) | (2^32 - 1 - e).
 //
-// Two kernels, no atomics:
-//   ngram_match_kernel  one 256-thread workgroup per (4096-position tile, sequence): the tile
-//       and a 32-token halo are staged in LDS with 16-byte loads, each thread extends the
-//       match of 16 positions (consecutive threads on consecutive positions), and the
-//       workgroup's best key goes to the workspace.
-//   ngram_emit_kernel   one wave per sequence: max of the tile keys, then the proposal is
-//       copied from the history.
+// No atomics.  ngram_match_kernel runs one 1024-thread workgroup per (8192-position tile,
+// sequence): the tile and a 32-token halo are staged in LDS with 16-byte loads, each thread
+// extends the match of 8 positions (consecutive threads on consecutive positions), and the
+// workgroup max-reduces the keys.  When one tile covers the whole history capacity the same
+// workgroup emits the proposal straight from LDS; otherwise each tile writes its key and
+// ngram_emit_kernel (one wave per sequence) takes the max over tiles and copies the proposal.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -27,9 +26,10 @@
 namespace specdec {
 namespace {
 
-constexpr int kNgThreads = 256;
-constexpr int kNgPer = kNgramTile / kNgThreads;  // 16 positions per thread
+constexpr int kNgThreads = 1024;
+constexpr int kNgPer = kNgramTile / kNgThreads;  // 8 positions per thread
 constexpr int kNgHalo = kNgramMaxN;              // tokens staged before the tile
+constexpr int kEmitThreads = 256;                // 4 sequences per emit workgroup
 
 __device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
@@ -45,10 +45,19 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
+// The proposal for key `key` (0: none) of a valid history of length L, written by one wave:
+// proposed[lane] = h[e + lane] for lane < cnt, else -1.
+__device__ __forceinline__ int proposal_count(unsigned long long key, int L, int K, int& e) {
+  if (key == 0ull) return 0;
+  e = static_cast<int>(0xffffffffull - (key & 0xffffffffull));
+  return min(K, L - e);
+}
+
 template <bool kVec>
 __global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ lengths, int capacity,
-    int n_min, int n_max, int ntiles, unsigned long long* __restrict__ partials) {
+    int n_min, int n_max, int K, int ntiles, unsigned long long* __restrict__ partials,
+    int32_t* __restrict__ proposed, int32_t* __restrict__ num_draft) {
   __shared__ int sh_tok[kNgHalo + kNgramTile];  // sh_tok[i] = h[t0 - kNgHalo + i]
   __shared__ int sh_suf[kNgramMaxN + 1];        // sh_suf[j] = h[L - j]
   __shared__ unsigned long long sh_best[kNgThreads / 64];
@@ -56,66 +65,77 @@ __global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
   const int b = static_cast<int>(blockIdx.x / ntiles), tile = static_cast<int>(blockIdx.x % ntiles);
   const int L = lengths[b];
   const int t0 = tile * kNgramTile;
-  unsigned long long* out = partials + static_cast<long long>(b) * ntiles + tile;
+  const bool valid = L >= 0 && L <= capacity;
   const int nmax = min(n_max, L - 1);
-  // Invalid length, nothing long enough to match, or no follower position in this tile.
-  if (L < 0 || L > capacity || nmax < n_min || t0 > L - 1) {
-    if (tid == 0) *out = 0ull;
+  // Nothing to match for an invalid length, a history too short for n_min, or a tile with no
+  // follower position (e in [1, L-1]); the condition is uniform over the workgroup.
+  const bool active = valid && nmax >= n_min && t0 <= L - 1;
+  const int32_t* h = tokens + static_cast<long long>(b) * capacity;
+  unsigned long long key = 0ull;
+  if (active) {
+    if (tid >= 1 && tid <= nmax) sh_suf[tid] = h[L - tid];
+    // Stage h[t0 - kNgHalo, t0 + kNgramTile) where it lies in [0, L); other slots are never
+    // compared (every compared index e - j lies in [0, L - 2]).
+    const int i0 = t0 - kNgHalo;
+    if constexpr (kVec) {
+      constexpr int kVecs = (kNgHalo + kNgramTile) / 4;
+      const int4* hv = reinterpret_cast<const int4*>(h);
+      for (int v = tid; v < kVecs; v += kNgThreads) {
+        const int idx = i0 + 4 * v;  // a multiple of 4; idx < L <= capacity keeps idx + 3 in the row
+        int4 d = make_int4(0, 0, 0, 0);
+        if (idx >= 0 && idx < L) d = hv[idx / 4];
+        sh_tok[4 * v] = d.x;
+        sh_tok[4 * v + 1] = d.y;
+        sh_tok[4 * v + 2] = d.z;
+        sh_tok[4 * v + 3] = d.w;
+      }
+    } else {
+      for (int i = tid; i < kNgHalo + kNgramTile; i += kNgThreads) {
+        const int idx = i0 + i;
+        sh_tok[i] = (idx >= 0 && idx < L) ? h[idx] : 0;
+      }
+    }
+    __syncthreads();
+    unsigned long long best = 0ull;
+#pragma unroll 4
+    for (int r = 0; r < kNgPer; ++r) {
+      const int e = t0 + r * kNgThreads + tid;
+      if (e < 1 || e > L - 1) continue;
+      const int base = kNgHalo + (e - t0);
+      const int jmax = min(nmax, e);
+      int J = 0;
+      while (J < jmax && sh_tok[base - J - 1] == sh_suf[J + 1]) ++J;
+      if (J >= n_min)
+        best = max_u64(best, (static_cast<unsigned long long>(J) << 32) |
+                                 (0xffffffffull - static_cast<unsigned>(e)));
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) sh_best[wave] = best;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kNgThreads / 64; ++w) key = max_u64(key, sh_best[w]);
+  }
+  if (ntiles > 1) {
+    if (tid == 0) partials[static_cast<long long>(b) * ntiles + tile] = key;
     return;
   }
-  const int32_t* h = tokens + static_cast<long long>(b) * capacity;
-  if (tid >= 1 && tid <= nmax) sh_suf[tid] = h[L - tid];
-  // Stage h[t0 - kNgHalo, t0 + kNgramTile) where it lies in [0, L); other slots are never
-  // compared (every compared index e - j lies in [0, L - 2]).
-  const int i0 = t0 - kNgHalo;
-  if constexpr (kVec) {
-    constexpr int kVecs = (kNgHalo + kNgramTile) / 4;
-    const int4* hv = reinterpret_cast<const int4*>(h);
-    for (int v = tid; v < kVecs; v += kNgThreads) {
-      const int idx = i0 + 4 * v;  // a multiple of 4; idx < L <= capacity keeps idx + 3 in the row
-      int4 d = make_int4(0, 0, 0, 0);
-      if (idx >= 0 && idx < L) d = hv[idx / 4];
-      sh_tok[4 * v] = d.x;
-      sh_tok[4 * v + 1] = d.y;
-      sh_tok[4 * v + 2] = d.z;
-      sh_tok[4 * v + 3] = d.w;
-    }
-  } else {
-    for (int i = tid; i < kNgHalo + kNgramTile; i += kNgThreads) {
-      const int idx = i0 + i;
-      sh_tok[i] = (idx >= 0 && idx < L) ? h[idx] : 0;
-    }
-  }
-  __syncthreads();
-  unsigned long long best = 0ull;
-#pragma unroll 4
-  for (int r = 0; r < kNgPer; ++r) {
-    const int e = t0 + r * kNgThreads + tid;
-    if (e < 1 || e > L - 1) continue;
-    const int base = kNgHalo + (e - t0);
-    const int jmax = min(nmax, e);
-    int J = 0;
-    while (J < jmax && sh_tok[base - J - 1] == sh_suf[J + 1]) ++J;
-    if (J >= n_min)
-      best = max_u64(best, (static_cast<unsigned long long>(J) << 32) |
-                               (0xffffffffull - static_cast<unsigned>(e)));
-  }
-  best = wave_max_u64(best);
-  if (lane == 0) sh_best[wave] = best;
-  __syncthreads();
-  if (tid == 0) {
-    unsigned long long v = sh_best[0];
-    for (int w = 1; w < kNgThreads / 64; ++w) v = max_u64(v, sh_best[w]);
-    *out = v;
-  }
+  // One tile covers the history: emit here, the proposal read from LDS (t0 = 0 and
+  // [e, e + cnt) lies in [0, L), all staged).
+  if (wave != 0) return;
+  int e = 0;
+  const int cnt = proposal_count(key, L, K, e);
+  if (lane < K)
+    proposed[static_cast<long long>(b) * K + lane] =
+        lane < cnt ? sh_tok[kNgHalo + e + lane] : -1;
+  if (lane == 0) num_draft[b] = valid ? cnt : -1;
 }
 
-__global__ __launch_bounds__(kNgThreads) void ngram_emit_kernel(
+__global__ __launch_bounds__(kEmitThreads) void ngram_emit_kernel(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ lengths, int B, int capacity,
     int K, int ntiles, const unsigned long long* __restrict__ partials,
     int32_t* __restrict__ proposed, int32_t* __restrict__ num_draft) {
   const int lane = threadIdx.x & 63;
-  const int b = static_cast<int>(blockIdx.x) * (kNgThreads / 64) + (threadIdx.x >> 6);
+  const int b = static_cast<int>(blockIdx.x) * (kEmitThreads / 64) + (threadIdx.x >> 6);
   if (b >= B) return;
   const int L = lengths[b];
   const bool valid = L >= 0 && L <= capacity;
@@ -125,11 +145,8 @@ __global__ __launch_bounds__(kNgThreads) void ngram_emit_kernel(
     for (int t = lane; t < ntiles; t += 64) key = max_u64(key, p[t]);
     key = wave_max_u64(key);
   }
-  int cnt = 0, e = 0;
-  if (key != 0ull) {
-    e = static_cast<int>(0xffffffffull - (key & 0xffffffffull));
-    cnt = min(K, L - e);
-  }
+  int e = 0;
+  const int cnt = proposal_count(key, L, K, e);
   if (lane < K) {
     const int32_t* h = tokens + static_cast<long long>(b) * capacity;
     proposed[static_cast<long long>(b) * K + lane] = lane < cnt ? h[e + lane] : -1;
@@ -146,12 +163,15 @@ hipError_t launch_ngram(const NgramArgs& a) {
   const unsigned grid1 = static_cast<unsigned>(static_cast<long long>(a.B) * ntiles);
   if (vec)
     ngram_match_kernel<true><<<grid1, kNgThreads, 0, a.stream>>>(
-        a.tokens, a.lengths, a.capacity, a.n_min, a.n_max, ntiles, a.partials);
+        a.tokens, a.lengths, a.capacity, a.n_min, a.n_max, a.K, ntiles, a.partials, a.proposed,
+        a.num_draft);
   else
     ngram_match_kernel<false><<<grid1, kNgThreads, 0, a.stream>>>(
-        a.tokens, a.lengths, a.capacity, a.n_min, a.n_max, ntiles, a.partials);
-  const unsigned grid2 = static_cast<unsigned>((a.B + kNgThreads / 64 - 1) / (kNgThreads / 64));
-  ngram_emit_kernel<<<grid2, kNgThreads, 0, a.stream>>>(a.tokens, a.lengths, a.B, a.capacity,
+        a.tokens, a.lengths, a.capacity, a.n_min, a.n_max, a.K, ntiles, a.partials, a.proposed,
+        a.num_draft);
+  if (ntiles == 1) return hipGetLastError();
+  const unsigned grid2 = static_cast<unsigned>((a.B + kEmitThreads / 64 - 1) / (kEmitThreads / 64));
+  ngram_emit_kernel<<<grid2, kEmitThreads, 0, a.stream>>>(a.tokens, a.lengths, a.B, a.capacity,
                                                         a.K, ntiles, a.partials, a.proposed,
                                                         a.num_draft);
   return hipGetLastError();

@@ -102,8 +102,8 @@ def _ngram(lib, **kw):
 def test_ngram_workspace_size(lib):
     assert lib.specdec_ngram_workspace_size(0, 100) == 0
     assert lib.specdec_ngram_workspace_size(3, 0) == 0
-    assert lib.specdec_ngram_workspace_size(3, 4096) == 3 * 8
-    assert lib.specdec_ngram_workspace_size(3, 4097) == 3 * 2 * 8
+    assert lib.specdec_ngram_workspace_size(3, 8192) == 3 * 8
+    assert lib.specdec_ngram_workspace_size(3, 8193) == 3 * 2 * 8
 
 
 @pytest.mark.parametrize("kw,status", [

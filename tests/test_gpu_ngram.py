@@ -1,6 +1,6 @@
 """GPU parity of the n-gram drafter (through the C ABI) against its CPU oracle.
 
-Integer work: proposals and counts must be bit-exact.  Cases span one and several 4096-position
+Integer work: proposals and counts must be bit-exact.  Cases span one and several 8192-position
 tiles with a ragged last tile, the 16-byte and the 4-byte load paths, every degenerate history
 (empty, one token, repeated token, nothing repeats), invalid lengths, and the full 512 x 8192
 drafting workload (sampled sequences, in the launch configuration the benchmark times).
@@ -59,23 +59,25 @@ def test_small_histories(V, cap, K, n_min, n_max):
     check(h, K, n_min, n_max)
 
 
-@pytest.mark.parametrize("cap,misalign", [(10004, False), (10001, False), (10004, True)])
+@pytest.mark.parametrize("cap,misalign", [(20004, False), (20001, False), (20004, True),
+                                          (8192, False), (8191, True)])
 def test_several_tiles_and_load_paths(cap, misalign):
-    # Three 4096-position tiles with a ragged last one; a small vocabulary makes matches
-    # frequent everywhere, including in the halo between tiles.
+    # Up to three 8192-position tiles with a ragged last one (one tile: the fused emit); a
+    # small vocabulary makes matches frequent everywhere, including in the halo between tiles.
     h = hist.make_histories(24, cap, 40, seed=300 + cap, len_range=(cap - 3000, cap),
                             seg_range=(2, 30), edge_cases=True, name="multi_tile")
     check(h, 8, 1, 4, misalign=misalign)
 
 
 def test_matches_that_straddle_a_tile_boundary():
-    # History ending in the run 1 2 3 4 whose only earlier occurrence straddles position 4096.
-    cap = 8200
+    # History ending in the run 1 2 3 4 whose only earlier occurrence straddles position 8192,
+    # the boundary between the first two 8192-position tiles.
+    cap = 16400
     toks = np.full((1, cap), hist.PAD_TOKEN, dtype=np.int32)
-    L = 8190
-    body = (np.arange(L) % 997 + 10).astype(np.int32)        # no 4-gram repeats except below
-    body[4094:4098] = [1, 2, 3, 4]
-    body[4098] = 77
+    L = 16390
+    body = (np.arange(L) % 997 + 10).astype(np.int32)        # only values >= 10 elsewhere
+    body[8190:8194] = [1, 2, 3, 4]
+    body[8194] = 77
     body[L - 4:] = [1, 2, 3, 4]
     toks[0, :L] = body
     h = hist.Histories(toks, np.array([L], dtype=np.int32), 1000, name="straddle")
