@@ -57,13 +57,19 @@ def measured_traffic(bytes_alg_per_launch: float):
 
 class HipEvents:
     """Raw hipEvent_t pairs from the HIP runtime (handed to the library, which records them on
-    the kernel's own stream)."""
+    the kernel's own stream).  They are timing-only events created without the system-scope
+    fence (hipEventDisableSystemFence): recording one then costs no L2 writeback / invalidate,
+    which would otherwise be charged to the bracketed kernel.  Elapsed times are read only after
+    a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, n: int):
         import ctypes
         self.ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -71,8 +77,8 @@ class HipEvents:
 
     def _make(self):
         e = self.ct.c_void_p()
-        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         return e.value
 
     def elapsed_ms(self, i: int) -> float:
