@@ -672,19 +672,42 @@ __device__ __forceinline__ void group_weights(const float (&zv)[kGroup], const f
   }
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// fp64 wave scans with DPP moves of both 32-bit halves (no LDS round trips): row_shr 1, 2, 4, 8
+// within each 16-lane row, then row_bcast 15 / 31 carry the row totals across rows.  Lanes whose
+// DPP source lies outside the row read 0, so the additions are the textbook inclusive scan.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_move_d(double v) {
+  const long long bits = __double_as_longlong(v);
+  const int lo =
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, kRowMask, 0xf, false);
+  const int hi =
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, kRowMask, 0xf, false);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  v += dpp_move_d<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move_d<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move_d<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move_d<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move_d<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(v, off, 64);
-    if (lane >= off) v = y + v;
-  }
-  return v;
+// Lane l's value, read by every lane (uniform).
+__device__ __forceinline__ double read_lane_d(double v, int l) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), l);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), l);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+// Sum over the wave, the same in every lane.
+__device__ __forceinline__ double wave_total(double v) {
+  return read_lane_d(wave_inclusive_scan(v), 63);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -770,8 +793,8 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
       le += ge;
     }
   }
-  lw = wave_sum(lw);
-  le = wave_sum(le);
+  lw = wave_total(lw);
+  le = wave_total(le);
   if (lane == 0) segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
 }
 
@@ -788,54 +811,53 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     const int nseg = S * kSegPerChunk;
     const SegSums* segs = all_segs + static_cast<long long>(b) * nseg;
-    // The first 64 segment sums are fetched alongside the sequence's state.
-    SegSums first{0.0, 0.0};
-    if (wave == 0 && lane < nseg) first = segs[lane];
+    // Lane l owns the contiguous segments [l * P, l * P + P); its sums are loaded with the state.
+    const int P = (nseg + 63) / 64;
+    const int j0 = lane * P;
+    double lw = 0.0, le = 0.0;
+    if (wave == 0)
+      for (int q = 0; q < P; ++q)
+        if (j0 + q < nseg) {
+          const SegSums sq = segs[j0 + q];
+          lw += sq.w;
+          le += sq.e;
+        }
     const SeqState st = states[b];
     if (st.mode == kNone) continue;
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
     const LT* z = logits + row * V;
-    // ---- The segment holding t = u * total (fp64 running sums in segment order). ----
+    // ---- The segment holding t = u * total: one fp64 scan of the lane totals. ----
     if (wave == 0) {
-      // Pass 1: totals of both weight kinds, with the same scan arithmetic as pass 2.
-      double base_w = 0.0, base_e = 0.0;
-      for (int j0 = 0; j0 < nseg; j0 += 64) {
-        const int j = j0 + lane;
-        const SegSums sj = j0 == 0 ? first : (j < nseg ? segs[j] : SegSums{0.0, 0.0});
-        const double vw = sj.w, ve = sj.e;
-        const double iw = wave_inclusive_scan(vw, lane), ie = wave_inclusive_scan(ve, lane);
-        base_w += __shfl(iw, 63, 64);
-        base_e += __shfl(ie, 63, 64);
-      }
-      const bool plain = !(base_w > 0.0);  // empty residual: draw from p itself
-      const double R = plain ? base_e : base_w;
+      const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
+      const bool plain = !(read_lane_d(iw, 63) > 0.0);  // empty residual: draw from p itself
+      const double inc = plain ? ie : iw;
+      const double own = plain ? le : lw;
+      const double R = read_lane_d(inc, 63);
       const double t =
           static_cast<double>(uniforms[static_cast<long long>(b) * (K + 1) + st.ucol]) * R;
-      // Pass 2: first segment whose running sum exceeds t.
-      double base = 0.0;
-      int seg = -1, lastpos = -1;
-      double base_at_seg = 0.0, base_at_last = 0.0;
-      for (int j0 = 0; j0 < nseg && seg < 0; j0 += 64) {
-        const int j = j0 + lane;
-        const SegSums sj = j0 == 0 ? first : (j < nseg ? segs[j] : SegSums{0.0, 0.0});
-        const double v = plain ? sj.e : sj.w;
-        const double inc = wave_inclusive_scan(v, lane);
-        const double exc = base + (inc - v);
-        const unsigned long long hit = __ballot(v > 0.0 && base + inc > t);
-        const unsigned long long pos = __ballot(v > 0.0);
-        if (hit) {
-          const int l = __ffsll(static_cast<long long>(hit)) - 1;
-          seg = j0 + l;
-          base_at_seg = __shfl(exc, l, 64);
-        } else if (pos) {
-          const int l = 63 - __clzll(static_cast<long long>(pos));
-          lastpos = j0 + l;
-          base_at_last = __shfl(exc, l, 64);
+      // The first lane whose running total passes t holds the segment; if rounding left t at
+      // the very top, the last lane with positive weight does.
+      const unsigned long long hit = __ballot(own > 0.0 && inc > t);
+      const unsigned long long pos = __ballot(own > 0.0);
+      const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
+                         : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+      if (lane == hl) {
+        double run = inc - own;                   // running sum before the lane's segments
+        int seg = -1, lastpos = -1;
+        double base_seg = 0.0, base_last = 0.0;
+        for (int q = 0; q < P && j0 + q < nseg; ++q) {
+          const SegSums sq = segs[j0 + q];        // L1-resident: loaded above
+          const double v = plain ? sq.e : sq.w;
+          if (v > 0.0) {
+            if (run + v > t) { seg = j0 + q; base_seg = run; break; }
+            lastpos = j0 + q;
+            base_last = run;
+          }
+          run += v;
         }
-        base += __shfl(inc, 63, 64);
+        if (seg < 0) { seg = lastpos >= 0 ? lastpos : j0; base_seg = base_last; }
+        sh_seg = seg; sh_plain = plain; sh_t = t; sh_base = base_seg;
       }
-      if (seg < 0) { seg = lastpos >= 0 ? lastpos : 0; base_at_seg = base_at_last; }
-      if (lane == 0) { sh_seg = seg; sh_plain = plain; sh_t = t; sh_base = base_at_seg; }
     }
     __syncthreads();
     // ---- Scan the chosen segment in ascending token order. ----
@@ -852,7 +874,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     float zg[kGroup], qg[kGroup], w[kGroup], gw, ge;
     load_group<LT, kVec>(z, qs, cc0 + v0, cnt, zg, qg);
     group_weights(zg, qg, cc0 + v0, cnt, st, plain, w, gw, ge);
-    const double inc = wave_inclusive_scan(static_cast<double>(gw), lane);
+    const double inc = wave_inclusive_scan(static_cast<double>(gw));
     if (lane == 63) sh_wtot[wave] = inc;
     __syncthreads();
     double before = sh_base;
