@@ -131,68 +131,60 @@ __device__ __forceinline__ Stat row16_reduce(Stat v, float c) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Streaming statistics of one chunk: (max, sum of exp2((z - max) * c)) of the thread's
-// kPerThread logits.
+// Streaming statistics of one wave's sub-chunk.  The wave's max is reduced first and every lane
+// exponentiates against it, so the sum is a plain wave sum: one exp per logit plus one, instead
+// of a rescaling (m, s) merge at every reduction step.
 // ------------------------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float read_lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Max over the wave (every lane gets it): 16-lane rows by DPP, then the four row results.
+// fmaxf ignores NaN; a NaN logit poisons the sum instead.
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  return fmaxf(fmaxf(read_lane_f(v, 0), read_lane_f(v, 16)),
+               fmaxf(read_lane_f(v, 32), read_lane_f(v, 48)));
+}
+
+// Sum over the wave in a fixed order (every lane gets it).
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x128>(v);
+  return (read_lane_f(v, 0) + read_lane_f(v, 16)) + (read_lane_f(v, 32) + read_lane_f(v, 48));
+}
+
 struct MaxSum {
   float m;
   float s;
 };
 
-__device__ __forceinline__ MaxSum merge_ms(const MaxSum& x, const MaxSum& y, float c) {
-  const float m = fmaxf(x.m, y.m);
-  if (m == -INFINITY) return MaxSum{m, x.s + y.s};  // both empty: sums are 0 (NaN stays NaN)
-  return MaxSum{m, x.s * __builtin_amdgcn_exp2f((x.m - m) * c) +
-                       y.s * __builtin_amdgcn_exp2f((y.m - m) * c)};
-}
-
-__device__ __forceinline__ MaxSum fold_chunk(const float (&x)[kPerThread], float c) {
-  float bm = x[0];
-#pragma unroll
-  for (int j = 1; j < kPerThread; ++j) bm = fmaxf(bm, x[j]);
-  // exp2((x - ref) * c) as exp2(fma(x, c, -hi)) * exp2(-lo) with ref * c = hi + lo exactly:
-  // one fma per logit, and the exponent is exact up to the fma's single rounding.  An all
-  // -inf (or NaN) chunk keeps the reference at 0 so -inf maps to exp2(-inf) = 0; NaN and
-  // +inf logits make the sum NaN, which marks the row invalid.
-  const float ref = (bm == -INFINITY) ? 0.f : bm;
-  const float hi = ref * c;
-  const float lo = fmaf(ref, c, -hi);
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-  for (int j = 0; j < kPerThread; j += 4) {
-    s0 += __builtin_amdgcn_exp2f(fmaf(x[j], c, -hi));
-    s1 += __builtin_amdgcn_exp2f(fmaf(x[j + 1], c, -hi));
-    s2 += __builtin_amdgcn_exp2f(fmaf(x[j + 2], c, -hi));
-    s3 += __builtin_amdgcn_exp2f(fmaf(x[j + 3], c, -hi));
-  }
-  return MaxSum{bm, ((s0 + s1) + (s2 + s3)) * __builtin_amdgcn_exp2f(-lo)};
-}
-
-// Match mode: (max, sum, sum below the drafted id) of the thread's logits, with the masked
-// sum taken in the same order and against the same reference as the whole sum.
-struct MaxSumPre {
-  float m;
-  float s;
-  float p;
-};
-
-__device__ __forceinline__ MaxSumPre merge_msp(const MaxSumPre& x, const MaxSumPre& y, float c) {
-  const float m = fmaxf(x.m, y.m);
-  if (m == -INFINITY) return MaxSumPre{m, x.s + y.s, x.p + y.p};
-  const float fx = __builtin_amdgcn_exp2f((x.m - m) * c), fy = __builtin_amdgcn_exp2f((y.m - m) * c);
-  return MaxSumPre{m, x.s * fx + y.s * fy, x.p * fx + y.p * fy};
-}
-
 template <typename LT, bool kVec>
 __device__ __forceinline__ int tok_of(int c0, int lane, int j);
 
-template <typename LT, bool kVec>
-__device__ __forceinline__ MaxSumPre fold_chunk_pre(const float (&x)[kPerThread], float c, int c0,
-                                                    int lane, int xid) {
+// (max, sum of exp2((z - max) * c)) of the wave's logits, and with kPre the same sum over the
+// tokens below `xid` (match mode).  exp2((z - m) * c) is taken as exp2(fma(z, c, -hi)) * exp2(-lo)
+// with m * c = hi + lo split exactly: one fma per logit and an exponent exact up to the fma's
+// rounding.  An all -inf (or NaN) sub-chunk keeps the reference at 0 so -inf maps to 0; NaN and
+// +inf logits make the sum NaN, which marks the row invalid.
+template <typename LT, bool kVec, bool kPre>
+__device__ __forceinline__ MaxSum fold_wave(const float (&x)[kPerThread], float c, int c0,
+                                           int lane, int xid, float& lane_max, float& pre) {
   float bm = x[0];
 #pragma unroll
   for (int j = 1; j < kPerThread; ++j) bm = fmaxf(bm, x[j]);
-  const float ref = (bm == -INFINITY) ? 0.f : bm;
+  lane_max = bm;
+  const float M = wave_max_f(bm);
+  const float ref = (M == -INFINITY) ? 0.f : M;
   const float hi = ref * c;
   const float lo = fmaf(ref, c, -hi);
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
@@ -203,13 +195,16 @@ __device__ __forceinline__ MaxSumPre fold_chunk_pre(const float (&x)[kPerThread]
     const float e2 = __builtin_amdgcn_exp2f(fmaf(x[j + 2], c, -hi));
     const float e3 = __builtin_amdgcn_exp2f(fmaf(x[j + 3], c, -hi));
     s0 += e0; s1 += e1; s2 += e2; s3 += e3;
-    p0 += tok_of<LT, kVec>(c0, lane, j) < xid ? e0 : 0.f;
-    p1 += tok_of<LT, kVec>(c0, lane, j + 1) < xid ? e1 : 0.f;
-    p2 += tok_of<LT, kVec>(c0, lane, j + 2) < xid ? e2 : 0.f;
-    p3 += tok_of<LT, kVec>(c0, lane, j + 3) < xid ? e3 : 0.f;
+    if constexpr (kPre) {
+      p0 += tok_of<LT, kVec>(c0, lane, j) < xid ? e0 : 0.f;
+      p1 += tok_of<LT, kVec>(c0, lane, j + 1) < xid ? e1 : 0.f;
+      p2 += tok_of<LT, kVec>(c0, lane, j + 2) < xid ? e2 : 0.f;
+      p3 += tok_of<LT, kVec>(c0, lane, j + 3) < xid ? e3 : 0.f;
+    }
   }
   const float f = __builtin_amdgcn_exp2f(-lo);
-  return MaxSumPre{bm, ((s0 + s1) + (s2 + s3)) * f, ((p0 + p1) + (p2 + p3)) * f};
+  if constexpr (kPre) pre = wave_sum_f((p0 + p1) + (p2 + p3)) * f;
+  return MaxSum{M, wave_sum_f((s0 + s1) + (s2 + s3)) * f};
 }
 
 __device__ __forceinline__ int wave_min(int v) {
@@ -567,33 +562,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     gathers[slot] = gi;
   }
   const float c = temp_valid(T) ? temp_scale(T) : kLog2e;  // invalid rows: result unused
-  // Match mode also needs, per drafted sampled row, the sum below the drafted id x_i: only the
-  // sub-chunk that contains x_i takes the masked sum; below x_i it is the whole sum.
+  // Match mode also needs, per drafted sampled row, the sum below the drafted id x_i (for other
+  // rows xi = -1 and that sum is 0).
   float pre = 0.f, lane_max;
   MaxSum st;
-  bool have_pre = false;
-  int xi = -1;
   if constexpr (kMatch) {
-    xi = (i < kb && T != 0.f) ? proposed[static_cast<long long>(b) * K + i] : -1;
-    if (xi >= c0 && xi < c0 + n) {
-      MaxSumPre sp = fold_chunk_pre<LT, kVec>(x, c, c0, lane, xi);
-      lane_max = sp.m;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1)
-        sp = merge_msp(sp, MaxSumPre{__shfl_xor(sp.m, off, 64), __shfl_xor(sp.s, off, 64),
-                                     __shfl_xor(sp.p, off, 64)}, c);
-      st = MaxSum{sp.m, sp.s};
-      pre = sp.p;
-      have_pre = true;
-    }
-  }
-  if (!have_pre) {
-    st = fold_chunk(x, c);
-    lane_max = st.m;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-      st = merge_ms(st, MaxSum{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)}, c);
-    if constexpr (kMatch) pre = xi >= c0 + n ? st.s : 0.f;
+    const int xi = (i < kb && T != 0.f) ? proposed[static_cast<long long>(b) * K + i] : -1;
+    st = fold_wave<LT, kVec, true>(x, c, c0, lane, xi, lane_max, pre);
+  } else {
+    st = fold_wave<LT, kVec, false>(x, c, c0, lane, -1, lane_max, pre);
   }
   int arg = 0;
   if (T == 0.f) {
