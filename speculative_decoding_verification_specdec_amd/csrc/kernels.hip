@@ -86,49 +86,6 @@ struct Stat {
   int a;
 };
 
-__device__ __forceinline__ Stat merge(const Stat& x, const Stat& y, float c) {
-  Stat r;
-  r.m = fmaxf(x.m, y.m);
-  if (r.m == -INFINITY) {  // both empty (or all -inf): sums are 0 (NaN stays NaN)
-    r.s = x.s + y.s;
-    r.a = min(x.a, y.a);
-    return r;
-  }
-  r.s = x.s * __builtin_amdgcn_exp2f((x.m - r.m) * c) +
-        y.s * __builtin_amdgcn_exp2f((y.m - r.m) * c);
-  r.a = (y.m > x.m || (y.m == x.m && y.a < x.a)) ? y.a : x.a;
-  return r;
-}
-
-__device__ __forceinline__ Stat wave_reduce(Stat v, float c) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Stat o;
-    o.m = __shfl_xor(v.m, off, 64);
-    o.s = __shfl_xor(v.s, off, 64);
-    o.a = __shfl_xor(v.a, off, 64);
-    v = merge(v, o, c);
-  }
-  return v;
-}
-
-// All-reduce of a Stat over each 16-lane row of the wave with DPP (quad_perm xor 1, xor 2,
-// then row_ror 4, 8): no LDS traffic.  Every lane of a row ends with its row's result; lane
-// 16k + 0 is read, so the merge order is fixed.
-template <int kCtrl>
-__device__ __forceinline__ Stat dpp_stat(const Stat& v) {
-  return Stat{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.m), kCtrl, 0xf, 0xf, false)),
-              __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.s), kCtrl, 0xf, 0xf, false)),
-              __builtin_amdgcn_update_dpp(0, v.a, kCtrl, 0xf, 0xf, false)};
-}
-
-__device__ __forceinline__ Stat row16_reduce(Stat v, float c) {
-  v = merge(v, dpp_stat<0xB1>(v), c);   // quad_perm [1,0,3,2]
-  v = merge(v, dpp_stat<0x4E>(v), c);   // quad_perm [2,3,0,1]
-  v = merge(v, dpp_stat<0x124>(v), c);  // row_ror:4
-  v = merge(v, dpp_stat<0x128>(v), c);  // row_ror:8
-  return v;
-}
 
 // ------------------------------------------------------------------------------------------
 // Streaming statistics of one wave's sub-chunk.  The wave's max is reduced first and every lane
@@ -161,6 +118,44 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   v += dpp_f<0x124>(v);
   v += dpp_f<0x128>(v);
   return (read_lane_f(v, 0) + read_lane_f(v, 16)) + (read_lane_f(v, 32) + read_lane_f(v, 48));
+}
+
+// fp64 wave scans with DPP moves of both 32-bit halves (no LDS round trips): row_shr 1, 2, 4, 8
+// within each 16-lane row, then row_bcast 15 / 31 carry the row totals across rows.  Lanes whose
+// DPP source lies outside the row read 0, so the additions are the textbook inclusive scan.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_move_d(double v) {
+  const long long bits = __double_as_longlong(v);
+  const int lo =
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, kRowMask, 0xf, false);
+  const int hi =
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, kRowMask, 0xf, false);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  v += dpp_move_d<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move_d<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move_d<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move_d<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move_d<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Lane l's value, read by every lane (uniform).
+__device__ __forceinline__ double read_lane_d(double v, int l) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), l);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), l);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+// Sum over the wave, the same in every lane.
+__device__ __forceinline__ double wave_total(double v) {
+  return read_lane_d(wave_inclusive_scan(v), 63);
 }
 
 struct MaxSum {
@@ -252,6 +247,55 @@ __device__ __forceinline__ int tok_of(int c0, int lane, int j) {
   }
 }
 
+// Max-first merges of the row partials for the accept scan: the maximum is found first and each
+// sum is rescaled once against it (independent exps, no dependent chain of pairwise merges).
+// The lowest index attaining the maximum is kept for greedy rows.
+__device__ __forceinline__ Stat merge4(const Stat& v, const RowPartial (&p)[4], float c) {
+  float M = v.m;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) M = fmaxf(M, p[t].m);
+  Stat r{M, 0.f, INT_MAX};
+  if (M == -INFINITY) {  // nothing but empty sub-chunks (NaN sums stay NaN)
+    r.s = v.s;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r.s += p[t].s;
+    return r;
+  }
+  r.s = v.s * __builtin_amdgcn_exp2f((v.m - M) * c);
+  r.a = v.m == M ? v.a : INT_MAX;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    r.s += p[t].s * __builtin_amdgcn_exp2f((p[t].m - M) * c);
+    if (p[t].m == M) r.a = min(r.a, p[t].arg);
+  }
+  return r;
+}
+
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+
+// The same over each 16-lane row (every lane of a row ends with its row's result).
+__device__ __forceinline__ Stat row16_reduce_mf(const Stat& v, float c) {
+  float M = v.m;
+  M = fmaxf(M, dpp_f<0xB1>(M));
+  M = fmaxf(M, dpp_f<0x4E>(M));
+  M = fmaxf(M, dpp_f<0x124>(M));
+  M = fmaxf(M, dpp_f<0x128>(M));
+  float sum = M == -INFINITY ? v.s : v.s * __builtin_amdgcn_exp2f((v.m - M) * c);
+  sum += dpp_f<0xB1>(sum);
+  sum += dpp_f<0x4E>(sum);
+  sum += dpp_f<0x124>(sum);
+  sum += dpp_f<0x128>(sum);
+  int a = v.m == M ? v.a : INT_MAX;
+  a = min(a, dpp_i<0xB1>(a));
+  a = min(a, dpp_i<0x4E>(a));
+  a = min(a, dpp_i<0x124>(a));
+  a = min(a, dpp_i<0x128>(a));
+  return Stat{M, sum, a};
+}
+
 // Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count
 // and temperature (an invalid pair poisons the sequence).  Every load that needs neither of
 // them goes out first: the drafted ids with their gathered logit and q (recorded by the
@@ -298,13 +342,11 @@ __device__ __forceinline__ SeqState accept_sequence(const uint8_t* onehot, const
         }
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[h] = merge(v[h], Stat{pb[h][t].m, pb[h][t].s, pb[h][t].arg}, c);
+      for (int h = 0; h < 2; ++h) v[h] = merge4(v[h], pb[h], c);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const Stat red = row16_reduce(v[h], c);
+      const Stat red = row16_reduce_mf(v[h], c);
       const int base = i0 + 4 * h;
       const int src = ((lane - base) & 3) * 16;
       const Stat got{__shfl(red.m, src, 64), __shfl(red.s, src, 64), __shfl(red.a, src, 64)};
@@ -389,37 +431,45 @@ struct StatD {
   double p;  // the same sum below the drafted id
 };
 
-__device__ __forceinline__ StatD merge_d(const StatD& x, const StatD& y, float c) {
-  const float m = fmaxf(x.m, y.m);
-  if (m == -INFINITY) return StatD{m, x.s + y.s, x.p + y.p};
-  const double fx = __builtin_amdgcn_exp2f((x.m - m) * c);
-  const double fy = __builtin_amdgcn_exp2f((y.m - m) * c);
-  return StatD{m, x.s * fx + y.s * fy, x.p * fx + y.p * fy};
+__device__ __forceinline__ StatD merge4_d(const StatD& v, const RowPartial (&p)[4], float c) {
+  float M = v.m;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) M = fmaxf(M, p[t].m);
+  StatD r{M, v.s, v.p};
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { r.s += p[t].s; r.p += p[t].pre; }
+    return r;
+  }
+  const double fv = __builtin_amdgcn_exp2f((v.m - M) * c);
+  r.s = v.s * fv;
+  r.p = v.p * fv;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const double f = __builtin_amdgcn_exp2f((p[t].m - M) * c);
+    r.s += static_cast<double>(p[t].s) * f;
+    r.p += static_cast<double>(p[t].pre) * f;
+  }
+  return r;
 }
 
-template <int kCtrl>
-__device__ __forceinline__ double dpp_d(double v) {
-  const long long bits = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, 0xf, 0xf,
-                                             false);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-template <int kCtrl>
-__device__ __forceinline__ StatD dpp_statd(const StatD& v) {
-  return StatD{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.m), kCtrl, 0xf, 0xf,
-                                                          false)),
-               dpp_d<kCtrl>(v.s), dpp_d<kCtrl>(v.p)};
-}
-
-__device__ __forceinline__ StatD row16_reduce_d(StatD v, float c) {
-  v = merge_d(v, dpp_statd<0xB1>(v), c);
-  v = merge_d(v, dpp_statd<0x4E>(v), c);
-  v = merge_d(v, dpp_statd<0x124>(v), c);
-  v = merge_d(v, dpp_statd<0x128>(v), c);
-  return v;
+__device__ __forceinline__ StatD row16_reduce_d(const StatD& v, float c) {
+  float M = v.m;
+  M = fmaxf(M, dpp_f<0xB1>(M));
+  M = fmaxf(M, dpp_f<0x4E>(M));
+  M = fmaxf(M, dpp_f<0x124>(M));
+  M = fmaxf(M, dpp_f<0x128>(M));
+  const double f = M == -INFINITY ? 1.0 : static_cast<double>(__builtin_amdgcn_exp2f((v.m - M) * c));
+  double sum = v.s * f, pre = v.p * f;
+  sum += dpp_move_d<0xB1, 0xf>(sum);
+  pre += dpp_move_d<0xB1, 0xf>(pre);
+  sum += dpp_move_d<0x4E, 0xf>(sum);
+  pre += dpp_move_d<0x4E, 0xf>(pre);
+  sum += dpp_move_d<0x124, 0xf>(sum);
+  pre += dpp_move_d<0x124, 0xf>(pre);
+  sum += dpp_move_d<0x128, 0xf>(sum);
+  pre += dpp_move_d<0x128, 0xf>(pre);
+  return StatD{M, sum, pre};
 }
 
 __device__ __forceinline__ double shfl_d(double v, int src) {
@@ -467,10 +517,7 @@ __device__ __forceinline__ SeqState accept_sequence_match(const float* uniforms,
         }
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          v[h] = merge_d(v[h], StatD{pb[h][t].m, pb[h][t].s, pb[h][t].pre}, c);
+      for (int h = 0; h < 2; ++h) v[h] = merge4_d(v[h], pb[h], c);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -649,43 +696,6 @@ __device__ __forceinline__ void group_weights(const float (&zv)[kGroup], const f
   }
 }
 
-// fp64 wave scans with DPP moves of both 32-bit halves (no LDS round trips): row_shr 1, 2, 4, 8
-// within each 16-lane row, then row_bcast 15 / 31 carry the row totals across rows.  Lanes whose
-// DPP source lies outside the row read 0, so the additions are the textbook inclusive scan.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ double dpp_move_d(double v) {
-  const long long bits = __double_as_longlong(v);
-  const int lo =
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, kRowMask, 0xf, false);
-  const int hi =
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, kRowMask, 0xf, false);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-__device__ __forceinline__ double wave_inclusive_scan(double v) {
-  v += dpp_move_d<0x111, 0xf>(v);  // row_shr:1
-  v += dpp_move_d<0x112, 0xf>(v);  // row_shr:2
-  v += dpp_move_d<0x114, 0xf>(v);  // row_shr:4
-  v += dpp_move_d<0x118, 0xf>(v);  // row_shr:8
-  v += dpp_move_d<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_move_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
-// Lane l's value, read by every lane (uniform).
-__device__ __forceinline__ double read_lane_d(double v, int l) {
-  const long long bits = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), l);
-  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), l);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-// Sum over the wave, the same in every lane.
-__device__ __forceinline__ double wave_total(double v) {
-  return read_lane_d(wave_inclusive_scan(v), 63);
-}
 
 // ------------------------------------------------------------------------------------------
 // Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
