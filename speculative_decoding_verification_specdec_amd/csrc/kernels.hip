@@ -614,8 +614,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   float pre = 0.f, lane_max;
   MaxSum st;
   if constexpr (kMatch) {
+    // Only the sub-chunk that holds x_i takes the masked sum (a wave-uniform branch); below
+    // x_i it is the whole sum, above it 0.
     const int xi = (i < kb && T != 0.f) ? proposed[static_cast<long long>(b) * K + i] : -1;
-    st = fold_wave<LT, kVec, true>(x, c, c0, lane, xi, lane_max, pre);
+    if (xi >= c0 && xi < c0 + n) {
+      st = fold_wave<LT, kVec, true>(x, c, c0, lane, xi, lane_max, pre);
+    } else {
+      st = fold_wave<LT, kVec, false>(x, c, c0, lane, -1, lane_max, pre);
+      pre = xi >= c0 + n ? st.s : 0.f;
+    }
   } else {
     st = fold_wave<LT, kVec, false>(x, c, c0, lane, -1, lane_max, pre);
   }
