@@ -13,10 +13,11 @@
 // that occurs is N = max_e m(e) and its earliest occurrence ends at the smallest e with
 // m(e) = N.  Both fall out of one max-reduction of the key (m(e) << 32) | (2^32 - 1 - e).
 //
-// No atomics.  ngram_match_kernel runs one 1024-thread workgroup per (8192-position tile,
-// sequence): the tile and a 32-token halo are staged in LDS with 16-byte loads, each thread
-// extends the match of 8 positions (consecutive threads on consecutive positions), and the
-// workgroup max-reduces the keys.  When one tile covers the whole history capacity the same
+// No atomics.  ngram_match_kernel runs one 512-thread workgroup per (8192-position tile,
+// sequence): the tile and a 32-token halo are staged in LDS with 16-byte loads (33 KB: four
+// workgroups fit a CU).  Each thread first tests its 16 positions (consecutive threads on
+// consecutive positions) for h[e-1] == h[L-1] with independent LDS reads, then extends only
+// those candidates, and the workgroup max-reduces the keys.  When one tile covers the whole history capacity the same
 // workgroup emits the proposal straight from LDS; otherwise each tile writes its key and
 // ngram_emit_kernel (one wave per sequence) takes the max over tiles and copies the proposal.
 #include <hip/hip_runtime.h>
@@ -26,8 +27,8 @@
 namespace specdec {
 namespace {
 
-constexpr int kNgThreads = 1024;
-constexpr int kNgPer = kNgramTile / kNgThreads;  // 8 positions per thread
+constexpr int kNgThreads = 512;
+constexpr int kNgPer = kNgramTile / kNgThreads;  // 16 positions per thread
 constexpr int kNgHalo = kNgramMaxN;              // tokens staged before the tile
 constexpr int kEmitThreads = 256;                // 4 sequences per emit workgroup
 
@@ -97,13 +98,21 @@ __global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
     }
     __syncthreads();
     unsigned long long best = 0ull;
-#pragma unroll 4
+    // m(e) >= 1 needs h[e-1] == h[L-1]: one independent LDS read per position.
+    const int last = sh_suf[1];
+    unsigned cand = 0u;
+#pragma unroll
     for (int r = 0; r < kNgPer; ++r) {
       const int e = t0 + r * kNgThreads + tid;
-      if (e < 1 || e > L - 1) continue;
+      if (e >= 1 && e <= L - 1 && sh_tok[kNgHalo + (e - t0) - 1] == last) cand |= 1u << r;
+    }
+    while (cand) {
+      const int r = __ffs(cand) - 1;
+      cand &= cand - 1u;
+      const int e = t0 + r * kNgThreads + tid;
       const int base = kNgHalo + (e - t0);
       const int jmax = min(nmax, e);
-      int J = 0;
+      int J = 1;
       while (J < jmax && sh_tok[base - J - 1] == sh_suf[J + 1]) ++J;
       if (J >= n_min)
         best = max_u64(best, (static_cast<unsigned long long>(J) << 32) |

@@ -60,10 +60,11 @@ def test_small_histories(V, cap, K, n_min, n_max):
 
 
 @pytest.mark.parametrize("cap,misalign", [(20004, False), (20001, False), (20004, True),
-                                          (8192, False), (8191, True)])
+                                          (8192, False), (8191, True), (4096, False),
+                                          (4093, True)])
 def test_several_tiles_and_load_paths(cap, misalign):
-    # Up to three 8192-position tiles with a ragged last one (one tile: the fused emit); a
-    # small vocabulary makes matches frequent everywhere, including in the halo between tiles.
+    # One or several 8192-position tiles with a ragged last one; a small vocabulary makes
+    # matches frequent everywhere, including across tile boundaries.
     h = hist.make_histories(24, cap, 40, seed=300 + cap, len_range=(cap - 3000, cap),
                             seg_range=(2, 30), edge_cases=True, name="multi_tile")
     check(h, 8, 1, 4, misalign=misalign)
