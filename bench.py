@@ -221,6 +221,32 @@ def bench_commit(dev, stream, steps=400):
             "sequences_per_s": B / (us * 1e-6)}
 
 
+def bench_workload(dev, stream, inp, description, steps=60):
+    """Whole verify steps on another workload (one replica: a single step's logits already exceed
+    twice the Infinity Cache): verified positions/s and algorithmic GB/s."""
+    import torch
+    from speculative_decoding_verification_specdec_amd import (inputs_to_device,
+                                                               specdec_workspace_size)
+    from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
+    B, K, V = inp.B, inp.K, inp.V
+    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    d = inputs_to_device(inp, dev)
+    call = PreparedVerify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
+                          d["uniforms"], draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
+                          workspace=ws)
+    us = time_replayed([call], steps, stream)
+    acc = call.out[0].cpu().numpy()
+    _, nbytes = algorithmic_bytes(inp, acc)
+    positions = int(inp.draft_counts().sum())
+    del d, call, ws
+    torch.cuda.empty_cache()
+    return {"workload": description, "us_per_call": us,
+            "verified_positions_per_s": positions / (us * 1e-6),
+            "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mean_accept_len": float(acc[acc >= 0].mean()), "invalid_rows": int((acc < 0).sum())}
+
+
 def bench_match(dev, stream, steps=300, replicas=6):
     """Sample-and-match verify on the same B=64, k=5, V=128256 bf16 batch: verified draft
     positions per second and the algorithmic bytes (every used logit row once, ids, uniforms,
@@ -284,6 +310,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the drafter / commit / match-mode / telemetry measurements")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the large-batch and ragged workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -442,6 +470,17 @@ def main():
         res["next_rows"]["verify_match"] = bench_match(dev, stream)
         print("[bench] telemetry", file=sys.stderr, flush=True)
         res["next_rows"]["telemetry"] = bench_telemetry(dev, stream)
+    if not args.no_other_workloads:
+        from speculative_decoding_verification_specdec_amd.inputs import (large_batch_deep,
+                                                                           ragged_mixed)
+        print("[bench] large batch, deep draft", file=sys.stderr, flush=True)
+        res["other_workloads"] = {"large_batch_deep": bench_workload(
+            dev, stream, large_batch_deep(),
+            "B=256, k=8, V=152064, bf16 logits ~N(0,4^2) + 8 on 1% of entries, 25% greedy rows")}
+        print("[bench] ragged mixed drafters", file=sys.stderr, flush=True)
+        res["other_workloads"]["ragged_mixed"] = bench_workload(
+            dev, stream, ragged_mixed(),
+            "B=512, k_b ~ U{1..8} padded to 8, V=128256, bf16; half n-gram (one-hot) rows")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
