@@ -11,8 +11,10 @@
 // operacionales", continuous batching).
 //
 // One 1024-thread workgroup: thread t owns sequences [t*per, (t+1)*per); their emitted counts
-// are summed, scanned across the workgroup (wave shuffles, then the 16 wave totals in LDS),
-// and each thread writes its sequences' offsets, tokens and lengths.  No atomics.
+// are summed and scanned across the workgroup (wave shuffles, then the 16 wave totals in LDS).
+// For batches up to 4096 sequences the counts, lengths and offsets are staged in LDS and the
+// tokens are copied over the flattened (sequence, slot) space, so that the copies coalesce;
+// larger batches copy per sequence.  No atomics.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -22,7 +24,7 @@ namespace {
 
 constexpr int kCmThreads = 1024;
 constexpr int kCmWaves = kCmThreads / 64;
-constexpr int kPre = 9;  // tokens per sequence prefetched before the scan
+constexpr int kCmLds = 4096;  // batches up to this size stage per-sequence data in LDS
 
 // Tokens sequence b commits: A + 1, or 0 for an invalid row / length / overflow.
 __device__ __forceinline__ int emitted_count(int A, int L, int K, int capacity) {
@@ -37,19 +39,21 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
     int32_t* __restrict__ target_kv, int32_t* __restrict__ draft_kv,
     int32_t* __restrict__ packed, int32_t* __restrict__ offsets) {
   __shared__ int sh_wave[kCmWaves];
+  __shared__ int sh_em[kCmLds], sh_base[kCmLds], sh_len[kCmLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (B + kCmThreads - 1) / kCmThreads;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-  // With one sequence per thread (B <= 1024) its first kPre emitted tokens are loaded together
-  // with the lengths, so the copies after the scan wait on no further load.
-  int32_t pre[kPre];
-  if (per == 1 && b0 < b1) {
-    const int32_t* src = out_tokens + static_cast<long long>(b0) * (K + 1);
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) pre[i] = i <= K ? src[i] : 0;
-  }
+  const bool staged = B <= kCmLds;  // per-sequence data fits LDS: coalesced copies below
   int local = 0;
-  for (int b = b0; b < b1; ++b) local += emitted_count(accept_len[b], seq_len[b], K, capacity);
+  for (int b = b0; b < b1; ++b) {
+    const int A = accept_len[b], L = seq_len[b];
+    const int em = emitted_count(A, L, K, capacity);
+    if (staged) {
+      sh_em[b] = em;
+      sh_len[b] = L;
+    }
+    local += em;
+  }
   // Exclusive scan of the per-thread counts over the workgroup.
   int inc = local;
 #pragma unroll
@@ -61,6 +65,38 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
   __syncthreads();
   int base = inc - local;
   for (int w = 0; w < wave; ++w) base += sh_wave[w];
+  if (tid == kCmThreads - 1 && offsets) offsets[B] = base + local;
+  if (staged) {
+    for (int b = b0; b < b1; ++b) {
+      sh_base[b] = base;
+      if (offsets) offsets[b] = base;
+      base += sh_em[b];
+    }
+    __syncthreads();
+    // Token copies over the flattened (sequence, slot) space: consecutive threads take
+    // consecutive slots of a row, so the reads of out_tokens and the writes of the history and
+    // of the packed stream coalesce.
+    const int items = B * (K + 1);
+    for (int g = tid; g < items; g += kCmThreads) {
+      const int b = g / (K + 1), i = g - b * (K + 1);
+      if (i < sh_em[b]) {
+        const int32_t t = out_tokens[g];
+        if (tokens) tokens[static_cast<long long>(b) * capacity + sh_len[b] + i] = t;
+        if (packed) packed[sh_base[b] + i] = t;
+      }
+    }
+    for (int b = tid; b < B; b += kCmThreads) {
+      const int em = sh_em[b];
+      if (em > 0) {
+        const int L = sh_len[b];
+        seq_len[b] = L + em;
+        if (target_kv) target_kv[b] = min(target_kv[b], L + em - 1);
+        if (draft_kv) draft_kv[b] = min(draft_kv[b], L + em - 1);
+      }
+    }
+    return;
+  }
+  // Larger batches: each thread copies its own sequences.
   for (int b = b0; b < b1; ++b) {
     const int A = accept_len[b], L = seq_len[b];
     const int em = emitted_count(A, L, K, capacity);
@@ -69,14 +105,7 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
       const int32_t* src = out_tokens + static_cast<long long>(b) * (K + 1);
       int32_t* dst = tokens ? tokens + static_cast<long long>(b) * capacity + L : nullptr;
       for (int i = 0; i < em; ++i) {
-        int32_t t;
-        if (per == 1 && i < kPre) {
-#pragma unroll
-          for (int j = 0; j < kPre; ++j)  // register array: select without dynamic indexing
-            if (j == i) t = pre[j];
-        } else {
-          t = src[i];
-        }
+        const int32_t t = src[i];
         if (dst) dst[i] = t;
         if (packed) packed[base + i] = t;
       }
@@ -86,7 +115,6 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
     }
     base += em;
   }
-  if (tid == kCmThreads - 1 && offsets) offsets[B] = base;
 }
 
 }  // namespace
