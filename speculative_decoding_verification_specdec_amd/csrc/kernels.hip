@@ -816,6 +816,9 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
           lw += sq.w;
           le += sq.e;
         }
+    // The draw's uniform is column K unless the state says otherwise (match mode), so that
+    // column is fetched with the state rather than after it.
+    const float u_k = uniforms[static_cast<long long>(b) * (K + 1) + K];
     const SeqState st = states[b];
     if (st.mode == kNone) continue;
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
@@ -827,8 +830,8 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
       const double inc = plain ? ie : iw;
       const double own = plain ? le : lw;
       const double R = read_lane_d(inc, 63);
-      const double t =
-          static_cast<double>(uniforms[static_cast<long long>(b) * (K + 1) + st.ucol]) * R;
+      const float u = st.ucol == K ? u_k : uniforms[static_cast<long long>(b) * (K + 1) + st.ucol];
+      const double t = static_cast<double>(u) * R;
       // The first lane whose running total passes t holds the segment; if rounding left t at
       // the very top, the last lane with positive weight does.
       const unsigned long long hit = __ballot(own > 0.0 && inc > t);
