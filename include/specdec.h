@@ -78,7 +78,8 @@ typedef enum {
 
 /* Bytes of device workspace specdec_verify / specdec_verify_greedy need for these sizes
  * (a pure function of B, K, V; 0 for B == 0 or invalid sizes).  The workspace holds
- * per-row partial statistics, per-sequence draw state and per-segment weight sums; it needs
+ * per-row partial statistics, the gathered drafted ids / logits / draft probabilities,
+ * per-sequence draw state and per-segment weight sums; it needs
  * no initialisation and its contents are meaningless after the call.  Calls that overlap
  * in time (different streams) need separate workspaces. */
 size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V);

@@ -8,19 +8,23 @@
 //
 // Three kernels, enqueued back to back on the caller's stream.  They communicate only through
 // the workspace across kernel boundaries: no atomics, no inter-workgroup waiting.
-//   stats_kernel   one 256-thread workgroup per (used target row, 8192-logit chunk).  Issues
-//       the chunk's 16-byte loads first, then folds them into (max, sum of
-//       exp2((z - max) * log2(e)/T), lowest argmax) and writes the chunk partial.
+//   stats_kernel   one 256-thread workgroup per (8192-logit chunk, used target row).  Each wave
+//       issues its 2048-token sub-chunk's 16-byte loads first, reduces the wave max, then sums
+//       exp2((z - max) * log2(e)/T) against it and writes one (max, sum, lowest argmax)
+//       partial per wave; chunk 0 of each drafted row also gathers x_i, z_i[x_i] and q_i(x_i).
 //   accept_draw_kernel  one workgroup per (chunk of the row to draw from, sequence).  Wave 0
 //       runs the sequence's accept scan (lane i <-> target row i: row i's sub-chunk partials
-//       merged by 16 lanes with a DPP all-reduce, p_i(x_i) in fp64, q_i(x_i) gathered, a 64-bit
-//       ballot finds the first rejection); the chunk-0 workgroup emits every token already
-//       known (accepted drafts, greedy argmaxes) and records what remains to be drawn.  Then the
-//       workgroup sums the draw's weights -- s * max(0, p - q), p without the rejected draft,
-//       or p -- over each 2048-token segment of its chunk.
-//   pick_kernel  one workgroup per sequence that needs a draw: scans the segment sums (fp64)
-//       to the segment holding u * total, then scans that one segment in ascending token
-//       order to the first running sum above u * total.
+//       merged max-first by 16 lanes with DPP, p_i(x_i) in fp64, a 64-bit ballot finds the first
+//       rejection); the chunk-0 workgroup emits every token already known (accepted drafts,
+//       greedy argmaxes) and records what remains to be drawn.  Then the workgroup sums the
+//       draw's weights -- s * max(0, p - q), p without the rejected draft, or p -- over each
+//       2048-token segment of its chunk (fp64 DPP wave sums).
+//   pick_kernel  one workgroup per sequence that needs a draw: one fp64 DPP scan over the
+//       segment sums finds the segment holding u * total, then a scan of that one segment in
+//       ascending token order finds the first running sum above u * total.
+// The sample-and-match mode uses the same three kernels (template flag): the streaming kernel
+// also sums below each drafted id, the scan decides y_i == x_i from those sums, and the draw is
+// a plain sample of p at the first mismatch.
 // Every reduction combines in a fixed order, so results are bit-reproducible.
 #include <float.h>
 #include <limits.h>
