@@ -744,7 +744,11 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
   }
   __syncthreads();
   const SeqState st = sh_st;
-  if (st.mode == kNone) return;
+  // A bonus draw (plain p, also every match-mode draw) needs no second pass: its weights summed
+  // per 2048-token segment are the streaming kernel's partials, which the pick kernel rescales
+  // itself.  Residuals are summed here exactly (a one-hot residual taken from the partials would
+  // subtract e(x) from its segment's sum and cancel when x dominates the row).
+  if (st.mode == kNone || st.mode == kBonus) return;
   const long long row = static_cast<long long>(b) * (K + 1) + st.row;
   const LT* z = logits + row * V;
   const float* q = st.mode == kResidual
@@ -801,7 +805,8 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const float* __restrict__ uniforms, int B, int K, int V, int S,
     const SeqState* __restrict__ states, const SegSums* __restrict__ all_segs,
-    int32_t* __restrict__ out_tokens, float* __restrict__ out_probs) {
+    const RowPartial* __restrict__ partials, int32_t* __restrict__ out_tokens,
+    float* __restrict__ out_probs) {
   __shared__ int sh_seg, sh_plain, sh_hit[kWaves], sh_lastpos[kWaves];
   __shared__ float sh_zhit[kWaves], sh_zlast[kWaves];
   __shared__ double sh_t, sh_base, sh_wtot[kWaves];
@@ -827,6 +832,33 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     if (st.mode == kNone) continue;
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
     const LT* z = logits + row * V;
+    // A bonus draw takes its segment sums from the row's partials: segment j's sum of
+    // exp2((z - m) * c) is s_j * exp2((m_j - m) * c).
+    const bool from_partials = st.mode == kBonus;
+    const RowPartial* prow = partials + row * nseg;
+    auto seg_sums = [&](int j, double& w, double& e) {
+      if (!from_partials) {
+        const SegSums sq = segs[j];
+        w = sq.w;
+        e = sq.e;
+        return;
+      }
+      const RowPartial pj = prow[j];
+      const float f = pj.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((pj.m - st.m) * st.c);
+      e = static_cast<double>(pj.s) * static_cast<double>(f);
+      w = e;
+    };
+    if (wave == 0 && from_partials) {
+      lw = 0.0;
+      le = 0.0;
+      for (int q = 0; q < P; ++q)
+        if (j0 + q < nseg) {
+          double w, e;
+          seg_sums(j0 + q, w, e);
+          lw += w;
+          le += e;
+        }
+    }
     // ---- The segment holding t = u * total: one fp64 scan of the lane totals. ----
     if (wave == 0) {
       const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
@@ -847,8 +879,9 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
         int seg = -1, lastpos = -1;
         double base_seg = 0.0, base_last = 0.0;
         for (int q = 0; q < P && j0 + q < nseg; ++q) {
-          const SegSums sq = segs[j0 + q];        // L1-resident: loaded above
-          const double v = plain ? sq.e : sq.w;
+          double sw, se;
+          seg_sums(j0 + q, sw, se);               // L1-resident: loaded above
+          const double v = plain ? se : sw;
           if (v > 0.0) {
             if (run + v > t) { seg = j0 + q; base_seg = run; break; }
             lastpos = j0 + q;
@@ -969,7 +1002,9 @@ hipError_t launch_typed(const LaunchArgs& a) {
                                         : accept_draw_kernel<LT, false, true>)
                            : (vec_draw ? accept_draw_kernel<LT, true, false>
                                        : accept_draw_kernel<LT, false, false>);
-  const int gx = a.greedy_all ? 1 : S;
+  // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
+  // partials): the chunk-0 workgroups that run the scan are enough.
+  const int gx = (a.greedy_all || match) ? 1 : S;
   for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
     const dim3 grid(gx, min(kMaxZ, a.B - b0));
     accept_draw<<<grid, kThreads, 0, a.stream>>>(
@@ -982,11 +1017,11 @@ hipError_t launch_typed(const LaunchArgs& a) {
   if (vec_draw)
     pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
-        a.out_tokens, a.out_probs);
+        a.ws.partials, a.out_tokens, a.out_probs);
   else
     pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
-        a.out_tokens, a.out_probs);
+        a.ws.partials, a.out_tokens, a.out_probs);
   return hipGetLastError();
 }
 
