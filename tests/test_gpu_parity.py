@@ -63,6 +63,12 @@ SMALL = {
     "all_greedy": lambda: gen.make_batch(16, 6, 9001, seed=45, greedy_frac=1.0),
     "all_onehot": lambda: gen.make_batch(16, 6, 9000, seed=46, onehot_frac=1.0),
     "max_K": lambda: gen.make_batch(3, 63, 700, seed=47, draft_sigma=0.2, draft_at_row_temp=True),
+    # q = p up to fp32 rounding: every draft survives and every sequence takes the bonus draw.
+    "bonus_everywhere": lambda: gen.make_batch(16, 5, 20008, seed=48, draft_scale=1.0,
+                                               draft_sigma=0.0, draft_at_row_temp=True),
+    "bonus_peaked_rows": lambda: gen.make_batch(16, 5, 30011, seed=49, z_sigma=4.0,
+                                                boost_frac=0.01, boost=8.0, draft_scale=1.0,
+                                                draft_sigma=0.0, draft_at_row_temp=True),
 }
 
 
