@@ -15,7 +15,7 @@ Sources (cited by title and section):
        (blog.lo0.es) -- section "Pitfalls operacionales", continuous batching: each request
        accepts a different number of tokens per iteration (nested raggedness).
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   C1  lengths are counts.  Before the round sequence b has L = seq_len[b] tokens; the round
       emits A + 1 tokens (A = accept_len[b] accepted drafts, then the correction or bonus),
       which are appended to its history: new seq_len = L + A + 1.

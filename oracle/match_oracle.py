@@ -9,7 +9,7 @@ draft token only while the two agree.  Every emitted token is a draw from p, so 
 but its acceptance rate is the sum of p(x) q(x), below the rejection rule's sum of
 min(p(x), q(x)).
 
-Readings (each also listed in the design doc):
+Readings where the pages leave a step open:
   M1  position i < k_b draws y_i from p_i with the uniform u[b, i]; the bonus position k_b
       draws with u[b, K] (the verify step's column layout, reading R3).  Draws use the verify
       step's inverse CDF (R5) on p_i.

@@ -19,7 +19,7 @@ Sources (cited by title and section):
        closing paragraph on draft-free techniques: drafts proposed by
        longest-prefix match against the last generated tokens.
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   N1  the "recent context" is the last n tokens of the sequence; n is tried
       from n_max down to n_min and the first n with an occurrence wins
       (longest match first, after P3's longest-prefix match).

@@ -13,7 +13,7 @@ Sources (cited by title and section):
        (blog.lo0.es) -- "La matemática que importa: techo y speedup" (same formulas);
        "Pitfalls operacionales": goodput-oriented work tunes the draft length dynamically.
 
-Readings (each also listed in the design doc):
+Readings where the pages leave a step open:
   T1  counters per route, accumulated over calls: rounds, drafted tokens sum k_b, accepted
       sum A_b, emitted sum (A_b + 1), full rounds (A_b = k_b), rejections (A_b < k_b),
       invalid rows, and a histogram of A_b (64 bins).  Rows whose route id is outside

@@ -29,7 +29,7 @@ What one sequence's round computes (all three pages agree on the rule):
     argmax, so a draft survives iff it equals that argmax and the "residual"
     is the argmax itself [P1, paragraph after the proof; P2 greedy argument].
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   R1  temperature: p_i = softmax(z_i / T) of the raw logit row; T = 0 means
       greedy.  Valid temperatures are 0 or finite T >= TEMPERATURE_MIN.
   R2  q is used exactly as supplied (never renormalised or tempered here).
