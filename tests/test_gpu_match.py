@@ -55,6 +55,8 @@ SMALL = {
     "max_K": lambda: gen.make_batch(3, 63, 700, seed=63, draft_sigma=0.1, draft_at_row_temp=True),
     "peaked_rows": lambda: gen.make_batch(24, 6, 30000, seed=64, z_sigma=4.0, boost_frac=0.01,
                                           boost=8.0, draft_sigma=0.2, draft_at_row_temp=True),
+    "huge_vocab": lambda: gen.make_batch(4, 3, 600011, seed=66, draft_sigma=0.1,
+                                         draft_at_row_temp=True),
 }
 
 

@@ -63,6 +63,12 @@ SMALL = {
     "all_greedy": lambda: gen.make_batch(16, 6, 9001, seed=45, greedy_frac=1.0),
     "all_onehot": lambda: gen.make_batch(16, 6, 9000, seed=46, onehot_frac=1.0),
     "max_K": lambda: gen.make_batch(3, 63, 700, seed=47, draft_sigma=0.2, draft_at_row_temp=True),
+    # 600,011 tokens: 74 chunks, 296 segments (several partials per accept-scan lane and
+    # several segments per pick lane), with a ragged last chunk.
+    "huge_vocab": lambda: gen.make_batch(3, 3, 600011, seed=50, draft_sigma=0.3,
+                                         draft_at_row_temp=True),
+    "huge_vocab_mixed": lambda: gen.make_batch(8, 2, 600016, seed=51, greedy_frac=0.25,
+                                               onehot_frac=0.25, ragged=True),
     # q = p up to fp32 rounding: every draft survives and every sequence takes the bonus draw.
     "bonus_everywhere": lambda: gen.make_batch(16, 5, 20008, seed=48, draft_scale=1.0,
                                                draft_sigma=0.0, draft_at_row_temp=True),
