@@ -42,6 +42,7 @@ constexpr float kTempMin = 1e-6f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSub = kChunk / kWaves;          // tokens per wave sub-chunk (2048)
 constexpr int kPerThread = kSub / 64;          // logits per lane per sub-chunk (32)
+constexpr int kMaxRows = 64;           // K + 1 <= 64 target rows per sequence
 
 __device__ __forceinline__ bool temp_valid(float T) {
   return T == 0.f || (T >= kTempMin && T <= FLT_MAX);
@@ -300,63 +301,75 @@ __device__ __forceinline__ Stat row16_reduce_mf(const Stat& v, float c) {
   return Stat{M, sum, a};
 }
 
-// Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count
-// and temperature (an invalid pair poisons the sequence).  Every load that needs neither of
-// them goes out first: the drafted ids with their gathered logit and q (recorded by the
-// streaming kernel), the uniforms, and all K + 1 rows' sub-chunk partials.  Returns what remains
-// to be drawn (the same value in every lane); with `write`, also emits the known tokens,
-// accept_len and the draw state.
-__device__ __forceinline__ SeqState accept_sequence(const uint8_t* onehot, const float* uniforms,
-                                    const Gather* gathers, bool have_q, int b, int kb_raw,
-                                    float T, int K, int V, int S, const RowPartial* partials,
+// Inputs of the accept scan that need neither the row statistics nor the temperature: the
+// drafted ids with their gathered logit and q (recorded by the streaming kernel), the uniforms
+// and the one-hot flag.  Lane i holds slot i; loaded by the deciding wave before anything else.
+struct ScanIn {
+  Gather g;
+  float u;
+  float uk;
+  int onehot;
+};
+
+__device__ __forceinline__ ScanIn load_scan_in(const uint8_t* onehot, const float* uniforms,
+                                               const Gather* gathers, int b, int K, int lane) {
+  const long long row0 = static_cast<long long>(b) * (K + 1);
+  ScanIn in;
+  in.g = lane < K ? gathers[static_cast<long long>(b) * K + lane] : Gather{0.f, 0.f, -1, 0};
+  in.u = (uniforms != nullptr && lane < K) ? uniforms[row0 + lane] : 0.f;
+  in.uk = (uniforms != nullptr && lane == 0) ? uniforms[row0 + K] : 0.f;
+  in.onehot = onehot != nullptr && onehot[b] != 0;
+  return in;
+}
+
+// Row statistics of rows 0..K of one sequence, by every wave of the workgroup: 16 lanes per
+// row, wave w taking rows 4w .. 4w+3 of each 16-row pass, each lane issuing up to 8 of its
+// row's sub-chunk partials (l, l + 16, ...) before merging them max-first; the row's lanes then
+// reduce with DPP and lane 0 of the row stores it in LDS.  Rows past k_b are merged too (their
+// partials are stale) and ignored.
+__device__ __forceinline__ void row_stats(const RowPartial* __restrict__ partials, long long row0,
+                                          int K, int nsub, float c, int wave, int lane,
+                                          Stat* sh_rows) {
+  const int per_lane = (nsub + 15) / 16;
+  const int sl = lane & 15;
+  const RowPartial empty{-INFINITY, 0.f, INT_MAX, 0.f};
+  for (int i0 = 4 * wave; i0 <= K; i0 += 4 * kWaves) {  // wave-uniform
+    const int ri = i0 + (lane >> 4);
+    const RowPartial* P = partials + (row0 + min(ri, K)) * nsub;
+    Stat v{-INFINITY, 0.f, INT_MAX};
+    for (int t0 = 0; t0 < per_lane; t0 += 8) {
+      RowPartial pa[4], pb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ja = sl + 16 * (t0 + t), jb = sl + 16 * (t0 + 4 + t);
+        pa[t] = (ri <= K && ja < nsub) ? P[ja] : empty;
+        pb[t] = (ri <= K && jb < nsub) ? P[jb] : empty;
+      }
+      v = merge4(v, pa, c);
+      v = merge4(v, pb, c);
+    }
+    const Stat red = row16_reduce_mf(v, c);
+    if (sl == 0 && ri <= K) sh_rows[ri] = red;
+  }
+}
+
+// Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count,
+// temperature and the row statistics in LDS (an invalid count or temperature poisons the
+// sequence).  Returns what remains to be drawn (the same value in every lane); with `write`,
+// also emits the known tokens, accept_len and the draw state.
+__device__ __forceinline__ SeqState accept_sequence(const ScanIn& in, bool have_q, int b,
+                                    int kb_raw, float T, int K, int V, const Stat* sh_rows,
                                     int32_t* accept_len, int32_t* out_tokens, float* out_probs,
                                     SeqState* states, bool write, int lane) {
   const long long row0 = static_cast<long long>(b) * (K + 1);
-  const Gather g = lane < K ? gathers[static_cast<long long>(b) * K + lane]
-                            : Gather{0.f, 0.f, -1, 0};
-  const float u = (uniforms != nullptr && lane < K) ? uniforms[row0 + lane] : 0.f;
-  const float uk = (uniforms != nullptr && lane == 0) ? uniforms[row0 + K] : 0.f;
-  const bool onehot_row = onehot != nullptr && onehot[b] != 0;
+  const Gather g = in.g;
+  const float u = in.u, uk = in.uk;
   const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
   const int kb = seq_ok ? kb_raw : 0;
   const bool greedy = (T == 0.f);
-  const bool is_onehot = !greedy && onehot_row;
+  const bool is_onehot = !greedy && in.onehot;
   const float c = seq_ok ? temp_scale(T) : kLog2e;
-
-  // Row statistics: four rows per pass, sixteen lanes per row, two passes' loads in flight
-  // at a time.  Lane l of a row merges the row's sub-chunk partials l, l + 16, ... in order,
-  // the row's lanes all-reduce with DPP, and lane i keeps row i's result (from the row's lane 0).
-  // Rows past k_b are merged too (their partials are stale) and ignored.
-  Stat st{-INFINITY, 0.f, INT_MAX};
-  const int nsub = S * kWaves;
-  const int per_lane = (nsub + 15) / 16;
-  const int sl = lane & 15;
-  for (int i0 = 0; i0 <= K; i0 += 8) {
-    Stat v[2] = {Stat{-INFINITY, 0.f, INT_MAX}, Stat{-INFINITY, 0.f, INT_MAX}};
-    for (int t0 = 0; t0 < per_lane; t0 += 4) {
-      RowPartial pb[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ri = i0 + 4 * h + (lane >> 4);
-        const RowPartial* P = partials + (row0 + ri) * nsub;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int j = sl + 16 * (t0 + t);
-          pb[h][t] = (ri <= K && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0.f};
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) v[h] = merge4(v[h], pb[h], c);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const Stat red = row16_reduce_mf(v[h], c);
-      const int base = i0 + 4 * h;
-      const int src = ((lane - base) & 3) * 16;
-      const Stat got{__shfl(red.m, src, 64), __shfl(red.s, src, 64), __shfl(red.a, src, 64)};
-      if (lane >= base && lane < base + 4) st = got;
-    }
-  }
+  const Stat st = lane <= K ? sh_rows[lane] : Stat{-INFINITY, 0.f, INT_MAX};
 
   const bool drafted = lane < kb;
   const int x = g.x;
@@ -484,54 +497,47 @@ __device__ __forceinline__ double shfl_d(double v, int src) {
                               static_cast<unsigned int>(lo));
 }
 
-// The match-mode scan of one sampled sequence (greedy and invalid-count sequences take the
-// rejection-rule scan, which treats them identically).  Same layout and outputs as
-// accept_sequence.
-__device__ __forceinline__ SeqState accept_sequence_match(const float* uniforms,
-                                    const Gather* gathers, int b, int kb_raw, float T, int K,
-                                    int V, int S, const RowPartial* partials,
-                                    int32_t* accept_len, int32_t* out_tokens, float* out_probs,
-                                    SeqState* states, bool write, int lane) {
-  const long long row0 = static_cast<long long>(b) * (K + 1);
-  const Gather g = lane < K ? gathers[static_cast<long long>(b) * K + lane]
-                            : Gather{0.f, 0.f, -1, 0};
-  const float u = lane < K ? uniforms[row0 + lane] : 0.f;
-  const float uk = lane == 0 ? uniforms[row0 + K] : 0.f;
-  const bool seq_ok = temp_valid(T);  // T != 0 and k_b in range here
-  const int kb = kb_raw;
-  const float c = seq_ok ? temp_scale(T) : kLog2e;
-
-  // Row sums in fp64 (fp32 partials, fp32 rescale factors), sixteen lanes per row.
-  StatD st{-INFINITY, 0.0, 0.0};
-  const int nsub = S * kWaves;
+// Match-mode row sums S_i and P_i in fp64 (fp32 partials and rescale factors), laid out and
+// merged like row_stats.
+__device__ __forceinline__ void row_stats_d(const RowPartial* __restrict__ partials,
+                                            long long row0, int K, int nsub, float c, int wave,
+                                            int lane, StatD* sh_rows) {
   const int per_lane = (nsub + 15) / 16;
   const int sl = lane & 15;
-  for (int i0 = 0; i0 <= K; i0 += 8) {
-    StatD v[2] = {StatD{-INFINITY, 0.0, 0.0}, StatD{-INFINITY, 0.0, 0.0}};
-    for (int t0 = 0; t0 < per_lane; t0 += 4) {
-      RowPartial pb[2][4];
+  const RowPartial empty{-INFINITY, 0.f, INT_MAX, 0.f};
+  for (int i0 = 4 * wave; i0 <= K; i0 += 4 * kWaves) {  // wave-uniform
+    const int ri = i0 + (lane >> 4);
+    const RowPartial* P = partials + (row0 + min(ri, K)) * nsub;
+    StatD v{-INFINITY, 0.0, 0.0};
+    for (int t0 = 0; t0 < per_lane; t0 += 8) {
+      RowPartial pa[4], pb[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ri = i0 + 4 * h + (lane >> 4);
-        const RowPartial* P = partials + (row0 + ri) * nsub;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int j = sl + 16 * (t0 + t);
-          pb[h][t] = (ri <= K && j < nsub) ? P[j] : RowPartial{-INFINITY, 0.f, INT_MAX, 0.f};
-        }
+      for (int t = 0; t < 4; ++t) {
+        const int ja = sl + 16 * (t0 + t), jb = sl + 16 * (t0 + 4 + t);
+        pa[t] = (ri <= K && ja < nsub) ? P[ja] : empty;
+        pb[t] = (ri <= K && jb < nsub) ? P[jb] : empty;
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) v[h] = merge4_d(v[h], pb[h], c);
+      v = merge4_d(v, pa, c);
+      v = merge4_d(v, pb, c);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const StatD red = row16_reduce_d(v[h], c);
-      const int base = i0 + 4 * h;
-      const int src = ((lane - base) & 3) * 16;
-      const StatD got{__shfl(red.m, src, 64), shfl_d(red.s, src), shfl_d(red.p, src)};
-      if (lane >= base && lane < base + 4) st = got;
-    }
+    const StatD red = row16_reduce_d(v, c);
+    if (sl == 0 && ri <= K) sh_rows[ri] = red;
   }
+}
+
+// The match-mode scan of one sampled sequence with a valid draft count (greedy and
+// invalid-count sequences take the rejection-rule scan, which treats them identically).  Same
+// layout and outputs as accept_sequence.
+__device__ __forceinline__ SeqState accept_sequence_match(const ScanIn& in, int b, int kb, float T,
+                                    int K, int V, const StatD* sh_rows, int32_t* accept_len,
+                                    int32_t* out_tokens, float* out_probs, SeqState* states,
+                                    bool write, int lane) {
+  const long long row0 = static_cast<long long>(b) * (K + 1);
+  const Gather g = in.g;
+  const float u = in.u, uk = in.uk;
+  const bool seq_ok = temp_valid(T);  // T != 0 and k_b in range here
+  const float c = seq_ok ? temp_scale(T) : kLog2e;
+  const StatD st = lane <= K ? sh_rows[lane] : StatD{-INFINITY, 0.0, 0.0};
 
   const bool drafted = lane < kb;
   const int x = g.x;
@@ -720,30 +726,54 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
     const int32_t* __restrict__ num_draft, const float* __restrict__ temperature,
-    const float* __restrict__ uniforms, int b0, int K, int V, int S, int greedy_all,
+    const float* __restrict__ uniforms, int b0, int K, int V, int S, int greedy_all, int phase,
     const RowPartial* __restrict__ partials, const Gather* __restrict__ gathers,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs) {
   constexpr int kGroupsPerLane = kSeg / kGroup / 64;  // 4
   constexpr int kZVec = kGroup * static_cast<int>(sizeof(LT)) / 16;  // 16-byte loads per group
   __shared__ SeqState sh_st;
+  __shared__ Stat sh_rows[kMaxRows];
+  __shared__ StatD sh_rows_d[kMatch ? kMaxRows : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.x, b = b0 + static_cast<int>(blockIdx.y);
-  if (wave == 0) {
+  // Workgroup x of a sequence draws chunks x, x + gridDim.x, ...  Phase 0 scans and draws;
+  // phase 1 only scans (one workgroup per sequence) and phase 2 only draws, reading the state
+  // phase 1 wrote: for a grid of several resident rounds the per-workgroup scan would otherwise
+  // be paid in every round.
+  const int b = b0 + static_cast<int>(blockIdx.y);
+  const bool first = blockIdx.x == 0;
+  if (phase == 2) {
+    if (tid == 0) sh_st = states[b];
+    __syncthreads();
+  } else {
     const int kb = num_draft ? num_draft[b] : K;
     const float T = greedy_all ? 0.f : temperature[b];
-    SeqState st;
-    if (kMatch && T != 0.f && kb >= 0 && kb <= K)
-      st = accept_sequence_match(uniforms, gathers, b, kb, T, K, V, S, partials, accept_len,
-                                 out_tokens, out_probs, states, s == 0, lane);
+    const bool use_match = kMatch && T != 0.f && kb >= 0 && kb <= K;
+    const float c = (kb >= 0 && kb <= K && temp_valid(T)) ? temp_scale(T) : kLog2e;
+    ScanIn in{};
+    if (wave == 0) in = load_scan_in(kMatch ? nullptr : onehot, uniforms, gathers, b, K, lane);
+    // Every wave merges some rows' partials (one round of loads for up to 16 rows), then wave 0
+    // decides.
+    const long long row0 = static_cast<long long>(b) * (K + 1);
+    if (use_match)
+      row_stats_d(partials, row0, K, S * kWaves, c, wave, lane, sh_rows_d);
     else
-      st = accept_sequence(kMatch ? nullptr : onehot, uniforms, gathers,
-                           draft_probs != nullptr, b, kb, T, K, V, S, partials, accept_len,
-                           out_tokens, out_probs, states, s == 0, lane);
-    if (lane == 0) sh_st = st;
+      row_stats(partials, row0, K, S * kWaves, c, wave, lane, sh_rows);
+    __syncthreads();
+    if (wave == 0) {
+      SeqState st;
+      if (use_match)
+        st = accept_sequence_match(in, b, kb, T, K, V, sh_rows_d, accept_len, out_tokens,
+                                   out_probs, states, first, lane);
+      else
+        st = accept_sequence(in, draft_probs != nullptr, b, kb, T, K, V, sh_rows, accept_len,
+                             out_tokens, out_probs, states, first, lane);
+      if (lane == 0) sh_st = st;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const SeqState st = sh_st;
+  if (phase == 1) return;
   // A bonus draw (plain p, also every match-mode draw) needs no second pass: its weights summed
   // per 2048-token segment are the streaming kernel's partials, which the pick kernel rescales
   // itself.  Residuals are summed here exactly (a one-hot residual taken from the partials would
@@ -754,50 +784,53 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
   const float* q = st.mode == kResidual
                        ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
                        : nullptr;
-  const int c0 = s * kChunk, n = min(kChunk, V - c0);
   const int seg0 = wave * kSeg;  // this wave's segment, relative to the chunk
-  double lw = 0.0, le = 0.0;
-  if constexpr (kVec) {
-    // All of the lane's 16-byte loads go out before any is unpacked.
-    uint4 zr[kGroupsPerLane][kZVec], qr[kGroupsPerLane][2];
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    const int c0 = s * kChunk, n = min(kChunk, V - c0);
+    double lw = 0.0, le = 0.0;
+    if constexpr (kVec) {
+      // All of the lane's 16-byte loads go out before any is unpacked.
+      uint4 zr[kGroupsPerLane][kZVec], qr[kGroupsPerLane][2];
 #pragma unroll
-    for (int g = 0; g < kGroupsPerLane; ++g) {
-      const int v0 = c0 + seg0 + (g * 64 + lane) * kGroup;
-      const bool in = v0 < c0 + n;
+      for (int g = 0; g < kGroupsPerLane; ++g) {
+        const int v0 = c0 + seg0 + (g * 64 + lane) * kGroup;
+        const bool in = v0 < c0 + n;
 #pragma unroll
-      for (int h = 0; h < kZVec; ++h)
-        zr[g][h] = in ? stream_load(z + v0 + h * (16 / sizeof(LT))) : make_uint4(0, 0, 0, 0);
+        for (int h = 0; h < kZVec; ++h)
+          zr[g][h] = in ? stream_load(z + v0 + h * (16 / sizeof(LT))) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        qr[g][h] = (in && q != nullptr) ? stream_load(q + v0 + 4 * h) : make_uint4(0, 0, 0, 0);
+        for (int h = 0; h < 2; ++h)
+          qr[g][h] = (in && q != nullptr) ? stream_load(q + v0 + 4 * h) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < kGroupsPerLane; ++g) {
+        const int v0 = seg0 + (g * 64 + lane) * kGroup;
+        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+#pragma unroll
+        for (int h = 0; h < kZVec; ++h)
+          unpack(zr[g][h], zv + h * (16 / sizeof(LT)), static_cast<const LT*>(nullptr));
+        unpack(qr[g][0], qv, static_cast<const float*>(nullptr));
+        unpack(qr[g][1], qv + 4, static_cast<const float*>(nullptr));
+        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+        lw += gw;
+        le += ge;
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < kGroupsPerLane; ++g) {
+        const int v0 = seg0 + (g * 64 + lane) * kGroup;
+        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+        load_group<LT, false>(z, q, c0 + v0, min(kGroup, n - v0), zv, qv);
+        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+        lw += gw;
+        le += ge;
+      }
     }
-#pragma unroll
-    for (int g = 0; g < kGroupsPerLane; ++g) {
-      const int v0 = seg0 + (g * 64 + lane) * kGroup;
-      float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
-#pragma unroll
-      for (int h = 0; h < kZVec; ++h)
-        unpack(zr[g][h], zv + h * (16 / sizeof(LT)), static_cast<const LT*>(nullptr));
-      unpack(qr[g][0], qv, static_cast<const float*>(nullptr));
-      unpack(qr[g][1], qv + 4, static_cast<const float*>(nullptr));
-      group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
-      lw += gw;
-      le += ge;
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < kGroupsPerLane; ++g) {
-      const int v0 = seg0 + (g * 64 + lane) * kGroup;
-      float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
-      load_group<LT, false>(z, q, c0 + v0, min(kGroup, n - v0), zv, qv);
-      group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
-      lw += gw;
-      le += ge;
-    }
+    lw = wave_total(lw);
+    le = wave_total(le);
+    if (lane == 0)
+      segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
   }
-  lw = wave_total(lw);
-  le = wave_total(le);
-  if (lane == 0) segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
 }
 
 template <typename LT, bool kVec>
@@ -1004,14 +1037,24 @@ hipError_t launch_typed(const LaunchArgs& a) {
                                        : accept_draw_kernel<LT, false, false>);
   // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
   // partials): the chunk-0 workgroups that run the scan are enough.
-  const int gx = (a.greedy_all || match) ? 1 : S;
-  for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
-    const dim3 grid(gx, min(kMaxZ, a.B - b0));
-    accept_draw<<<grid, kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms, b0,
-        a.K, a.V, S, a.greedy_all, a.ws.partials, a.ws.gathers, a.accept_len, a.out_tokens,
-        a.out_probs, a.ws.states, a.ws.segs);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  // Otherwise one workgroup per chunk of the row to draw from.
+  // A draw grid of more than one resident round (about six 256-thread workgroups per CU on 256
+  // CUs) scans once per sequence in a separate pass instead.
+  constexpr long long kDrawRound = 1536;
+  const bool draws = !(a.greedy_all || match);
+  const bool split = draws && static_cast<long long>(a.B) * S > kDrawRound;
+  const int phases[2] = {split ? 1 : 0, 2};
+  for (int ph = 0; ph < (split ? 2 : 1); ++ph) {
+    const int phase = phases[ph];
+    const int gx = (phase == 1 || !draws) ? 1 : S;
+    for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
+      const dim3 grid(gx, min(kMaxZ, a.B - b0));
+      accept_draw<<<grid, kThreads, 0, a.stream>>>(
+          logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms,
+          b0, a.K, a.V, S, a.greedy_all, phase, a.ws.partials, a.ws.gathers, a.accept_len,
+          a.out_tokens, a.out_probs, a.ws.states, a.ws.segs);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
   if (a.greedy_all) return hipSuccess;
   if (vec_draw)
