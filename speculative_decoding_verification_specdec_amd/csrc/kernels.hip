@@ -714,6 +714,31 @@ __device__ __forceinline__ void group_weights(const float (&zv)[kGroup], const f
 }
 
 
+// Four consecutive logits as one nontemporal load: 8 bytes of bf16 or 16 bytes of fp32.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <typename LT> struct DrawVec;
+template <> struct DrawVec<uint16_t> {
+  uint2 d;
+  static __device__ __forceinline__ DrawVec load(const uint16_t* p) {
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return DrawVec{make_uint2(t.x, t.y)};
+  }
+  static __device__ __forceinline__ DrawVec zero() { return DrawVec{make_uint2(0, 0)}; }
+  __device__ __forceinline__ void unpack(float* o) const {
+    o[0] = __uint_as_float(d.x << 16); o[1] = __uint_as_float(d.x & 0xffff0000u);
+    o[2] = __uint_as_float(d.y << 16); o[3] = __uint_as_float(d.y & 0xffff0000u);
+  }
+};
+template <> struct DrawVec<float> {
+  uint4 d;
+  static __device__ __forceinline__ DrawVec load(const float* p) { return DrawVec{stream_load(p)}; }
+  static __device__ __forceinline__ DrawVec zero() { return DrawVec{make_uint4(0, 0, 0, 0)}; }
+  __device__ __forceinline__ void unpack(float* o) const {
+    o[0] = __uint_as_float(d.x); o[1] = __uint_as_float(d.y);
+    o[2] = __uint_as_float(d.z); o[3] = __uint_as_float(d.w);
+  }
+};
+
 // ------------------------------------------------------------------------------------------
 // Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
 // by b0).  Wave 0 of every workgroup runs its sequence's accept scan (the partials it reads are
@@ -730,8 +755,7 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const RowPartial* __restrict__ partials, const Gather* __restrict__ gathers,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs) {
-  constexpr int kGroupsPerLane = kSeg / kGroup / 64;  // 4
-  constexpr int kZVec = kGroup * static_cast<int>(sizeof(LT)) / 16;  // 16-byte loads per group
+  constexpr int kGroupsPerLane = kSeg / kGroup / 64;  // 4 (scalar path)
   __shared__ SeqState sh_st;
   __shared__ Stat sh_rows[kMaxRows];
   __shared__ StatD sh_rows_d[kMatch ? kMaxRows : 1];
@@ -789,29 +813,34 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const int c0 = s * kChunk, n = min(kChunk, V - c0);
     double lw = 0.0, le = 0.0;
     if constexpr (kVec) {
-      // All of the lane's 16-byte loads go out before any is unpacked.
-      uint4 zr[kGroupsPerLane][kZVec], qr[kGroupsPerLane][2];
+      // Lane l owns the 4-token quads l, l + 64, ... of the segment: every load instruction of
+      // the wave reads one contiguous span (4 logits, 8 or 16 bytes, and 4 fp32 draft
+      // probabilities, 16 bytes, per lane), and all of them go out before any is unpacked.
+      constexpr int kQuads = kSeg / 4 / 64;  // 8
+      DrawVec<LT> zr[kQuads];
+      uint4 qr[kQuads];
 #pragma unroll
-      for (int g = 0; g < kGroupsPerLane; ++g) {
-        const int v0 = c0 + seg0 + (g * 64 + lane) * kGroup;
+      for (int h = 0; h < kQuads; ++h) {
+        const int v0 = c0 + seg0 + (h * 64 + lane) * 4;
         const bool in = v0 < c0 + n;
-#pragma unroll
-        for (int h = 0; h < kZVec; ++h)
-          zr[g][h] = in ? stream_load(z + v0 + h * (16 / sizeof(LT))) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          qr[g][h] = (in && q != nullptr) ? stream_load(q + v0 + 4 * h) : make_uint4(0, 0, 0, 0);
+        zr[h] = in ? DrawVec<LT>::load(z + v0) : DrawVec<LT>::zero();
+        qr[h] = (in && q != nullptr) ? stream_load(q + v0) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int g = 0; g < kGroupsPerLane; ++g) {
-        const int v0 = seg0 + (g * 64 + lane) * kGroup;
-        float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
+      for (int h = 0; h < kQuads; ++h) {
+        const int v0 = seg0 + (h * 64 + lane) * 4;
+        float zv[4], qv[4];
+        zr[h].unpack(zv);
+        unpack(qr[h], qv, static_cast<const float*>(nullptr));
+        const int cnt = min(4, n - v0);
+        float gw = 0.f, ge = 0.f;
 #pragma unroll
-        for (int h = 0; h < kZVec; ++h)
-          unpack(zr[g][h], zv + h * (16 / sizeof(LT)), static_cast<const LT*>(nullptr));
-        unpack(qr[g][0], qv, static_cast<const float*>(nullptr));
-        unpack(qr[g][1], qv + 4, static_cast<const float*>(nullptr));
-        group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
+        for (int k = 0; k < 4; ++k) {
+          float e = 0.f;
+          const float w = k < cnt ? draw_weight(zv[k], qv[k], c0 + v0 + k, st, false, e) : 0.f;
+          gw += w;
+          ge += k < cnt ? e : 0.f;
+        }
         lw += gw;
         le += ge;
       }
