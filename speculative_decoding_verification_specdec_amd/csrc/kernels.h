@@ -14,8 +14,9 @@ constexpr int kGroup = 8;                   // consecutive tokens per thread in 
 constexpr int kSeg = kThreads * kGroup;     // 2048 tokens per draw segment
 constexpr int kSegPerChunk = kChunk / kSeg; // 4
 
-// Per (row, 2048-token sub-chunk) partial statistics of the streaming pass.
-struct RowPartial {
+// Per (row, 2048-token sub-chunk) partial statistics of the streaming pass.  The 16-byte
+// records (also SeqState, Gather, SegSums) are 16-byte aligned so each is one vector load.
+struct alignas(16) RowPartial {
   float m;      // max logit in the sub-chunk (-inf if none)
   float s;      // sum of exp2((z - m) * c) over the sub-chunk
   int32_t arg;  // lowest index attaining m (greedy rows only)
@@ -30,7 +31,7 @@ enum SampleMode : int32_t {
   kBonus = 3,           // p_k (every draft accepted)
 };
 
-struct SeqState {
+struct alignas(16) SeqState {
   int32_t mode;   // SampleMode
   int32_t row;    // target row j the draw is taken from
   int32_t excl;   // x_j for kResidualOnehot
@@ -43,7 +44,7 @@ struct SeqState {
 
 // One drafted slot's gathered inputs, recorded by the streaming kernel: the proposed id x_i,
 // the target logit z_i[x_i] and the drafter probability q_i(x_i).
-struct Gather {
+struct alignas(16) Gather {
   float z;
   float q;
   int32_t x;
@@ -51,7 +52,7 @@ struct Gather {
 };
 
 // Weight sums of one 2048-token draw segment.
-struct SegSums {
+struct alignas(16) SegSums {
   double w;       // the draw's weights
   double e;       // exp2((z - m) * c), i.e. s * p (fallback when the residual is empty)
 };

@@ -12,13 +12,14 @@
 //       issues its 2048-token sub-chunk's 16-byte loads first, reduces the wave max, then sums
 //       exp2((z - max) * log2(e)/T) against it and writes one (max, sum, lowest argmax)
 //       partial per wave; chunk 0 of each drafted row also gathers x_i, z_i[x_i] and q_i(x_i).
-//   accept_draw_kernel  one workgroup per (chunk of the row to draw from, sequence).  Wave 0
-//       runs the sequence's accept scan (lane i <-> target row i: row i's sub-chunk partials
-//       merged max-first by 16 lanes with DPP, p_i(x_i) in fp64, a 64-bit ballot finds the first
-//       rejection); the chunk-0 workgroup emits every token already known (accepted drafts,
-//       greedy argmaxes) and records what remains to be drawn.  Then the workgroup sums the
-//       draw's weights -- s * max(0, p - q), p without the rejected draft, or p -- over each
-//       2048-token segment of its chunk (fp64 DPP wave sums).
+//   accept_draw_kernel  one workgroup per (chunk of the row to draw from, sequence).  Every
+//       wave merges some rows' sub-chunk partials (16 lanes per row, max-first, DPP) and wave 0
+//       runs the sequence's accept scan (lane i <-> target row i, p_i(x_i) in fp64, a 64-bit
+//       ballot finds the first rejection); the chunk-0 workgroup emits every token already
+//       known (accepted drafts, greedy argmaxes) and records what remains to be drawn.  Then
+//       the workgroup sums the draw's weights -- s * max(0, p - q) or p without the rejected
+//       draft -- over each 2048-token segment of its chunk (fp64 DPP wave sums); a plain draw
+//       of p takes those sums from the streaming kernel's partials instead.
 //   pick_kernel  one workgroup per sequence that needs a draw: one fp64 DPP scan over the
 //       segment sums finds the segment holding u * total, then a scan of that one segment in
 //       ascending token order finds the first running sum above u * total.
@@ -303,7 +304,7 @@ __device__ __forceinline__ Stat row16_reduce_mf(const Stat& v, float c) {
 
 // Inputs of the accept scan that need neither the row statistics nor the temperature: the
 // drafted ids with their gathered logit and q (recorded by the streaming kernel), the uniforms
-// and the one-hot flag.  Lane i holds slot i; loaded by the deciding wave before anything else.
+// and the one-hot flag.  Lane i holds slot i.
 struct ScanIn {
   Gather g;
   float u;
@@ -311,46 +312,38 @@ struct ScanIn {
   int onehot;
 };
 
-__device__ __forceinline__ ScanIn load_scan_in(const uint8_t* onehot, const float* uniforms,
-                                               const Gather* gathers, int b, int K, int lane) {
+// Their loads, issued unconditionally so that all of them -- and the partials after them -- are
+// in flight together: an absent operand (null pointer, or no drafted slot) is read from `any`, a
+// valid 16-byte-aligned stand-in, and discarded by finish_scan_in.  Lane min(i, K) reads
+// uniforms column i, so lane K holds column K.
+struct ScanLoads {
+  Gather g;
+  float u;
+  uint8_t oh;
+};
+
+__device__ __forceinline__ ScanLoads load_scan_in(const uint8_t* onehot, const float* uniforms,
+                                                  const Gather* gathers, const void* any, int b,
+                                                  int K, int lane) {
   const long long row0 = static_cast<long long>(b) * (K + 1);
-  ScanIn in;
-  in.g = lane < K ? gathers[static_cast<long long>(b) * K + lane] : Gather{0.f, 0.f, -1, 0};
-  in.u = (uniforms != nullptr && lane < K) ? uniforms[row0 + lane] : 0.f;
-  in.uk = (uniforms != nullptr && lane == 0) ? uniforms[row0 + K] : 0.f;
-  in.onehot = onehot != nullptr && onehot[b] != 0;
-  return in;
+  const Gather* gp = K > 0 ? gathers + static_cast<long long>(b) * K + min(lane, K - 1)
+                           : static_cast<const Gather*>(any);
+  const float* up = uniforms != nullptr ? uniforms + row0 + min(lane, K)
+                                        : static_cast<const float*>(any);
+  // Lane 0 reads the flag (the others the stand-in) and finish_scan_in broadcasts it.
+  const uint8_t* op = (onehot != nullptr && lane == 0) ? onehot + b
+                                                       : static_cast<const uint8_t*>(any);
+  return ScanLoads{*gp, *up, *op};
 }
 
-// Row statistics of rows 0..K of one sequence, by every wave of the workgroup: 16 lanes per
-// row, wave w taking rows 4w .. 4w+3 of each 16-row pass, each lane issuing up to 8 of its
-// row's sub-chunk partials (l, l + 16, ...) before merging them max-first; the row's lanes then
-// reduce with DPP and lane 0 of the row stores it in LDS.  Rows past k_b are merged too (their
-// partials are stale) and ignored.
-__device__ __forceinline__ void row_stats(const RowPartial* __restrict__ partials, long long row0,
-                                          int K, int nsub, float c, int wave, int lane,
-                                          Stat* sh_rows) {
-  const int per_lane = (nsub + 15) / 16;
-  const int sl = lane & 15;
-  const RowPartial empty{-INFINITY, 0.f, INT_MAX, 0.f};
-  for (int i0 = 4 * wave; i0 <= K; i0 += 4 * kWaves) {  // wave-uniform
-    const int ri = i0 + (lane >> 4);
-    const RowPartial* P = partials + (row0 + min(ri, K)) * nsub;
-    Stat v{-INFINITY, 0.f, INT_MAX};
-    for (int t0 = 0; t0 < per_lane; t0 += 8) {
-      RowPartial pa[4], pb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ja = sl + 16 * (t0 + t), jb = sl + 16 * (t0 + 4 + t);
-        pa[t] = (ri <= K && ja < nsub) ? P[ja] : empty;
-        pb[t] = (ri <= K && jb < nsub) ? P[jb] : empty;
-      }
-      v = merge4(v, pa, c);
-      v = merge4(v, pb, c);
-    }
-    const Stat red = row16_reduce_mf(v, c);
-    if (sl == 0 && ri <= K) sh_rows[ri] = red;
-  }
+__device__ __forceinline__ ScanIn finish_scan_in(const ScanLoads& r, const uint8_t* onehot,
+                                                 const float* uniforms, int K, int lane) {
+  ScanIn in;
+  in.g = lane < K ? r.g : Gather{0.f, 0.f, -1, 0};
+  in.u = (uniforms != nullptr && lane < K) ? r.u : 0.f;
+  in.uk = uniforms != nullptr ? read_lane_f(r.u, K) : 0.f;
+  in.onehot = onehot != nullptr && __builtin_amdgcn_readlane(static_cast<int>(r.oh), 0) != 0;
+  return in;
 }
 
 // Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count,
@@ -497,31 +490,83 @@ __device__ __forceinline__ double shfl_d(double v, int src) {
                               static_cast<unsigned int>(lo));
 }
 
-// Match-mode row sums S_i and P_i in fp64 (fp32 partials and rescale factors), laid out and
-// merged like row_stats.
-__device__ __forceinline__ void row_stats_d(const RowPartial* __restrict__ partials,
-                                            long long row0, int K, int nsub, float c, int wave,
-                                            int lane, StatD* sh_rows) {
+// Row statistics of rows 0..K of one sequence, by every wave of the workgroup: 16 lanes per
+// row, wave w taking rows 4w .. 4w+3 of each 16-row pass, each lane loading up to 8 of its
+// row's sub-chunk partials (l, l + 16, ...) before merging them max-first; the row's lanes then
+// reduce with DPP and lane 0 of the row stores it in LDS.  Rows past k_b are merged too (their
+// partials are stale) and ignored.  With `use_d` (match mode, sampled rows) the merge is the
+// fp64 one of S_i and P_i.
+//
+// The loads are unconditional (indices clamped into the row, out-of-range values replaced
+// after they arrive), and the first batch -- the whole merge while K + 1 <= 16 rows and a row
+// has at most 128 partials -- is issued by prefetch_partials before the kernel reads the draft
+// count and temperature, so no load waits behind a branch or a scalar load.
+struct PartialBatch {
+  RowPartial a[4], b[4];
+};
+
+__device__ __forceinline__ void load_partial_batch(const RowPartial* __restrict__ partials,
+                                                   long long row0, int K, int nsub, int i0,
+                                                   int t0, int lane, PartialBatch& p) {
+  const int ri = i0 + (lane >> 4), sl = lane & 15;
+  const RowPartial* P = partials + (row0 + min(ri, K)) * nsub;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    p.a[t] = P[min(sl + 16 * (t0 + t), nsub - 1)];
+    p.b[t] = P[min(sl + 16 * (t0 + 4 + t), nsub - 1)];
+  }
+}
+
+__device__ __forceinline__ void prefetch_partials(const RowPartial* __restrict__ partials,
+                                                  long long row0, int K, int nsub, int wave,
+                                                  int lane, PartialBatch& p) {
+  load_partial_batch(partials, row0, K, nsub, min(4 * wave, K), 0, lane, p);
+}
+
+template <bool kMatch>
+__device__ __forceinline__ void row_stats(const RowPartial* __restrict__ partials, long long row0,
+                                          int K, int nsub, float c, bool use_d, int wave,
+                                          int lane, const PartialBatch& batch0, Stat* sh_rows,
+                                          StatD* sh_rows_d) {
   const int per_lane = (nsub + 15) / 16;
   const int sl = lane & 15;
   const RowPartial empty{-INFINITY, 0.f, INT_MAX, 0.f};
   for (int i0 = 4 * wave; i0 <= K; i0 += 4 * kWaves) {  // wave-uniform
     const int ri = i0 + (lane >> 4);
-    const RowPartial* P = partials + (row0 + min(ri, K)) * nsub;
-    StatD v{-INFINITY, 0.0, 0.0};
-    for (int t0 = 0; t0 < per_lane; t0 += 8) {
-      RowPartial pa[4], pb[4];
+    Stat v{-INFINITY, 0.f, INT_MAX};
+    StatD vd{-INFINITY, 0.0, 0.0};
+    auto merge_batch = [&](PartialBatch p, int t0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int ja = sl + 16 * (t0 + t), jb = sl + 16 * (t0 + 4 + t);
-        pa[t] = (ri <= K && ja < nsub) ? P[ja] : empty;
-        pb[t] = (ri <= K && jb < nsub) ? P[jb] : empty;
+        if (!(ri <= K && ja < nsub)) p.a[t] = empty;
+        if (!(ri <= K && jb < nsub)) p.b[t] = empty;
       }
-      v = merge4_d(v, pa, c);
-      v = merge4_d(v, pb, c);
+      if (kMatch && use_d) {
+        vd = merge4_d(vd, p.a, c);
+        vd = merge4_d(vd, p.b, c);
+      } else {
+        v = merge4(v, p.a, c);
+        v = merge4(v, p.b, c);
+      }
+    };
+    int t0 = 0;
+    if (i0 == 4 * wave) {  // the prefetched batch
+      merge_batch(batch0, 0);
+      t0 = 8;
     }
-    const StatD red = row16_reduce_d(v, c);
-    if (sl == 0 && ri <= K) sh_rows[ri] = red;
+    for (; t0 < per_lane; t0 += 8) {
+      PartialBatch p;
+      load_partial_batch(partials, row0, K, nsub, i0, t0, lane, p);
+      merge_batch(p, t0);
+    }
+    if (kMatch && use_d) {
+      const StatD red = row16_reduce_d(vd, c);
+      if (sl == 0 && ri <= K) sh_rows_d[ri] = red;
+    } else {
+      const Stat red = row16_reduce_mf(v, c);
+      if (sl == 0 && ri <= K) sh_rows[ri] = red;
+    }
   }
 }
 
@@ -664,29 +709,30 @@ __device__ __forceinline__ float draw_weight(float z, float q, int v, const SeqS
   return fmaxf(0.f, fmaf(-st.s, q, e));  // s * max(0, p - q)
 }
 
-// Loads of the kGroup tokens [v0, v0 + cnt) (cnt <= 0: none); -inf / 0 past cnt.
+// Loads of the kGroup tokens [v0, v0 + cnt) (cnt <= 0: none); -inf / 0 past cnt.  The vector
+// path loads unconditionally -- from `any`, a valid 16-byte-aligned stand-in of at least 32
+// bytes, when there is nothing to read -- and then selects, so the target and draft loads are
+// in flight together.
 template <typename LT, bool kVec>
 __device__ __forceinline__ void load_group(const LT* __restrict__ z, const float* __restrict__ q,
-                                           int v0, int cnt, float (&zv)[kGroup],
-                                           float (&qv)[kGroup]) {
+                                           const void* any, int v0, int cnt,
+                                           float (&zv)[kGroup], float (&qv)[kGroup]) {
   if constexpr (kVec) {  // cnt is kGroup or <= 0; 16-byte aligned
-    if (cnt > 0) {
-      if constexpr (sizeof(LT) == 2) {
-        unpack(stream_load(z + v0), zv, static_cast<const LT*>(nullptr));
-      } else {
-        unpack(stream_load(z + v0), zv, static_cast<const LT*>(nullptr));
-        unpack(stream_load(z + v0 + 4), zv + 4, static_cast<const LT*>(nullptr));
-      }
-      if (q != nullptr) {
-        unpack(stream_load(q + v0), qv, static_cast<const float*>(nullptr));
-        unpack(stream_load(q + v0 + 4), qv + 4, static_cast<const float*>(nullptr));
-      } else {
+    const bool in = cnt > 0, inq = in && q != nullptr;
+    const LT* zp = in ? z + v0 : static_cast<const LT*>(any);
+    const float* qp = inq ? q + v0 : static_cast<const float*>(any);
+    const uint4 z0 = stream_load(zp);
+    uint4 z1 = make_uint4(0, 0, 0, 0);
+    if constexpr (sizeof(LT) == 4) z1 = stream_load(zp + 4);
+    const uint4 q0 = stream_load(qp), q1 = stream_load(qp + 4);
+    unpack(z0, zv, static_cast<const LT*>(nullptr));
+    if constexpr (sizeof(LT) == 4) unpack(z1, zv + 4, static_cast<const LT*>(nullptr));
+    unpack(q0, qv, static_cast<const float*>(nullptr));
+    unpack(q1, qv + 4, static_cast<const float*>(nullptr));
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) qv[j] = 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) { zv[j] = -INFINITY; qv[j] = 0.f; }
+    for (int j = 0; j < kGroup; ++j) {
+      if (!in) zv[j] = -INFINITY;
+      if (!inq) qv[j] = 0.f;
     }
   } else {
 #pragma unroll
@@ -770,21 +816,31 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     if (tid == 0) sh_st = states[b];
     __syncthreads();
   } else {
-    const int kb = num_draft ? num_draft[b] : K;
-    const float T = greedy_all ? 0.f : temperature[b];
+    // The partials, the scan inputs, the draft count and the temperature all go out before
+    // any of them is used (absent operands are read from a stand-in and discarded).
+    const long long row0 = static_cast<long long>(b) * (K + 1);
+    PartialBatch batch0;
+    prefetch_partials(partials, row0, K, S * kWaves, wave, lane, batch0);
+    const void* any = partials;
+    const uint8_t* oh_ptr = kMatch ? nullptr : onehot;
+    const ScanLoads raw = load_scan_in(oh_ptr, uniforms, gathers, any, b, K, lane);
+    const int kb_ld = *(num_draft != nullptr ? num_draft + b : static_cast<const int32_t*>(any));
+    const float T_ld = *((greedy_all || temperature == nullptr) ? static_cast<const float*>(any)
+                                                                : temperature + b);
+    const int kb = num_draft != nullptr ? kb_ld : K;
+    const float T = greedy_all ? 0.f : T_ld;
     const bool use_match = kMatch && T != 0.f && kb >= 0 && kb <= K;
-    const float c = (kb >= 0 && kb <= K && temp_valid(T)) ? temp_scale(T) : kLog2e;
-    ScanIn in{};
-    if (wave == 0) in = load_scan_in(kMatch ? nullptr : onehot, uniforms, gathers, b, K, lane);
+    // temp_scale(T) for a valid sampled row, else log2(e) (= log2(e) / 1 exactly), written as
+    // one division without a branch so that nothing holds back the loads below.
+    const bool scaled = kb >= 0 && kb <= K && temp_valid(T) && T != 0.f;
+    const float c = kLog2e / (scaled ? T : 1.f);
     // Every wave merges some rows' partials (one round of loads for up to 16 rows), then wave 0
     // decides.
-    const long long row0 = static_cast<long long>(b) * (K + 1);
-    if (use_match)
-      row_stats_d(partials, row0, K, S * kWaves, c, wave, lane, sh_rows_d);
-    else
-      row_stats(partials, row0, K, S * kWaves, c, wave, lane, sh_rows);
+    row_stats<kMatch>(partials, row0, K, S * kWaves, c, use_match, wave, lane, batch0, sh_rows,
+                      sh_rows_d);
     __syncthreads();
     if (wave == 0) {
+      const ScanIn in = finish_scan_in(raw, oh_ptr, uniforms, K, lane);
       SeqState st;
       if (use_match)
         st = accept_sequence_match(in, b, kb, T, K, V, sh_rows_d, accept_len, out_tokens,
@@ -797,13 +853,25 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     __syncthreads();
   }
   const SeqState st = sh_st;
-  if (phase == 1) return;
-  // A bonus draw (plain p, also every match-mode draw) needs no second pass: its weights summed
-  // per 2048-token segment are the streaming kernel's partials, which the pick kernel rescales
-  // itself.  Residuals are summed here exactly (a one-hot residual taken from the partials would
-  // subtract e(x) from its segment's sum and cancel when x dominates the row).
-  if (st.mode == kNone || st.mode == kBonus) return;
+  if (phase == 1 || st.mode == kNone) return;
   const long long row = static_cast<long long>(b) * (K + 1) + st.row;
+  const int nseg = S * kSegPerChunk;
+  if (st.mode == kBonus) {
+    // A bonus draw (plain p, also every match-mode draw) needs no pass over the row: its weight
+    // sum over 2048-token segment j is the streaming kernel's partial j of that row rescaled to
+    // the row max, s_j * exp2((m_j - m) * c).  The sequence's workgroups write them in parallel
+    // (one segment per thread) for the pick kernel.  Residuals are summed below exactly (a
+    // one-hot residual taken from the partials would subtract e(x) from its segment's sum and
+    // cancel when x dominates the row).
+    const RowPartial* prow = partials + row * nseg;
+    for (int j = blockIdx.x * kThreads + tid; j < nseg; j += gridDim.x * kThreads) {
+      const RowPartial pj = prow[j];
+      const float f = pj.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((pj.m - st.m) * st.c);
+      const double e = static_cast<double>(pj.s) * static_cast<double>(f);
+      segs[static_cast<long long>(b) * nseg + j] = SegSums{e, e};
+    }
+    return;
+  }
   const LT* z = logits + row * V;
   const float* q = st.mode == kResidual
                        ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
@@ -849,7 +917,7 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
       for (int g = 0; g < kGroupsPerLane; ++g) {
         const int v0 = seg0 + (g * 64 + lane) * kGroup;
         float zv[kGroup], qv[kGroup], w[kGroup], gw, ge;
-        load_group<LT, false>(z, q, c0 + v0, min(kGroup, n - v0), zv, qv);
+        load_group<LT, false>(z, q, nullptr, c0 + v0, min(kGroup, n - v0), zv, qv);
         group_weights(zv, qv, c0 + v0, min(kGroup, n - v0), st, false, w, gw, ge);
         lw += gw;
         le += ge;
@@ -867,60 +935,38 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const float* __restrict__ uniforms, int B, int K, int V, int S,
     const SeqState* __restrict__ states, const SegSums* __restrict__ all_segs,
-    const RowPartial* __restrict__ partials, int32_t* __restrict__ out_tokens,
-    float* __restrict__ out_probs) {
+    int32_t* __restrict__ out_tokens, float* __restrict__ out_probs) {
   __shared__ int sh_seg, sh_plain, sh_hit[kWaves], sh_lastpos[kWaves];
   __shared__ float sh_zhit[kWaves], sh_zlast[kWaves];
   __shared__ double sh_t, sh_base, sh_wtot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nseg = S * kSegPerChunk;
+  // Lane l owns the contiguous segments [l * P, l * P + P).
+  const int P = (nseg + 63) / 64;
+  const int j0 = lane * P;
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
-    const int nseg = S * kSegPerChunk;
     const SegSums* segs = all_segs + static_cast<long long>(b) * nseg;
-    // Lane l owns the contiguous segments [l * P, l * P + P); its sums are loaded with the state.
-    const int P = (nseg + 63) / 64;
-    const int j0 = lane * P;
-    double lw = 0.0, le = 0.0;
-    if (wave == 0)
-      for (int q = 0; q < P; ++q)
-        if (j0 + q < nseg) {
-          const SegSums sq = segs[j0 + q];
-          lw += sq.w;
-          le += sq.e;
-        }
-    // The draw's uniform is column K unless the state says otherwise (match mode), so that
-    // column is fetched with the state rather than after it.
-    const float u_k = uniforms[static_cast<long long>(b) * (K + 1) + K];
+    // The state, the sequence's uniforms (lane i: column min(i, K)) and the lane's segment sums
+    // do not depend on each other: every load goes out before any value is used.
     const SeqState st = states[b];
+    const float u_lane = uniforms[static_cast<long long>(b) * (K + 1) + min(lane, K)];
+    double lw = 0.0, le = 0.0;
+    if (wave == 0) {
+      for (int q0 = 0; q0 < P; q0 += 4) {
+        SegSums sq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sq[q] = segs[min(j0 + q0 + q, nseg - 1)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q0 + q < P && j0 + q0 + q < nseg) {
+            lw += sq[q].w;
+            le += sq[q].e;
+          }
+      }
+    }
     if (st.mode == kNone) continue;
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
     const LT* z = logits + row * V;
-    // A bonus draw takes its segment sums from the row's partials: segment j's sum of
-    // exp2((z - m) * c) is s_j * exp2((m_j - m) * c).
-    const bool from_partials = st.mode == kBonus;
-    const RowPartial* prow = partials + row * nseg;
-    auto seg_sums = [&](int j, double& w, double& e) {
-      if (!from_partials) {
-        const SegSums sq = segs[j];
-        w = sq.w;
-        e = sq.e;
-        return;
-      }
-      const RowPartial pj = prow[j];
-      const float f = pj.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((pj.m - st.m) * st.c);
-      e = static_cast<double>(pj.s) * static_cast<double>(f);
-      w = e;
-    };
-    if (wave == 0 && from_partials) {
-      lw = 0.0;
-      le = 0.0;
-      for (int q = 0; q < P; ++q)
-        if (j0 + q < nseg) {
-          double w, e;
-          seg_sums(j0 + q, w, e);
-          lw += w;
-          le += e;
-        }
-    }
     // ---- The segment holding t = u * total: one fp64 scan of the lane totals. ----
     if (wave == 0) {
       const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
@@ -928,7 +974,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
       const double inc = plain ? ie : iw;
       const double own = plain ? le : lw;
       const double R = read_lane_d(inc, 63);
-      const float u = st.ucol == K ? u_k : uniforms[static_cast<long long>(b) * (K + 1) + st.ucol];
+      const float u = read_lane_f(u_lane, st.ucol);
       const double t = static_cast<double>(u) * R;
       // The first lane whose running total passes t holds the segment; if rounding left t at
       // the very top, the last lane with positive weight does.
@@ -941,9 +987,8 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
         int seg = -1, lastpos = -1;
         double base_seg = 0.0, base_last = 0.0;
         for (int q = 0; q < P && j0 + q < nseg; ++q) {
-          double sw, se;
-          seg_sums(j0 + q, sw, se);               // L1-resident: loaded above
-          const double v = plain ? se : sw;
+          const SegSums sq = segs[j0 + q];        // L1-resident: loaded above
+          const double v = plain ? sq.e : sq.w;
           if (v > 0.0) {
             if (run + v > t) { seg = j0 + q; base_seg = run; break; }
             lastpos = j0 + q;
@@ -968,7 +1013,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
                           ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
                           : nullptr;
     float zg[kGroup], qg[kGroup], w[kGroup], gw, ge;
-    load_group<LT, kVec>(z, qs, cc0 + v0, cnt, zg, qg);
+    load_group<LT, kVec>(z, qs, segs, cc0 + v0, cnt, zg, qg);
     group_weights(zg, qg, cc0 + v0, cnt, st, plain, w, gw, ge);
     const double inc = wave_inclusive_scan(static_cast<double>(gw));
     if (lane == 63) sh_wtot[wave] = inc;
@@ -1089,11 +1134,11 @@ hipError_t launch_typed(const LaunchArgs& a) {
   if (vec_draw)
     pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
-        a.ws.partials, a.out_tokens, a.out_probs);
+        a.out_tokens, a.out_probs);
   else
     pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
-        a.ws.partials, a.out_tokens, a.out_probs);
+        a.out_tokens, a.out_probs);
   return hipGetLastError();
 }
 
