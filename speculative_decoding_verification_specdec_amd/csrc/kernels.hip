@@ -346,15 +346,37 @@ __device__ __forceinline__ ScanIn finish_scan_in(const ScanLoads& r, const uint8
   return in;
 }
 
+// What an accept scan decides: the draw state (the same in every lane), the accept length and
+// lane i's output slot i (token and probability; -1 / 0 where the draw or nothing goes).
+struct ScanOut {
+  SeqState st;
+  int A;
+  int tok;
+  float prob;
+};
+
+// The scan's global writes, made after the workgroup barrier that publishes the state in LDS
+// (a barrier waits for every outstanding store of the workgroup).
+__device__ __forceinline__ void write_scan_out(const ScanOut& o, int b, int K,
+                                               int32_t* accept_len, int32_t* out_tokens,
+                                               float* out_probs, SeqState* states, int lane) {
+  const long long row0 = static_cast<long long>(b) * (K + 1);
+  if (lane <= K) {
+    out_tokens[row0 + lane] = o.tok;
+    if (out_probs) out_probs[row0 + lane] = o.prob;
+  }
+  if (lane == 0) {
+    accept_len[b] = o.A;
+    states[b] = o.st;
+  }
+}
+
 // Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count,
 // temperature and the row statistics in LDS (an invalid count or temperature poisons the
-// sequence).  Returns what remains to be drawn (the same value in every lane); with `write`,
-// also emits the known tokens, accept_len and the draw state.
-__device__ __forceinline__ SeqState accept_sequence(const ScanIn& in, bool have_q, int b,
-                                    int kb_raw, float T, int K, int V, const Stat* sh_rows,
-                                    int32_t* accept_len, int32_t* out_tokens, float* out_probs,
-                                    SeqState* states, bool write, int lane) {
-  const long long row0 = static_cast<long long>(b) * (K + 1);
+// sequence).  Returns what remains to be drawn and the tokens already known.
+__device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q, int kb_raw,
+                                                   float T, int K, int V, const Stat* sh_rows,
+                                                   int lane) {
   const Gather g = in.g;
   const float u = in.u, uk = in.uk;
   const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
@@ -404,26 +426,16 @@ __device__ __forceinline__ SeqState accept_sequence(const ScanIn& in, bool have_
     out = SeqState{mode, A, __shfl(x, A, 64), K, c, __shfl(st.m, A, 64), __shfl(st.s, A, 64),
                    0.f};
   }
-  if (write) {
-    if (lane <= K) {
-      int tok = -1;
-      float prob = 0.f;
-      if (ok && lane < A) {
-        tok = x;
-        prob = static_cast<float>(px);
-      } else if (ok && lane == A && greedy) {
-        tok = st.a;                                  // argmax: exp2(0) / s
-        prob = static_cast<float>(1.0 / static_cast<double>(st.s));
-      }
-      out_tokens[row0 + lane] = tok;                 // a sampled slot is filled by the draw
-      if (out_probs) out_probs[row0 + lane] = prob;
-    }
-    if (lane == 0) {
-      accept_len[b] = A;
-      states[b] = out;
-    }
+  int tok = -1;                                      // a sampled slot is filled by the draw
+  float prob = 0.f;
+  if (ok && lane < A) {
+    tok = x;
+    prob = static_cast<float>(px);
+  } else if (ok && lane == A && greedy) {
+    tok = st.a;                                      // argmax: exp2(0) / s
+    prob = static_cast<float>(1.0 / static_cast<double>(st.s));
   }
-  return out;
+  return ScanOut{out, A, tok, prob};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -573,11 +585,9 @@ __device__ __forceinline__ void row_stats(const RowPartial* __restrict__ partial
 // The match-mode scan of one sampled sequence with a valid draft count (greedy and
 // invalid-count sequences take the rejection-rule scan, which treats them identically).  Same
 // layout and outputs as accept_sequence.
-__device__ __forceinline__ SeqState accept_sequence_match(const ScanIn& in, int b, int kb, float T,
-                                    int K, int V, const StatD* sh_rows, int32_t* accept_len,
-                                    int32_t* out_tokens, float* out_probs, SeqState* states,
-                                    bool write, int lane) {
-  const long long row0 = static_cast<long long>(b) * (K + 1);
+__device__ __forceinline__ ScanOut accept_sequence_match(const ScanIn& in, int kb, float T,
+                                                         int K, int V, const StatD* sh_rows,
+                                                         int lane) {
   const Gather g = in.g;
   const float u = in.u, uk = in.uk;
   const bool seq_ok = temp_valid(T);  // T != 0 and k_b in range here
@@ -612,18 +622,8 @@ __device__ __forceinline__ SeqState accept_sequence_match(const ScanIn& in, int 
   if (ok)  // a plain draw of p_A with u[b, A] (mismatch) or u[b, K] (bonus)
     out = SeqState{kBonus, A, -1, A < kb ? A : K, c, __shfl(st.m, A, 64),
                    static_cast<float>(shfl_d(st.s, A)), 0.f};
-  if (write) {
-    if (lane <= K) {
-      const bool kept = ok && lane < A;
-      out_tokens[row0 + lane] = kept ? x : -1;     // slot A is filled by the draw
-      if (out_probs) out_probs[row0 + lane] = kept ? static_cast<float>(px) : 0.f;
-    }
-    if (lane == 0) {
-      accept_len[b] = A;
-      states[b] = out;
-    }
-  }
-  return out;
+  const bool kept = ok && lane < A;                  // slot A is filled by the draw
+  return ScanOut{out, A, kept ? x : -1, kept ? static_cast<float>(px) : 0.f};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -792,12 +792,12 @@ template <> struct DrawVec<float> {
 // wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns groups l,
 // l + 64, ...), in fp64.
 // ------------------------------------------------------------------------------------------
-template <typename LT, bool kVec, bool kMatch>
+template <typename LT, bool kVec, bool kMatch, int kPhase>
 __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
     const int32_t* __restrict__ num_draft, const float* __restrict__ temperature,
-    const float* __restrict__ uniforms, int b0, int K, int V, int S, int greedy_all, int phase,
+    const float* __restrict__ uniforms, int b0, int K, int V, int S, int greedy_all,
     const RowPartial* __restrict__ partials, const Gather* __restrict__ gathers,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs) {
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
   // be paid in every round.
   const int b = b0 + static_cast<int>(blockIdx.y);
   const bool first = blockIdx.x == 0;
-  if (phase == 2) {
+  if constexpr (kPhase == 2) {
     if (tid == 0) sh_st = states[b];
     __syncthreads();
   } else {
@@ -839,21 +839,22 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     row_stats<kMatch>(partials, row0, K, S * kWaves, c, use_match, wave, lane, batch0, sh_rows,
                       sh_rows_d);
     __syncthreads();
+    ScanOut so{};
     if (wave == 0) {
       const ScanIn in = finish_scan_in(raw, oh_ptr, uniforms, K, lane);
-      SeqState st;
       if (use_match)
-        st = accept_sequence_match(in, b, kb, T, K, V, sh_rows_d, accept_len, out_tokens,
-                                   out_probs, states, first, lane);
+        so = accept_sequence_match(in, kb, T, K, V, sh_rows_d, lane);
       else
-        st = accept_sequence(in, draft_probs != nullptr, b, kb, T, K, V, sh_rows, accept_len,
-                             out_tokens, out_probs, states, first, lane);
-      if (lane == 0) sh_st = st;
+        so = accept_sequence(in, draft_probs != nullptr, kb, T, K, V, sh_rows, lane);
+      if (lane == 0) sh_st = so.st;
     }
     __syncthreads();
+    // The chunk-0 workgroup emits the scan's outputs; the stores drain while the draw runs.
+    if (wave == 0 && first)
+      write_scan_out(so, b, K, accept_len, out_tokens, out_probs, states, lane);
   }
   const SeqState st = sh_st;
-  if (phase == 1 || st.mode == kNone) return;
+  if (kPhase == 1 || st.mode == kNone) return;
   const long long row = static_cast<long long>(b) * (K + 1) + st.row;
   const int nseg = S * kSegPerChunk;
   if (st.mode == kBonus) {
@@ -1074,6 +1075,14 @@ inline unsigned grid_for(long long work) {
   return static_cast<unsigned>(work < 1 ? 1 : (work < kMaxGrid ? work : kMaxGrid));
 }
 
+template <typename LT, int kPhase>
+auto accept_draw_for(bool match, bool vec) -> decltype(&accept_draw_kernel<LT, true, true, kPhase>) {
+  return match ? (vec ? accept_draw_kernel<LT, true, true, kPhase>
+                      : accept_draw_kernel<LT, false, true, kPhase>)
+               : (vec ? accept_draw_kernel<LT, true, false, kPhase>
+                      : accept_draw_kernel<LT, false, false, kPhase>);
+}
+
 template <typename LT>
 hipError_t launch_typed(const LaunchArgs& a) {
   const LT* logits = static_cast<const LT*>(a.logits);
@@ -1104,11 +1113,13 @@ hipError_t launch_typed(const LaunchArgs& a) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // Accept scan + draw sums: one workgroup per (chunk, sequence); greedy-only calls need just
-  // the chunk-0 workgroups (no draw).
-  auto accept_draw = match ? (vec_draw ? accept_draw_kernel<LT, true, true>
-                                        : accept_draw_kernel<LT, false, true>)
-                           : (vec_draw ? accept_draw_kernel<LT, true, false>
-                                       : accept_draw_kernel<LT, false, false>);
+  // the chunk-0 workgroups (no draw).  Each phase is its own kernel, so the draw-only pass does
+  // not carry the scan's registers (its occupancy sets the draw's bandwidth).
+  auto accept_draw = [&](int phase) {
+    return phase == 0   ? accept_draw_for<LT, 0>(match, vec_draw)
+           : phase == 1 ? accept_draw_for<LT, 1>(match, vec_draw)
+                        : accept_draw_for<LT, 2>(match, vec_draw);
+  };
   // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
   // partials): the chunk-0 workgroups that run the scan are enough.
   // Otherwise one workgroup per chunk of the row to draw from.
@@ -1123,9 +1134,9 @@ hipError_t launch_typed(const LaunchArgs& a) {
     const int gx = (phase == 1 || !draws) ? 1 : S;
     for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
       const dim3 grid(gx, min(kMaxZ, a.B - b0));
-      accept_draw<<<grid, kThreads, 0, a.stream>>>(
+      accept_draw(phase)<<<grid, kThreads, 0, a.stream>>>(
           logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms,
-          b0, a.K, a.V, S, a.greedy_all, phase, a.ws.partials, a.ws.gathers, a.accept_len,
+          b0, a.K, a.V, S, a.greedy_all, a.ws.partials, a.ws.gathers, a.accept_len,
           a.out_tokens, a.out_probs, a.ws.states, a.ws.segs);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
