@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ lengths, int capacity,
     int n_min, int n_max, int K, int ntiles, unsigned long long* __restrict__ partials,
     int32_t* __restrict__ proposed, int32_t* __restrict__ num_draft) {
-  __shared__ int sh_tok[kNgHalo + kNgramTile];  // sh_tok[i] = h[t0 - kNgHalo + i]
+  __shared__ __align__(16) int sh_tok[kNgHalo + kNgramTile];  // sh_tok[i] = h[t0 - kNgHalo + i]
   __shared__ int sh_suf[kNgramMaxN + 1];        // sh_suf[j] = h[L - j]
   __shared__ unsigned long long sh_best[kNgThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -74,23 +74,35 @@ __global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
   const int32_t* h = tokens + static_cast<long long>(b) * capacity;
   unsigned long long key = 0ull;
   if (active) {
-    if (tid >= 1 && tid <= nmax) sh_suf[tid] = h[L - tid];
     // Stage h[t0 - kNgHalo, t0 + kNgramTile) where it lies in [0, L); other slots are never
     // compared (every compared index e - j lies in [0, L - 2]).
     const int i0 = t0 - kNgHalo;
     if constexpr (kVec) {
+      // All of the thread's 16-byte loads go out before any is stored: an out-of-range slot
+      // reads h[0..3] (in the row: L >= 1 here) and is zeroed afterwards.
       constexpr int kVecs = (kNgHalo + kNgramTile) / 4;
+      constexpr int kIters = (kVecs + kNgThreads - 1) / kNgThreads;
       const int4* hv = reinterpret_cast<const int4*>(h);
-      for (int v = tid; v < kVecs; v += kNgThreads) {
+      int4 d[kIters];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int v = tid + it * kNgThreads;
         const int idx = i0 + 4 * v;  // a multiple of 4; idx < L <= capacity keeps idx + 3 in the row
-        int4 d = make_int4(0, 0, 0, 0);
-        if (idx >= 0 && idx < L) d = hv[idx / 4];
-        sh_tok[4 * v] = d.x;
-        sh_tok[4 * v + 1] = d.y;
-        sh_tok[4 * v + 2] = d.z;
-        sh_tok[4 * v + 3] = d.w;
+        const bool ok = v < kVecs && idx >= 0 && idx < L;
+        d[it] = hv[ok ? idx / 4 : 0];
+      }
+      const int suf = h[L - min(max(tid, 1), nmax)];  // sh_suf[tid] for tid in [1, nmax]
+      if (tid >= 1 && tid <= nmax) sh_suf[tid] = suf;
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int v = tid + it * kNgThreads;
+        const int idx = i0 + 4 * v;
+        if (v < kVecs)
+          reinterpret_cast<int4*>(sh_tok)[v] =
+              (idx >= 0 && idx < L) ? d[it] : make_int4(0, 0, 0, 0);
       }
     } else {
+      if (tid >= 1 && tid <= nmax) sh_suf[tid] = h[L - tid];
       for (int i = tid; i < kNgHalo + kNgramTile; i += kNgThreads) {
         const int idx = i0 + i;
         sh_tok[i] = (idx >= 0 && idx < L) ? h[idx] : 0;
