@@ -25,6 +25,7 @@ namespace {
 constexpr int kCmThreads = 1024;
 constexpr int kCmWaves = kCmThreads / 64;
 constexpr int kCmLds = 4096;  // batches up to this size stage per-sequence data in LDS
+constexpr int kCmBatch = 8;   // emitted-token slots per thread whose loads go out together
 
 // Tokens sequence b commits: A + 1, or 0 for an invalid row / length / overflow.
 __device__ __forceinline__ int emitted_count(int A, int L, int K, int capacity) {
@@ -44,6 +45,20 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
   const int per = (B + kCmThreads - 1) / kCmThreads;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
   const bool staged = B <= kCmLds;  // per-sequence data fits LDS: coalesced copies below
+  const int items = B * (K + 1);
+  // Loads that do not depend on the scan go out first: the first batch of emitted-token slots
+  // (flattened index tid + j * kCmThreads, clamped into range) and the first cache lengths.
+  int32_t tok0[kCmBatch];
+  int tkv0 = 0, dkv0 = 0;
+  if (staged) {
+#pragma unroll
+    for (int j = 0; j < kCmBatch; ++j)
+      tok0[j] = items > 0 ? out_tokens[min(tid + j * kCmThreads, items - 1)] : 0;
+    if (tid < B) {
+      if (target_kv) tkv0 = target_kv[tid];
+      if (draft_kv) dkv0 = draft_kv[tid];
+    }
+  }
   int local = 0;
   for (int b = b0; b < b1; ++b) {
     const int A = accept_len[b], L = seq_len[b];
@@ -76,22 +91,40 @@ __global__ __launch_bounds__(kCmThreads) void commit_kernel(
     // Token copies over the flattened (sequence, slot) space: consecutive threads take
     // consecutive slots of a row, so the reads of out_tokens and the writes of the history and
     // of the packed stream coalesce.
-    const int items = B * (K + 1);
-    for (int g = tid; g < items; g += kCmThreads) {
-      const int b = g / (K + 1), i = g - b * (K + 1);
-      if (i < sh_em[b]) {
-        const int32_t t = out_tokens[g];
-        if (tokens) tokens[static_cast<long long>(b) * capacity + sh_len[b] + i] = t;
-        if (packed) packed[sh_base[b] + i] = t;
+    // Batches of kCmBatch slots per thread, every load of a batch issued before its stores.
+    for (int g0 = 0; g0 < items; g0 += kCmBatch * kCmThreads) {
+      int32_t tv[kCmBatch];
+      if (g0 == 0) {
+#pragma unroll
+        for (int j = 0; j < kCmBatch; ++j) tv[j] = tok0[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kCmBatch; ++j)
+          tv[j] = out_tokens[min(g0 + tid + j * kCmThreads, items - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kCmBatch; ++j) {
+        const int g = g0 + tid + j * kCmThreads;
+        if (g >= items) break;
+        const int b = g / (K + 1), i = g - b * (K + 1);
+        if (i < sh_em[b]) {
+          if (tokens) tokens[static_cast<long long>(b) * capacity + sh_len[b] + i] = tv[j];
+          if (packed) packed[sh_base[b] + i] = tv[j];
+        }
       }
     }
     for (int b = tid; b < B; b += kCmThreads) {
       const int em = sh_em[b];
+      int tkv = tkv0, dkv = dkv0;
+      if (b != tid) {
+        if (target_kv) tkv = target_kv[b];
+        if (draft_kv) dkv = draft_kv[b];
+      }
       if (em > 0) {
         const int L = sh_len[b];
         seq_len[b] = L + em;
-        if (target_kv) target_kv[b] = min(target_kv[b], L + em - 1);
-        if (draft_kv) draft_kv[b] = min(draft_kv[b], L + em - 1);
+        if (target_kv) target_kv[b] = min(tkv, L + em - 1);
+        if (draft_kv) draft_kv[b] = min(dkv, L + em - 1);
       }
     }
     return;

@@ -35,16 +35,28 @@ __global__ __launch_bounds__(kTmThreads) void telemetry_kernel(
   const int n = n_routes * kTelemetryRow;
   for (int i = tid; i < n; i += kTmThreads) sh[i] = 0ull;
   __syncthreads();
+  // The caller's counters are read now (after the barrier, which would wait for them), while
+  // the batch is counted.
+  constexpr int kPre = 5;
+  static_assert(kTelemetryMaxRoutes * kTelemetryRow <= kPre * kTmThreads, "counter prefetch");
+  long long cpre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) cpre[j] = counters[min(tid + j * kTmThreads, n - 1)];
   for (int b0 = 0; b0 < B; b0 += kTmThreads) {
     const int b = b0 + tid;
+    // The three per-sequence loads go out together (index clamped into the batch).
+    const int bc = min(b, B - 1);
+    const int r_ld = route ? route[bc] : 0;
+    const int A_ld = accept_len[bc];
+    const int k_ld = num_draft ? num_draft[bc] : K;
     int r = -1, A = 0, k = 0;
     bool counted = false, valid = false;
     if (b < B) {
-      r = route ? route[b] : 0;
+      r = r_ld;
       if (r >= 0 && r < n_routes) {
         counted = true;
-        A = accept_len[b];
-        k = num_draft ? num_draft[b] : K;
+        A = A_ld;
+        k = k_ld;
         valid = A >= 0 && k >= 0 && k <= K && A <= k;
       }
     }
@@ -71,7 +83,11 @@ __global__ __launch_bounds__(kTmThreads) void telemetry_kernel(
     if (valid) atomicAdd(&sh[r * kTelemetryRow + kTelemetryFields + A], 1ull);
   }
   __syncthreads();
-  for (int i = tid; i < n; i += kTmThreads) counters[i] += static_cast<long long>(sh[i]);
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int i = tid + j * kTmThreads;
+    if (i < n) counters[i] = cpre[j] + static_cast<long long>(sh[i]);
+  }
 }
 
 __global__ __launch_bounds__(256) void apply_k_kernel(int32_t* __restrict__ num_draft,
@@ -80,10 +96,10 @@ __global__ __launch_bounds__(256) void apply_k_kernel(int32_t* __restrict__ num_
                                                       int B, int n_routes) {
   const int b = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
   if (b >= B) return;
+  // The route and the draft count are read together; the table read waits only for the route.
   const int r = route ? route[b] : 0;
-  if (r < 0 || r >= n_routes) return;
   const int nd = num_draft[b];
-  if (nd < 0) return;
+  if (r < 0 || r >= n_routes || nd < 0) return;
   num_draft[b] = min(nd, max(0, k_table[r]));
 }
 
