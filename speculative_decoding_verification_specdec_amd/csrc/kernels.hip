@@ -347,12 +347,14 @@ __device__ __forceinline__ ScanIn finish_scan_in(const ScanLoads& r, const uint8
 }
 
 // What an accept scan decides: the draw state (the same in every lane), the accept length and
-// lane i's output slot i (token and probability; -1 / 0 where the draw or nothing goes).
+// lane i's output slot i: its token (-1 where the draw or nothing goes) and its probability as
+// num / den, divided only when the outputs are written (after the state is published).
 struct ScanOut {
   SeqState st;
   int A;
   int tok;
-  float prob;
+  double num;
+  double den;
 };
 
 // The scan's global writes, made after the workgroup barrier that publishes the state in LDS
@@ -363,7 +365,7 @@ __device__ __forceinline__ void write_scan_out(const ScanOut& o, int b, int K,
   const long long row0 = static_cast<long long>(b) * (K + 1);
   if (lane <= K) {
     out_tokens[row0 + lane] = o.tok;
-    if (out_probs) out_probs[row0 + lane] = o.prob;
+    if (out_probs) out_probs[row0 + lane] = static_cast<float>(o.num / o.den);
   }
   if (lane == 0) {
     accept_len[b] = o.A;
@@ -372,25 +374,26 @@ __device__ __forceinline__ void write_scan_out(const ScanOut& o, int b, int K,
 }
 
 // Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count,
-// temperature and the row statistics in LDS (an invalid count or temperature poisons the
-// sequence).  Returns what remains to be drawn and the tokens already known.
+// temperature, exp2 scale c (temp_scale(T) for a valid sequence, else log2(e)) and the row
+// statistics in LDS (an invalid count or temperature poisons the sequence).  Returns what
+// remains to be drawn and the tokens already known.  The test u * q(x) < p(x) = e / s is taken
+// as u * q(x) * s < e in fp64, so no division stands before the decision.
 __device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q, int kb_raw,
-                                                   float T, int K, int V, const Stat* sh_rows,
-                                                   int lane) {
+                                                   float T, float c, int K, int V,
+                                                   const Stat* sh_rows, int lane) {
   const Gather g = in.g;
   const float u = in.u, uk = in.uk;
   const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
   const int kb = seq_ok ? kb_raw : 0;
   const bool greedy = (T == 0.f);
   const bool is_onehot = !greedy && in.onehot;
-  const float c = seq_ok ? temp_scale(T) : kLog2e;
   const Stat st = lane <= K ? sh_rows[lane] : Stat{-INFINITY, 0.f, INT_MAX};
 
   const bool drafted = lane < kb;
   const int x = g.x;
   const bool x_ok = x >= 0 && x < V;
   bool lane_ok = true;
-  double px = 0.0;
+  double ex = 0.0;  // exp2((z_i[x_i] - m_i) * c) = s_i * p_i(x_i)
   bool acc = true;
   if (lane <= kb) {
     lane_ok = st.s > 0.f;  // NaN / +inf logit -> NaN; all -inf -> 0
@@ -398,8 +401,8 @@ __device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q
       if (!x_ok) {
         lane_ok = false;
       } else {
-        px = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
-                  static_cast<double>(c)) / static_cast<double>(st.s);
+        ex = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
+                  static_cast<double>(c));
         if (greedy) {
           acc = (x == st.a);
         } else {
@@ -410,7 +413,7 @@ __device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q
             else if (!(g.q >= 0.f && g.q <= FLT_MAX)) lane_ok = false;
             qx = g.q;
           }
-          acc = static_cast<double>(u) * qx < px;
+          acc = static_cast<double>(u) * qx * static_cast<double>(st.s) < ex;
         }
       }
     }
@@ -426,16 +429,17 @@ __device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q
     out = SeqState{mode, A, __shfl(x, A, 64), K, c, __shfl(st.m, A, 64), __shfl(st.s, A, 64),
                    0.f};
   }
-  int tok = -1;                                      // a sampled slot is filled by the draw
-  float prob = 0.f;
+  ScanOut o{out, A, -1, 0.0, 1.0};                  // a sampled slot is filled by the draw
   if (ok && lane < A) {
-    tok = x;
-    prob = static_cast<float>(px);
+    o.tok = x;
+    o.num = ex;
+    o.den = static_cast<double>(st.s);
   } else if (ok && lane == A && greedy) {
-    tok = st.a;                                      // argmax: exp2(0) / s
-    prob = static_cast<float>(1.0 / static_cast<double>(st.s));
+    o.tok = st.a;                                    // argmax: exp2(0) / s
+    o.num = 1.0;
+    o.den = static_cast<double>(st.s);
   }
-  return ScanOut{out, A, tok, prob};
+  return o;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -586,18 +590,17 @@ __device__ __forceinline__ void row_stats(const RowPartial* __restrict__ partial
 // invalid-count sequences take the rejection-rule scan, which treats them identically).  Same
 // layout and outputs as accept_sequence.
 __device__ __forceinline__ ScanOut accept_sequence_match(const ScanIn& in, int kb, float T,
-                                                         int K, int V, const StatD* sh_rows,
-                                                         int lane) {
+                                                         float c, int K, int V,
+                                                         const StatD* sh_rows, int lane) {
   const Gather g = in.g;
   const float u = in.u, uk = in.uk;
   const bool seq_ok = temp_valid(T);  // T != 0 and k_b in range here
-  const float c = seq_ok ? temp_scale(T) : kLog2e;
   const StatD st = lane <= K ? sh_rows[lane] : StatD{-INFINITY, 0.0, 0.0};
 
   const bool drafted = lane < kb;
   const int x = g.x;
   bool lane_ok = true, keep = true;
-  double px = 0.0;
+  double ex = 0.0;
   if (lane <= kb) {
     lane_ok = st.s > 0.0;  // NaN / +inf logit -> NaN; all -inf -> 0
     if (drafted) {
@@ -605,11 +608,10 @@ __device__ __forceinline__ ScanOut accept_sequence_match(const ScanIn& in, int k
         lane_ok = false;
       } else {
         // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
-        const double ex = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
-                               static_cast<double>(c));
+        ex = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
+                  static_cast<double>(c));
         const double t = static_cast<double>(u) * st.s;
         keep = st.p <= t && t < st.p + ex;
-        px = ex / st.s;
       }
     }
   }
@@ -623,7 +625,7 @@ __device__ __forceinline__ ScanOut accept_sequence_match(const ScanIn& in, int k
     out = SeqState{kBonus, A, -1, A < kb ? A : K, c, __shfl(st.m, A, 64),
                    static_cast<float>(shfl_d(st.s, A)), 0.f};
   const bool kept = ok && lane < A;                  // slot A is filled by the draw
-  return ScanOut{out, A, kept ? x : -1, kept ? static_cast<float>(px) : 0.f};
+  return ScanOut{out, A, kept ? x : -1, kept ? ex : 0.0, kept ? st.s : 1.0};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -843,9 +845,9 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     if (wave == 0) {
       const ScanIn in = finish_scan_in(raw, oh_ptr, uniforms, K, lane);
       if (use_match)
-        so = accept_sequence_match(in, kb, T, K, V, sh_rows_d, lane);
+        so = accept_sequence_match(in, kb, T, c, K, V, sh_rows_d, lane);
       else
-        so = accept_sequence(in, draft_probs != nullptr, kb, T, K, V, sh_rows, lane);
+        so = accept_sequence(in, draft_probs != nullptr, kb, T, c, K, V, sh_rows, lane);
       if (lane == 0) sh_st = so.st;
     }
     __syncthreads();
