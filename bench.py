@@ -37,8 +37,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_verification_specdec_am
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code: comments and blank lines stripped, so a comment
+    edit does not invalidate a counter summary taken on the same code."""
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(line.strip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(bytes_alg_per_launch: float):

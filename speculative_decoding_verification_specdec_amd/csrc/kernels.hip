@@ -789,10 +789,11 @@ template <> struct DrawVec<float> {
 
 // ------------------------------------------------------------------------------------------
 // Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
-// by b0).  Wave 0 of every workgroup runs its sequence's accept scan (the partials it reads are
-// L2-resident); the chunk-0 workgroup also writes the scan's outputs and the draw state.  Then
-// wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns groups l,
-// l + 64, ...), in fp64.
+// by b0).  kPhase 0: every workgroup runs its sequence's accept scan (all waves merge partials,
+// wave 0 decides) and the chunk-0 workgroup writes the scan's outputs and the draw state; then
+// wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns 4-token quads
+// l, l + 64, ...), in fp64.  kPhase 1: the scan only (one workgroup per sequence).  kPhase 2:
+// the draw only, from the state kPhase 1 wrote.
 // ------------------------------------------------------------------------------------------
 template <typename LT, bool kVec, bool kMatch, int kPhase>
 __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
