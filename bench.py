@@ -142,8 +142,14 @@ def cpu_baseline(inp, budget_s: float = 6.0, parallel_s: float = 1.5):
         el_p = time.perf_counter() - t0
     _CPU_INP = None
     assert done == inp.B * reps
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=positions * reps / el_p, unit="positions/s", cores=len(shards),
-                kind="oracle",
+                kind="oracle", cpu_model=model,
                 sample=f"{reps} passes over the B=64 V=128256 k=5 batch, its sequences split "
                        f"across {len(shards)} forked worker processes (one per host core, "
                        f"numpy fp64; {el_p:.1f} s)",
@@ -261,24 +267,28 @@ def bench_commit(dev, stream, steps=400):
             "sequences_per_s": B / (us * 1e-6)}
 
 
-def bench_workload(dev, stream, inp, description, steps=60):
-    """Whole verify steps on another workload (one replica: a single step's logits already exceed
-    twice the Infinity Cache): verified positions/s and algorithmic GB/s."""
+def bench_workload(dev, stream, inp, description, steps=60, replicas=1):
+    """Whole verify steps on another workload: verified positions/s and algorithmic GB/s.  One
+    replica when a single step's logits already exceed twice the Infinity Cache, else
+    ``replicas`` copies rotated step to step."""
     import torch
     from speculative_decoding_verification_specdec_amd import (inputs_to_device,
                                                                specdec_workspace_size)
     from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
     B, K, V = inp.B, inp.K, inp.V
     ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
-    d = inputs_to_device(inp, dev)
-    call = PreparedVerify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
-                          d["uniforms"], draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
-                          workspace=ws)
-    us = time_replayed([call], steps, stream)
-    acc = call.out[0].cpu().numpy()
+    calls = []
+    for _ in range(replicas):
+        d = inputs_to_device(inp, dev)
+        calls.append(PreparedVerify(d["logits"], d["draft_probs"], d["proposed"],
+                                    d["temperature"], d["uniforms"],
+                                    draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
+                                    workspace=ws, out=calls[0].out if calls else None))
+    us = time_replayed(calls, steps, stream)
+    acc = calls[0].out[0].cpu().numpy()
     _, nbytes = algorithmic_bytes(inp, acc)
     positions = int(inp.draft_counts().sum())
-    del d, call, ws
+    del d, calls, ws
     torch.cuda.empty_cache()
     return {"workload": description, "us_per_call": us,
             "verified_positions_per_s": positions / (us * 1e-6),
@@ -527,6 +537,11 @@ def main():
         res["other_workloads"]["ragged_mixed"] = bench_workload(
             dev, stream, ragged_mixed(),
             "B=512, k_b ~ U{1..8} padded to 8, V=128256, bf16; half n-gram (one-hot) rows")
+        print("[bench] batch, calibrated drafter", file=sys.stderr, flush=True)
+        res["other_workloads"]["batch64_calibrated"] = bench_workload(
+            dev, stream, batch64(calibrated=True),
+            "batch64 with draft noise 0.5 and q softmaxed at the row's temperature (acceptance "
+            "0.6-0.8); 6 replicas rotated", steps=300, replicas=6)
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
