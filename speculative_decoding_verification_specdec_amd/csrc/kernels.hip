@@ -426,8 +426,8 @@ __device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q
   SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
   if (ok && !greedy) {  // A is wave-uniform: lane A's row is the one to draw from
     const int mode = (A == kb) ? kBonus : (is_onehot ? kResidualOnehot : kResidual);
-    out = SeqState{mode, A, __shfl(x, A, 64), K, c, __shfl(st.m, A, 64), __shfl(st.s, A, 64),
-                   0.f};
+    out = SeqState{mode, A, __builtin_amdgcn_readlane(x, A), K, c, read_lane_f(st.m, A),
+                   read_lane_f(st.s, A), 0.f};
   }
   ScanOut o{out, A, -1, 0.0, 1.0};                  // a sampled slot is filled by the draw
   if (ok && lane < A) {
@@ -496,14 +496,6 @@ __device__ __forceinline__ StatD row16_reduce_d(const StatD& v, float c) {
   sum += dpp_move_d<0x128, 0xf>(sum);
   pre += dpp_move_d<0x128, 0xf>(pre);
   return StatD{M, sum, pre};
-}
-
-__device__ __forceinline__ double shfl_d(double v, int src) {
-  const long long bits = __double_as_longlong(v);
-  const int lo = __shfl(static_cast<int>(bits), src, 64);
-  const int hi = __shfl(static_cast<int>(bits >> 32), src, 64);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
 }
 
 // Row statistics of rows 0..K of one sequence, by every wave of the workgroup: 16 lanes per
@@ -622,8 +614,8 @@ __device__ __forceinline__ ScanOut accept_sequence_match(const ScanIn& in, int k
 
   SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
   if (ok)  // a plain draw of p_A with u[b, A] (mismatch) or u[b, K] (bonus)
-    out = SeqState{kBonus, A, -1, A < kb ? A : K, c, __shfl(st.m, A, 64),
-                   static_cast<float>(shfl_d(st.s, A)), 0.f};
+    out = SeqState{kBonus, A, -1, A < kb ? A : K, c, read_lane_f(st.m, A),
+                   static_cast<float>(read_lane_d(st.s, A)), 0.f};
   const bool kept = ok && lane < A;                  // slot A is filled by the draw
   return ScanOut{out, A, kept ? x : -1, kept ? ex : 0.0, kept ? st.s : 1.0};
 }
@@ -1040,10 +1032,11 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     const unsigned long long pm = __ballot(lastpos >= 0);
     const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 0;
     const int ll = pm ? 63 - __clzll(static_cast<long long>(pm)) : 0;
-    const int wave_hit = hm ? __shfl(hit, hl, 64) : -1;
-    const float wave_zhit = __shfl(zhit, hl, 64);
-    const int wave_last = pm ? __shfl(lastpos, ll, 64) : -1;
-    const float wave_zlast = __shfl(zlast, ll, 64);
+    // hl and ll are wave-uniform: readlane, not a cross-lane shuffle through LDS.
+    const int wave_hit = hm ? __builtin_amdgcn_readlane(hit, hl) : -1;
+    const float wave_zhit = read_lane_f(zhit, hl);
+    const int wave_last = pm ? __builtin_amdgcn_readlane(lastpos, ll) : -1;
+    const float wave_zlast = read_lane_f(zlast, ll);
     if (lane == 0) {
       sh_hit[wave] = wave_hit; sh_zhit[wave] = wave_zhit;
       sh_lastpos[wave] = wave_last; sh_zlast[wave] = wave_zlast;
