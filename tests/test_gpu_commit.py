@@ -31,8 +31,9 @@ def random_round(B, K, cap, seed):
     return acc, out, seq, hist, tkv, dkv
 
 
-@pytest.mark.parametrize("B,K,cap", [(1, 1, 8), (7, 5, 40), (512, 8, 256), (1024, 3, 64),
-                                     (3000, 8, 128), (4096, 63, 80), (5000, 4, 64)])
+# (512, 8, 8192) is the benchmark's commit shape.
+@pytest.mark.parametrize("B,K,cap", [(1, 1, 8), (7, 5, 40), (512, 8, 256), (512, 8, 8192),
+                                     (1024, 3, 64), (3000, 8, 128), (4096, 63, 80), (5000, 4, 64)])
 def test_commit_matches_oracle(B, K, cap):
     print(f"\n[case] commit B={B} K={K} cap={cap}", flush=True)
     acc, out, seq, hist, tkv, dkv = random_round(B, K, cap, seed=B + K)

@@ -111,6 +111,15 @@ def test_full_workload_sampled():
         assert (prop[b, k:] == -1).all()
 
 
+def test_long_workload_sampled():
+    # 256 histories of 32768-65536 tokens, capacity 65536: eight tiles per history, so the
+    # multi-tile path (per-tile keys, then the emit kernel) in the benchmark's launch shape.
+    h = hist.ngram_long_workload()
+    rows = np.random.default_rng(13).choice(h.B, size=32, replace=False)
+    prop, nd = check(h, 8, 1, 4, rows=rows)
+    assert ((nd >= 0) & (nd <= 8)).all()
+
+
 def test_drafts_feed_the_verify_step():
     # The drafter's proposals, verified as one-hot rows, match the verify oracle.
     B, K, V = 16, 6, 3000
