@@ -528,7 +528,9 @@ def main():
         res["next_rows"]["telemetry"] = bench_telemetry(dev, stream)
     if not args.no_other_workloads:
         from speculative_decoding_verification_specdec_amd.inputs import (large_batch_deep,
-                                                                           ragged_mixed)
+                                                                           ragged_mixed,
+                                                                           single_sequence,
+                                                                           tiny_vocab)
         print("[bench] large batch, deep draft", file=sys.stderr, flush=True)
         res["other_workloads"] = {"large_batch_deep": bench_workload(
             dev, stream, large_batch_deep(),
@@ -537,6 +539,19 @@ def main():
         res["other_workloads"]["ragged_mixed"] = bench_workload(
             dev, stream, ragged_mixed(),
             "B=512, k_b ~ U{1..8} padded to 8, V=128256, bf16; half n-gram (one-hot) rows")
+        print("[bench] single-sequence latency", file=sys.stderr, flush=True)
+        res["latency"] = {
+            "single_sequence": bench_workload(
+                dev, stream, single_sequence(),
+                "B=1, k=4, V=32000, fp32 logits ~N(0,3^2), T=0.7: one call's latency", steps=400),
+            "tiny_vocab_one_round": bench_workload(
+                dev, stream, tiny_vocab(rounds=1),
+                "B=1, k=4, V=32, fp32: one round's latency", steps=400)}
+        print("[bench] tiny vocabulary, 1e5 rounds in one call", file=sys.stderr, flush=True)
+        res["other_workloads"]["tiny_vocab"] = bench_workload(
+            dev, stream, tiny_vocab(),
+            "B=100000 rounds of one sequence, k=4, V=32, fp32 logits ~N(0,2^2), q = softmax of "
+            "logits + N(0,1), T=1: one call (one wave per sequence)", steps=100)
         print("[bench] batch, calibrated drafter", file=sys.stderr, flush=True)
         res["other_workloads"]["batch64_calibrated"] = bench_workload(
             dev, stream, batch64(calibrated=True),

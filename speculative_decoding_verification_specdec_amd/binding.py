@@ -25,7 +25,19 @@ class SpecdecError(RuntimeError):
 
 
 class _Options(ctypes.Structure):
-    _fields_ = [("hot_event_begin", ctypes.c_void_p), ("hot_event_end", ctypes.c_void_p)]
+    _fields_ = [("hot_event_begin", ctypes.c_void_p), ("hot_event_end", ctypes.c_void_p),
+                ("path", ctypes.c_int32)]
+
+
+# Execution paths of specdec_verify (include/specdec.h).
+SPECDEC_SMALL_V_MAX = 1024
+SPECDEC_PATH_AUTO, SPECDEC_PATH_STREAMING, SPECDEC_PATH_SMALL_VOCAB = 0, 1, 2
+
+
+def _options(hot_events, path):
+    ev = (None, None) if hot_events is None else tuple(
+        e if isinstance(e, int) or e is None else e.cuda_event for e in hot_events)
+    return _Options(ev[0], ev[1], int(path))
 
 
 def library_path() -> pathlib.Path:
@@ -144,14 +156,16 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
                    proposed: torch.Tensor | None, temperature: torch.Tensor,
                    uniforms: torch.Tensor, *, draft_onehot: torch.Tensor | None = None,
                    num_draft: torch.Tensor | None = None, out=None, workspace=None,
-                   want_probs: bool = True, stream=None, hot_events=None):
+                   want_probs: bool = True, stream=None, hot_events=None,
+                   path: int = SPECDEC_PATH_AUTO):
     """Batched verify.  Shapes: target_logits [B, K+1, V] (bf16 or fp32), draft_probs
     [B, K, V] fp32 or None, proposed [B, K] int32, temperature [B] fp32, uniforms [B, K+1]
     fp32, draft_onehot [B] uint8 or None, num_draft [B] int32 or None.  Returns
     (accept_len [B] int32, out_tokens [B, K+1] int32, out_probs [B, K+1] fp32 or None),
     enqueued on ``stream`` (default: torch's current stream) without synchronising.
     ``hot_events``: optional (begin, end) pair of hipEvent_t handles (ints) recorded around the
-    streaming logit-row kernel."""
+    kernel that reads every target row.  ``path``: SPECDEC_PATH_AUTO (one wave per sequence when
+    V <= SPECDEC_SMALL_V_MAX, else the streaming kernels), _STREAMING or _SMALL_VOCAB."""
     lib = load_library()
     if target_logits.dim() != 3:
         raise SpecdecError("target_logits must be [B, K+1, V]")
@@ -177,11 +191,10 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     args = (_ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_onehot), _ptr(proposed),
             _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc), _ptr(tok),
             _ptr(prb), _ptr(ws), ws.numel(), _stream_handle(stream))
-    if hot_events is None:
+    if hot_events is None and path == SPECDEC_PATH_AUTO:
         status = lib.specdec_verify(*args)
     else:
-        opts = _Options(*(e if isinstance(e, int) or e is None else e.cuda_event
-                          for e in hot_events))
+        opts = _options(hot_events, path)
         status = lib.specdec_verify_ex(*args, ctypes.byref(opts))
     _raise(status, "specdec_verify")
     return acc, tok, prb
@@ -406,7 +419,8 @@ class PreparedVerify:
     torch's current stream) and raises on a non-zero status."""
 
     def __init__(self, target_logits, draft_probs, proposed, temperature, uniforms, *,
-                 draft_onehot=None, num_draft=None, out=None, workspace=None):
+                 draft_onehot=None, num_draft=None, out=None, workspace=None,
+                 path=SPECDEC_PATH_AUTO):
         # Validate once through the checked entry point's rules.
         B, K1, V = (int(s) for s in target_logits.shape)
         dev = target_logits.device
@@ -423,17 +437,17 @@ class PreparedVerify:
         self.out = _outputs(B, K1 - 1, dev, out, True)
         self.ws, _ = _workspace(B, K1 - 1, V, dev, workspace)
         acc, tok, prb = self.out
+        self.path = int(path)
         self.args = (_ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_onehot),
                      _ptr(proposed), _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B,
                      K1 - 1, V, _ptr(acc), _ptr(tok), _ptr(prb), _ptr(self.ws), self.ws.numel())
 
     def __call__(self, stream=None, hot_events=None):
         s = _stream_handle(stream)
-        if hot_events is None:
+        if hot_events is None and self.path == SPECDEC_PATH_AUTO:
             status = self.lib.specdec_verify(*self.args, s)
         else:
-            opts = _Options(*(e if isinstance(e, int) or e is None else e.cuda_event
-                              for e in hot_events))
+            opts = _options(hot_events, self.path)
             status = self.lib.specdec_verify_ex(*self.args, s, ctypes.byref(opts))
         if status != 0:
             _raise(status, "specdec_verify")

@@ -7,6 +7,8 @@
 #include "kernels.h"
 #include "specdec.h"
 
+static_assert(SPECDEC_SMALL_V_MAX == specdec::kSmallVMax, "one-wave path limit");
+
 namespace {
 
 bool misaligned(const void* p, size_t a) {
@@ -70,6 +72,12 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.stream = static_cast<hipStream_t>(stream);
   a.hot_begin = opts ? static_cast<hipEvent_t>(opts->hot_event_begin) : nullptr;
   a.hot_end = opts ? static_cast<hipEvent_t>(opts->hot_event_end) : nullptr;
+  a.path = opts ? opts->path : SPECDEC_PATH_AUTO;
+  if (a.path != SPECDEC_PATH_AUTO && a.path != SPECDEC_PATH_STREAMING &&
+      a.path != SPECDEC_PATH_SMALL_VOCAB)
+    return SPECDEC_ERR_SHAPE;
+  if (a.path == SPECDEC_PATH_SMALL_VOCAB && (match || V > SPECDEC_SMALL_V_MAX))
+    return SPECDEC_ERR_SHAPE;
   return specdec::launch_verify(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 

@@ -92,11 +92,16 @@ struct LaunchArgs {
   float* out_probs;
   Workspace ws;
   hipStream_t stream;
-  hipEvent_t hot_begin;      // optional, recorded around the streaming kernel
-  hipEvent_t hot_end;
+  hipEvent_t hot_begin;      // optional, recorded around the streaming (or small-vocabulary)
+  hipEvent_t hot_end;        // kernel
+  int path;                  // 0: automatic, 1: streaming kernels, 2: one wave per sequence
 };
 
+// Largest vocabulary the one-wave-per-sequence path takes (four 4-token quads per lane).
+constexpr int kSmallVMax = 1024;
+
 hipError_t launch_verify(const LaunchArgs& a);
+hipError_t launch_small_verify(const LaunchArgs& a);  // small.hip; V <= kSmallVMax, no match
 
 // ---- n-gram drafter (ngram.hip) ----
 constexpr int kNgramTile = 8192;   // candidate positions per workgroup

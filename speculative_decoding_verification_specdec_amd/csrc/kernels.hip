@@ -34,22 +34,15 @@
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace specdec {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kTempMin = 1e-6f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSub = kChunk / kWaves;          // tokens per wave sub-chunk (2048)
 constexpr int kPerThread = kSub / 64;          // logits per lane per sub-chunk (32)
 constexpr int kMaxRows = 64;           // K + 1 <= 64 target rows per sequence
-
-__device__ __forceinline__ bool temp_valid(float T) {
-  return T == 0.f || (T >= kTempMin && T <= FLT_MAX);
-}
-// exp2 scale: log2(e)/T for sampled rows, log2(e) (softmax at T = 1) for greedy rows.
-__device__ __forceinline__ float temp_scale(float T) { return T == 0.f ? kLog2e : kLog2e / T; }
 
 __device__ __forceinline__ float load_logit(const uint16_t* p, long long i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
@@ -98,72 +91,6 @@ struct Stat {
 // exponentiates against it, so the sum is a plain wave sum: one exp per logit plus one, instead
 // of a rescaling (m, s) merge at every reduction step.
 // ------------------------------------------------------------------------------------------
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float read_lane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Max over the wave (every lane gets it): 16-lane rows by DPP, then the four row results.
-// fmaxf ignores NaN; a NaN logit poisons the sum instead.
-__device__ __forceinline__ float wave_max_f(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
-  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
-  return fmaxf(fmaxf(read_lane_f(v, 0), read_lane_f(v, 16)),
-               fmaxf(read_lane_f(v, 32), read_lane_f(v, 48)));
-}
-
-// Sum over the wave in a fixed order (every lane gets it).
-__device__ __forceinline__ float wave_sum_f(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x124>(v);
-  v += dpp_f<0x128>(v);
-  return (read_lane_f(v, 0) + read_lane_f(v, 16)) + (read_lane_f(v, 32) + read_lane_f(v, 48));
-}
-
-// fp64 wave scans with DPP moves of both 32-bit halves (no LDS round trips): row_shr 1, 2, 4, 8
-// within each 16-lane row, then row_bcast 15 / 31 carry the row totals across rows.  Lanes whose
-// DPP source lies outside the row read 0, so the additions are the textbook inclusive scan.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ double dpp_move_d(double v) {
-  const long long bits = __double_as_longlong(v);
-  const int lo =
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, kRowMask, 0xf, false);
-  const int hi =
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, kRowMask, 0xf, false);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-__device__ __forceinline__ double wave_inclusive_scan(double v) {
-  v += dpp_move_d<0x111, 0xf>(v);  // row_shr:1
-  v += dpp_move_d<0x112, 0xf>(v);  // row_shr:2
-  v += dpp_move_d<0x114, 0xf>(v);  // row_shr:4
-  v += dpp_move_d<0x118, 0xf>(v);  // row_shr:8
-  v += dpp_move_d<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_move_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
-// Lane l's value, read by every lane (uniform).
-__device__ __forceinline__ double read_lane_d(double v, int l) {
-  const long long bits = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), l);
-  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), l);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-// Sum over the wave, the same in every lane.
-__device__ __forceinline__ double wave_total(double v) {
-  return read_lane_d(wave_inclusive_scan(v), 63);
-}
-
 struct MaxSum {
   float m;
   float s;
@@ -275,11 +202,6 @@ __device__ __forceinline__ Stat merge4(const Stat& v, const RowPartial (&p)[4], 
     if (p[t].m == M) r.a = min(r.a, p[t].arg);
   }
   return r;
-}
-
-template <int kCtrl>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
 }
 
 // The same over each 16-lane row (every lane of a row ends with its row's result).
@@ -1170,6 +1092,11 @@ WorkspaceLayout workspace_layout(int B, int K, int V) {
 }
 
 hipError_t launch_verify(const LaunchArgs& a) {
+  // Rows of at most kSmallVMax tokens fit one wave's registers: one kernel, one wave per
+  // sequence (small.hip), unless the streaming kernels are asked for.  Match mode always
+  // streams.
+  const bool small = !a.match && a.V <= kSmallVMax && a.path != 1;
+  if (small) return launch_small_verify(a);
   return a.logits_bf16 ? launch_typed<uint16_t>(a) : launch_typed<float>(a);
 }
 

@@ -11,26 +11,29 @@ import torch
 
 import oracle
 from oracle.parity import compare
-from speculative_decoding_verification_specdec_amd import (inputs_to_device, specdec_verify,
-                                                           specdec_verify_greedy)
+from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
+                                                           SPECDEC_PATH_STREAMING,
+                                                           SPECDEC_SMALL_V_MAX, inputs_to_device,
+                                                           specdec_verify, specdec_verify_greedy)
 from speculative_decoding_verification_specdec_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_gpu(inp, d=None):
+def run_gpu(inp, d=None, path=SPECDEC_PATH_AUTO):
     d = d or inputs_to_device(inp, DEV)
     acc, tok, prb = specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
                                    d["uniforms"], draft_onehot=d["draft_onehot"],
-                                   num_draft=d["num_draft"])
+                                   num_draft=d["num_draft"], path=path)
     torch.cuda.synchronize()
     return acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy()
 
 
-def check(inp, rows=None, max_boundary=None):
-    print(f"\n[case] {inp.name} B={inp.B} K={inp.K} V={inp.V} {inp.logits_dtype}", flush=True)
-    acc, tok, prb = run_gpu(inp)
+def check(inp, rows=None, max_boundary=None, path=SPECDEC_PATH_AUTO):
+    print(f"\n[case] {inp.name} B={inp.B} K={inp.K} V={inp.V} {inp.logits_dtype} path={path}",
+          flush=True)
+    acc, tok, prb = run_gpu(inp, path=path)
     ref = oracle.verify(inp, rows=rows)
     sub = inp
     if rows is not None:
@@ -81,6 +84,15 @@ SMALL = {
 @pytest.mark.parametrize("name", list(SMALL))
 def test_parity_small(name):
     check(SMALL[name]())
+
+
+# The cases with V <= SPECDEC_SMALL_V_MAX take the one-wave path by default; the streaming
+# kernels must give the oracle's results on them too.
+@pytest.mark.parametrize("name", ["tiny_vocab_20k", "one_chunk", "vocab_of_one", "max_K"])
+def test_parity_small_vocab_cases_on_the_streaming_path(name):
+    inp = SMALL[name]()
+    assert inp.V <= SPECDEC_SMALL_V_MAX
+    check(inp, path=SPECDEC_PATH_STREAMING)
 
 
 FULL = {
