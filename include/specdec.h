@@ -133,7 +133,8 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
  * workgroup per 8192-logit chunk of each row, then the accept scan and draw, then the pick).
  * Both paths implement the same rule and pass the same parity tests; SPECDEC_PATH_STREAMING
  * forces the streaming kernels at any V, SPECDEC_PATH_SMALL_VOCAB the one-wave path (an error,
- * SPECDEC_ERR_SHAPE, when V > SPECDEC_SMALL_V_MAX).  Sample-and-match always streams. */
+ * SPECDEC_ERR_SHAPE, when V > SPECDEC_SMALL_V_MAX).  specdec_verify_greedy and
+ * specdec_verify_match take the automatic choice. */
 #define SPECDEC_SMALL_V_MAX 1024
 #define SPECDEC_PATH_AUTO 0
 #define SPECDEC_PATH_STREAMING 1

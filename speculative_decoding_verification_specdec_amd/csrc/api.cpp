@@ -76,7 +76,7 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   if (a.path != SPECDEC_PATH_AUTO && a.path != SPECDEC_PATH_STREAMING &&
       a.path != SPECDEC_PATH_SMALL_VOCAB)
     return SPECDEC_ERR_SHAPE;
-  if (a.path == SPECDEC_PATH_SMALL_VOCAB && (match || V > SPECDEC_SMALL_V_MAX))
+  if (a.path == SPECDEC_PATH_SMALL_VOCAB && V > SPECDEC_SMALL_V_MAX)
     return SPECDEC_ERR_SHAPE;
   return specdec::launch_verify(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }

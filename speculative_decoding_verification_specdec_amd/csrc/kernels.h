@@ -101,7 +101,7 @@ struct LaunchArgs {
 constexpr int kSmallVMax = 1024;
 
 hipError_t launch_verify(const LaunchArgs& a);
-hipError_t launch_small_verify(const LaunchArgs& a);  // small.hip; V <= kSmallVMax, no match
+hipError_t launch_small_verify(const LaunchArgs& a);  // small.hip; V <= kSmallVMax
 
 // ---- n-gram drafter (ngram.hip) ----
 constexpr int kNgramTile = 8192;   // candidate positions per workgroup

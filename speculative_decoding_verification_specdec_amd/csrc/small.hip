@@ -5,7 +5,10 @@
 // snowch.github.io, section "Why the result is exactly the target model"; "Speculative decoding:
 // el secretario...", blog.lo0.es, section "El mecanismo desnudo"): accept x_i while
 // u_i * q_i(x_i) < p_i(x_i), then draw the correction from max(0, p - q) (one-hot rows: p without
-// x) or the bonus from p_k, by inverse CDF over ascending token id with u[b, K].
+// x) or the bonus from p_k, by inverse CDF over ascending token id with u[b, K].  In the
+// sample-and-match mode (same page, the simpler exact scheme) slot i keeps x_i iff the draw
+// from p_i with u[b, i] is x_i, decided from the row total and the sum below x_i, and the first
+// mismatch (or the bonus) is a plain draw of p.
 //
 // When a row fits a wave's registers (V <= 1024: at most four 4-token quads per lane) one wave
 // runs the whole round of its sequence.  Quad q of a row sits in lane q % 64, register q / 64, so
@@ -139,6 +142,28 @@ __device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, 
   return r;
 }
 
+// Match mode: the row's total S and the sum P below token x, both in fp64 from the same
+// per-token exponentials as reduce_row (the row max m is given).
+template <int kQ>
+__device__ __forceinline__ void match_sums(const float (&z)[kQ][4], float m, float c, int x,
+                                           int lane, double& S, double& P) {
+  const float ref = (m == -INFINITY) ? 0.f : m;
+  const float hi = ref * c;
+  const float lo = fmaf(ref, c, -hi);
+  float ls = 0.f, lp = 0.f;
+#pragma unroll
+  for (int j = 0; j < kQ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ee = __builtin_amdgcn_exp2f(fmaf(z[j][e], c, -hi));
+      ls += ee;
+      lp += (j * 64 + lane) * 4 + e < x ? ee : 0.f;
+    }
+  const double f = static_cast<double>(__builtin_amdgcn_exp2f(-lo));
+  S = wave_total(static_cast<double>(ls)) * f;
+  P = wave_total(static_cast<double>(lp)) * f;
+}
+
 // Register value z[j][e] of lane l for a wave-uniform token t = (j * 64 + l) * 4 + e.
 template <int kQ>
 __device__ __forceinline__ float token_value(const float (&z)[kQ][4], int t) {
@@ -152,7 +177,7 @@ __device__ __forceinline__ float token_value(const float (&z)[kQ][4], int t) {
   return read_lane_f(v, l);
 }
 
-template <typename LT, int kQ, bool kVec>
+template <typename LT, int kQ, bool kVec, bool kMatch>
 __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
@@ -179,8 +204,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
   const int kb = seq_ok ? kb_raw : 0;
   const bool greedy = T == 0.f;
-  const bool is_onehot = !greedy && is_oh_flag;
-  const bool model = !greedy && !is_onehot;
+  // Match mode never reads q: one-hot and model-draft rows are alike there.
+  const bool is_onehot = !kMatch && !greedy && is_oh_flag;
+  const bool model = !kMatch && !greedy && !is_onehot;
   const float c = seq_ok ? temp_scale(T) : kLog2e;
   // q_i(x_i) gathers (lane i < k_b of a sampled model-draft row), in flight during row 0.
   float q_lane = 0.f;
@@ -223,8 +249,16 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
       const double ex = exp2((static_cast<double>(token_value<kQ>(zc, x)) -
                               static_cast<double>(st.m)) * static_cast<double>(c));
       bool acc;
+      double den = static_cast<double>(st.s);
       if (greedy) {
         acc = x == st.a;
+      } else if constexpr (kMatch) {
+        // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
+        double S, P;
+        match_sums<kQ>(zc, st.m, c, x, lane, S, P);
+        const double t = static_cast<double>(read_lane_f(u_lane, i)) * S;
+        acc = P <= t && t < P + ex;
+        den = S;
       } else {
         const double qx = model ? static_cast<double>(read_lane_f(q_lane, i)) : 1.0;
         acc = static_cast<double>(read_lane_f(u_lane, i)) * qx * static_cast<double>(st.s) < ex;
@@ -232,7 +266,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
       if (acc) {
         if (lane == i) {
           num_lane = ex;
-          den_lane = static_cast<double>(st.s);
+          den_lane = den;
         }
       } else {
         A = i;
@@ -269,8 +303,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
         prob_lane = static_cast<float>(1.0 / static_cast<double>(sA.s));
       }
     } else {
-      // The draw: residual s * max(0, p - q) (model draft), p without x_A (one-hot), or p.
-      const bool residual = A < kb;
+      // The draw: residual s * max(0, p - q) (model draft), p without x_A (one-hot), or p
+      // (the bonus; every match-mode draw, with u[b, A] at a mismatch).
+      const bool residual = !kMatch && A < kb;
+      const int ucol = (kMatch && A < kb) ? A : K;
       const int excl = (residual && is_onehot) ? __builtin_amdgcn_readlane(x_lane, A) : -1;
       float qv[kQ][4];
       if (residual && model)
@@ -307,7 +343,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
       }
       const bool plain = !(R > 0.0);  // empty residual: draw from p itself
       const double total = plain ? E : R;
-      const double t = static_cast<double>(read_lane_f(u_lane, K)) * total;
+      const double t = static_cast<double>(read_lane_f(u_lane, ucol)) * total;
       // The register (quad column) whose running total passes t; the last positive one if
       // rounding left t at the very top.
       int jh = -1, jlast = -1;
@@ -380,7 +416,10 @@ template <typename LT, int kQ>
 hipError_t launch_q(const LaunchArgs& a, bool vec, bool q_vec) {
   const LT* z = static_cast<const LT*>(a.logits);
   const unsigned grid = static_cast<unsigned>((a.B + kSmallWaves - 1) / kSmallWaves);
-  auto k = vec ? small_verify_kernel<LT, kQ, true> : small_verify_kernel<LT, kQ, false>;
+  auto k = a.match ? (vec ? small_verify_kernel<LT, kQ, true, true>
+                          : small_verify_kernel<LT, kQ, false, true>)
+                   : (vec ? small_verify_kernel<LT, kQ, true, false>
+                          : small_verify_kernel<LT, kQ, false, false>);
   if (a.hot_begin || a.hot_end)
     hipExtLaunchKernelGGL(k, dim3(grid), dim3(64 * kSmallWaves), 0, a.stream, a.hot_begin,
                           a.hot_end, 0, z, a.draft_probs, a.onehot, a.proposed, a.num_draft,
