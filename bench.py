@@ -363,6 +363,9 @@ def main():
                     help="skip the drafter / commit / match-mode / telemetry measurements")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the large-batch and ragged workloads")
+    ap.add_argument("--small-vocab-only", action="store_true",
+                    help="only the one-wave-path workloads (tiny vocabulary call, one-round "
+                         "latency): for profiling that kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -379,7 +382,7 @@ def main():
     from speculative_decoding_verification_specdec_amd.inputs import batch64
 
     cpu = None
-    if not args.no_cpu_baseline and not args.copy_calibration:
+    if not (args.no_cpu_baseline or args.copy_calibration or args.small_vocab_only):
         # Before any GPU call: the all-core leg forks worker processes.
         print("[bench] timing the CPU oracle on the batch", file=sys.stderr, flush=True)
         cpu = cpu_baseline(batch64(), args.cpu_budget)
@@ -397,6 +400,15 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 20}))
         return
     from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
+    if args.small_vocab_only:
+        from speculative_decoding_verification_specdec_amd.inputs import tiny_vocab
+        stream = torch.cuda.Stream()
+        print(json.dumps({
+            "tiny_vocab": bench_workload(dev, stream, tiny_vocab(), "B=100000, k=4, V=32, fp32",
+                                         steps=100),
+            "tiny_vocab_one_round": bench_workload(dev, stream, tiny_vocab(rounds=1),
+                                                   "B=1, k=4, V=32, fp32", steps=400)}))
+        return
 
     print("[bench] generating the B=64 V=128256 k=5 batch", file=sys.stderr, flush=True)
     inp = batch64()
