@@ -1,4 +1,5 @@
-// gfx950 kernel of the verify step for small vocabularies: one wave64 per sequence.
+// gfx950 kernel of the verify step for small vocabularies: one wave64 (or one 16-lane group of a
+// wave) per sequence.
 //
 // The rule is the one kernels.hip implements ("Decodificação especulativa explicada",
 // gsantana.dev, section "A regra de amostragem por rejeição"; "ch15 · Speculative Decoding",
@@ -10,17 +11,21 @@
 // from p_i with u[b, i] is x_i, decided from the row total and the sum below x_i, and the first
 // mismatch (or the bonus) is a plain draw of p.
 //
-// When a row fits a wave's registers (V <= 1024: at most four 4-token quads per lane) one wave
-// runs the whole round of its sequence.  Quad q of a row sits in lane q % 64, register q / 64, so
-// every load instruction of the wave reads one contiguous span.  The wave reads rows 0..k_b once
-// each (the next row's loads are in flight while the current one is reduced), reduces each
-// row's max, sum and lowest argmax with DPP, takes the accept test of each drafted slot as it
-// goes, keeps the row to draw from in registers, and draws: fp64 wave totals per register, the
-// register whose running total passes u * total, one fp64 wave scan inside it, then the four
-// tokens of the hit lane's quad.  One launch, no workspace and no inter-wave communication,
-// where the streaming path would spend a 256-thread workgroup and three launches on rows of at
-// most 1024 tokens.  (Eight quads per lane would need over 256 registers per lane: one wave per
-// SIMD.)
+// When a row fits a wave's registers (V <= 1024: at most four 4-token quads per lane) a group of
+// kG lanes runs the whole round of one sequence: the whole wave (kG = 64), or, when a row is at
+// most 64 tokens and K < 16, each 16-lane DPP row of the wave (kG = 16: four sequences per
+// wave), or, for rows of at most 32 tokens and K < 8, each half row (kG = 8: eight per wave).  Quad q of a row sits in group lane q % kG, register q / kG, so every load instruction
+// reads contiguous spans.  The group reads rows 0..k_b once each (the next row's loads are in
+// flight while the current one is reduced), reduces each row's max, sum and lowest argmax with
+// DPP, takes the accept test of each drafted slot (group lane i <-> slot i) as it goes, keeps
+// the row to draw from in registers, and draws: fp64 group totals per register, the register
+// whose running total passes u * total, one fp64 group scan inside it, then the four tokens of
+// the hit lane's quad.  Every cross-lane operation stays within its group and sits under
+// branches that are uniform over the group, so each one sees its whole group active; the loop over rows runs to the
+// largest k_b of the wave (groups past their own k_b change nothing).  One launch, no
+// workspace and no inter-wave communication, where the streaming path would spend a 256-thread
+// workgroup and three launches on rows of at most 1024 tokens.  (Eight quads per lane would need
+// over 256 registers per lane: one wave per SIMD.)
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -33,7 +38,7 @@
 namespace specdec {
 namespace {
 
-constexpr int kSmallWaves = 4;  // sequences per 256-thread workgroup
+constexpr int kSmallWaves = 4;  // waves per 256-thread workgroup
 
 template <typename LT> struct QuadT;
 template <> struct QuadT<uint16_t> {  // four bf16 logits: 8 bytes
@@ -54,15 +59,100 @@ template <> struct QuadT<float> {  // four fp32 logits: 16 bytes
   static __device__ __forceinline__ float one(const float* p, int i) { return p[i]; }
 };
 
-// Row r's quads for this lane: token (j * 64 + lane) * 4 + e in z[j][e]; -inf past V.  Loads are
-// unconditional (addresses clamped into the row) and masked afterwards.  kVec: V % 4 == 0 and
-// the row is quad-aligned, so each quad is one load.
-template <typename LT, int kQ, bool kVec>
-__device__ __forceinline__ void load_row(const LT* __restrict__ row, int V, int lane,
+// Cross-lane operations within a group of kG lanes (base = its first lane).  Every lane of a
+// group ends with the same value (scan_d: its inclusive prefix within the group).
+//
+// Groups inside one 16-lane DPP row (kG = 8: half rows, kG = 16: whole rows).  Quad permutes,
+// then row_half_mirror (8) or row_ror 4 and 8 (16), leave the group's max / min / sum in every
+// lane; the scan shifts with row_shr and drops what crosses into an 8-lane group from below.
+template <int kG> struct Grp {
+  static_assert(kG == 8 || kG == 16, "groups of 8 or 16 lanes, or the whole wave");
+  template <typename T, typename F>
+  static __device__ __forceinline__ T reduce(T v, F op) {
+    v = op(v, dpp_x<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = op(v, dpp_x<0x4E>(v));    // quad_perm [2,3,0,1]
+    if constexpr (kG == 8) return op(v, dpp_x<0x141>(v));  // row_half_mirror
+    v = op(v, dpp_x<0x124>(v));   // row_ror:4
+    return op(v, dpp_x<0x128>(v));  // row_ror:8
+  }
+  template <int kCtrl>
+  static __device__ __forceinline__ float dpp_x(float v) { return dpp_f<kCtrl>(v); }
+  template <int kCtrl>
+  static __device__ __forceinline__ int dpp_x(int v) { return dpp_i<kCtrl>(v); }
+  static __device__ __forceinline__ float max_f(float v) {
+    return reduce(v, [](float x, float y) { return fmaxf(x, y); });
+  }
+  static __device__ __forceinline__ float at_f(float v, int base, int i) {
+    return __shfl(v, base + i, 64);
+  }
+  static __device__ __forceinline__ int at_i(int v, int base, int i) {
+    return __shfl(v, base + i, 64);
+  }
+  static __device__ __forceinline__ float sum_f(float v, int base) {
+    v = reduce(v, [](float x, float y) { return x + y; });
+    // row_ror pairs different partial sums in different lanes: take one lane's, so that the
+    // group agrees bit for bit (the half-row mirror pairs them commutatively).
+    if constexpr (kG == 16) v = at_f(v, base, 0);
+    return v;
+  }
+  static __device__ __forceinline__ int min_i(int v) {
+    return reduce(v, [](int x, int y) { return min(x, y); });
+  }
+  static __device__ __forceinline__ double scan_d(double v) {
+    const int gl = static_cast<int>(__lane_id()) & (kG - 1);
+    double t = dpp_move_d<0x111, 0xf>(v);  // row_shr:1
+    v += (kG == 16 || gl >= 1) ? t : 0.0;
+    t = dpp_move_d<0x112, 0xf>(v);         // row_shr:2
+    v += (kG == 16 || gl >= 2) ? t : 0.0;
+    t = dpp_move_d<0x114, 0xf>(v);         // row_shr:4
+    v += (kG == 16 || gl >= 4) ? t : 0.0;
+    if constexpr (kG == 16) v += dpp_move_d<0x118, 0xf>(v);  // row_shr:8
+    return v;
+  }
+  static __device__ __forceinline__ double total_d(double v, int base) {
+    const long long bits = __double_as_longlong(scan_d(v));
+    const int lo = __shfl(static_cast<int>(bits), base + kG - 1, 64);
+    const int hi = __shfl(static_cast<int>(bits >> 32), base + kG - 1, 64);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                                static_cast<unsigned int>(lo));
+  }
+  static __device__ __forceinline__ unsigned long long bits(unsigned long long m, int base) {
+    return (m >> base) & ((1ull << kG) - 1ull);
+  }
+};
+
+// The whole wave.
+template <> struct Grp<64> {
+  static __device__ __forceinline__ float max_f(float v) { return wave_max_f(v); }
+  static __device__ __forceinline__ float sum_f(float v, int) { return wave_sum_f(v); }
+  static __device__ __forceinline__ int min_i(int v) {
+    v = min(v, dpp_i<0xB1>(v));
+    v = min(v, dpp_i<0x4E>(v));
+    v = min(v, dpp_i<0x124>(v));
+    v = min(v, dpp_i<0x128>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  }
+  static __device__ __forceinline__ double scan_d(double v) { return wave_inclusive_scan(v); }
+  static __device__ __forceinline__ double total_d(double v, int) { return wave_total(v); }
+  // Lane base + i's value (i the same in every lane of the wave).
+  static __device__ __forceinline__ int at_i(int v, int, int i) {
+    return __builtin_amdgcn_readlane(v, i);
+  }
+  static __device__ __forceinline__ float at_f(float v, int, int i) { return read_lane_f(v, i); }
+  static __device__ __forceinline__ unsigned long long bits(unsigned long long m, int) {
+    return m;
+  }
+};
+// Row r's quads for this lane (group lane gl): token (j * kG + gl) * 4 + e in z[j][e]; -inf past
+// V.  Loads are unconditional (addresses clamped into the row) and masked afterwards.  kVec:
+// V % 4 == 0 and the row is quad-aligned, so each quad is one load.
+template <typename LT, int kQ, int kG, bool kVec>
+__device__ __forceinline__ void load_row(const LT* __restrict__ row, int V, int gl,
                                          float (&z)[kQ][4]) {
 #pragma unroll
   for (int j = 0; j < kQ; ++j) {
-    const int v0 = (j * 64 + lane) * 4;
+    const int v0 = (j * kG + gl) * 4;
     if constexpr (kVec) {
       QuadT<LT>::load(row + min(v0, V - 4), z[j]);
     } else {
@@ -74,15 +164,15 @@ __device__ __forceinline__ void load_row(const LT* __restrict__ row, int V, int 
   for (int j = 0; j < kQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if ((j * 64 + lane) * 4 + e >= V) z[j][e] = -INFINITY;
+      if ((j * kG + gl) * 4 + e >= V) z[j][e] = -INFINITY;
 }
 
-template <int kQ>
-__device__ __forceinline__ void load_q_row(const float* __restrict__ q, int V, int lane, bool vec,
+template <int kQ, int kG>
+__device__ __forceinline__ void load_q_row(const float* __restrict__ q, int V, int gl, bool vec,
                                            float (&w)[kQ][4]) {
 #pragma unroll
   for (int j = 0; j < kQ; ++j) {
-    const int v0 = (j * 64 + lane) * 4;
+    const int v0 = (j * kG + gl) * 4;
     if (vec) {
       QuadT<float>::load(q + min(v0, V - 4), w[j]);
     } else {
@@ -92,15 +182,6 @@ __device__ __forceinline__ void load_q_row(const float* __restrict__ q, int V, i
   }
 }
 
-__device__ __forceinline__ int wave_min_i(int v) {
-  v = min(v, dpp_i<0xB1>(v));
-  v = min(v, dpp_i<0x4E>(v));
-  v = min(v, dpp_i<0x124>(v));
-  v = min(v, dpp_i<0x128>(v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
 struct RowStat {
   float m;  // row max
   float s;  // sum of exp2((z - m) * c)
@@ -108,17 +189,16 @@ struct RowStat {
 };
 
 // Max first, then one exp per logit against it (m * c = hi + lo split exactly, as in the
-// streaming kernel), then the lowest argmax when asked.  NaN / +inf logits make s NaN and an
-// all -inf row gives s = 0: both fail the caller's s > 0 check.
-template <int kQ>
-__device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, bool argmax,
-                                              int lane) {
+// streaming kernel), then the lowest argmax.  NaN / +inf logits make s NaN and an all -inf row
+// gives s = 0: both fail the caller's s > 0 check.
+template <int kQ, int kG>
+__device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, int gl, int base) {
   float lm = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) lm = fmaxf(lm, z[j][e]);
-  const float M = wave_max_f(lm);
+  const float M = Grp<kG>::max_f(lm);
   const float ref = (M == -INFINITY) ? 0.f : M;
   const float hi = ref * c;
   const float lo = fmaf(ref, c, -hi);
@@ -127,26 +207,22 @@ __device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, 
   for (int j = 0; j < kQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) ls += __builtin_amdgcn_exp2f(fmaf(z[j][e], c, -hi));
-  RowStat r{M, wave_sum_f(ls) * __builtin_amdgcn_exp2f(-lo), INT_MAX};
-  if (argmax) {
-    int a = INT_MAX;
-    if (lm == M) {
+  int a = INT_MAX;
+  if (lm == M) {
 #pragma unroll
-      for (int j = kQ - 1; j >= 0; --j)
+    for (int j = kQ - 1; j >= 0; --j)
 #pragma unroll
-        for (int e = 3; e >= 0; --e)
-          if (z[j][e] == M) a = (j * 64 + lane) * 4 + e;
-    }
-    r.a = wave_min_i(a);
+      for (int e = 3; e >= 0; --e)
+        if (z[j][e] == M) a = (j * kG + gl) * 4 + e;
   }
-  return r;
+  return RowStat{M, Grp<kG>::sum_f(ls, base) * __builtin_amdgcn_exp2f(-lo), Grp<kG>::min_i(a)};
 }
 
 // Match mode: the row's total S and the sum P below token x, both in fp64 from the same
 // per-token exponentials as reduce_row (the row max m is given).
-template <int kQ>
+template <int kQ, int kG>
 __device__ __forceinline__ void match_sums(const float (&z)[kQ][4], float m, float c, int x,
-                                           int lane, double& S, double& P) {
+                                           int gl, int base, double& S, double& P) {
   const float ref = (m == -INFINITY) ? 0.f : m;
   const float hi = ref * c;
   const float lo = fmaf(ref, c, -hi);
@@ -157,27 +233,28 @@ __device__ __forceinline__ void match_sums(const float (&z)[kQ][4], float m, flo
     for (int e = 0; e < 4; ++e) {
       const float ee = __builtin_amdgcn_exp2f(fmaf(z[j][e], c, -hi));
       ls += ee;
-      lp += (j * 64 + lane) * 4 + e < x ? ee : 0.f;
+      lp += (j * kG + gl) * 4 + e < x ? ee : 0.f;
     }
   const double f = static_cast<double>(__builtin_amdgcn_exp2f(-lo));
-  S = wave_total(static_cast<double>(ls)) * f;
-  P = wave_total(static_cast<double>(lp)) * f;
+  S = Grp<kG>::total_d(static_cast<double>(ls), base) * f;
+  P = Grp<kG>::total_d(static_cast<double>(lp), base) * f;
 }
 
-// Register value z[j][e] of lane l for a wave-uniform token t = (j * 64 + l) * 4 + e.
-template <int kQ>
-__device__ __forceinline__ float token_value(const float (&z)[kQ][4], int t) {
-  const int j = t >> 8, e = t & 3, l = (t >> 2) & 63;
+// Register value z[j][e] of group lane l for the group's token t = (j * kG + l) * 4 + e
+// (0 <= t < kQ * kG * 4).
+template <int kQ, int kG>
+__device__ __forceinline__ float token_value(const float (&z)[kQ][4], int t, int base) {
+  const int j = t / (4 * kG), e = t & 3, l = (t >> 2) & (kG - 1);
   float v = 0.f;
 #pragma unroll
   for (int jj = 0; jj < kQ; ++jj)
 #pragma unroll
     for (int ee = 0; ee < 4; ++ee)
       if (jj == j && ee == e) v = z[jj][ee];
-  return read_lane_f(v, l);
+  return Grp<kG>::at_f(v, base, l);
 }
 
-template <typename LT, int kQ, bool kVec, bool kMatch>
+template <typename LT, int kQ, int kG, bool kVec, bool kMatch>
 __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
@@ -185,20 +262,25 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     const float* __restrict__ uniforms, int B, int K, int V, int greedy_all, int q_vec,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ out_probs) {
-  const int lane = threadIdx.x & 63;
-  const int b = static_cast<int>(blockIdx.x) * kSmallWaves + static_cast<int>(threadIdx.x >> 6);
-  if (b >= B) return;  // whole wave
+  constexpr int kPerWave = 64 / kG;
+  const int lane = threadIdx.x & 63, gl = lane & (kG - 1), base = lane & ~(kG - 1);
+  const int wave_seq = (static_cast<int>(blockIdx.x) * kSmallWaves +
+                        static_cast<int>(threadIdx.x >> 6)) * kPerWave;
+  if (wave_seq >= B) return;  // whole wave
+  const int b_raw = wave_seq + lane / kG;
+  const bool live = b_raw < B;             // groups past the batch compute on sequence B - 1
+  const int b = live ? b_raw : B - 1;     // and write nothing
   const long long row0 = static_cast<long long>(b) * (K + 1);
   const LT* zrow0 = logits + row0 * V;
 
   // Everything that does not depend on another load goes out first: row 0, the draft count,
-  // the temperature, the drafted ids (lane i: slot i) and the uniforms (lane i: column i).
+  // the temperature, the drafted ids (group lane i: slot i) and the uniforms (column i).
   float zc[kQ][4];
-  load_row<LT, kQ, kVec>(zrow0, V, lane, zc);
+  load_row<LT, kQ, kG, kVec>(zrow0, V, gl, zc);
   const int kb_raw = num_draft != nullptr ? num_draft[b] : K;
   const float T = (greedy_all || temperature == nullptr) ? 0.f : temperature[b];
-  const int x_lane = (K > 0 && lane < K) ? proposed[static_cast<long long>(b) * K + lane] : -1;
-  const float u_lane = (uniforms != nullptr && lane <= K) ? uniforms[row0 + lane] : 0.f;
+  const int x_lane = (K > 0 && gl < K) ? proposed[static_cast<long long>(b) * K + gl] : -1;
+  const float u_lane = (uniforms != nullptr && gl <= K) ? uniforms[row0 + gl] : 0.f;
   const bool is_oh_flag = onehot != nullptr && onehot[b] != 0;
 
   const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
@@ -208,73 +290,74 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   const bool is_onehot = !kMatch && !greedy && is_oh_flag;
   const bool model = !kMatch && !greedy && !is_onehot;
   const float c = seq_ok ? temp_scale(T) : kLog2e;
-  // q_i(x_i) gathers (lane i < k_b of a sampled model-draft row), in flight during row 0.
+  // q_i(x_i) gathers (slot i < k_b of a sampled model-draft row), in flight during row 0.
   float q_lane = 0.f;
   const bool x_ok_lane = x_lane >= 0 && x_lane < V;
-  if (seq_ok && model && draft_probs != nullptr && lane < kb && x_ok_lane)
-    q_lane = draft_probs[(static_cast<long long>(b) * K + lane) * V + x_lane];
+  if (seq_ok && model && draft_probs != nullptr && gl < kb && x_ok_lane)
+    q_lane = draft_probs[(static_cast<long long>(b) * K + gl) * V + x_lane];
 
   bool ok = seq_ok;
-  if (ok && !greedy) {
-    // Used uniforms: columns < k_b and column K.
-    const bool bad_u = (lane < kb || lane == K) && !(u_lane >= 0.f && u_lane < 1.f);
-    if (__ballot(bad_u) != 0ull) ok = false;
-    if (model && kb > 0) {
-      if (draft_probs == nullptr) ok = false;
-      const bool bad_q = lane < kb && x_ok_lane && !(q_lane >= 0.f && q_lane <= FLT_MAX);
-      if (__ballot(bad_q) != 0ull) ok = false;
-    }
+  {
+    // Used uniforms: columns < k_b and column K (sampled rows); drafted ids in [0, V);
+    // gathered q in [0, FLT_MAX] (sampled model-draft rows).
+    const bool bad_u = !greedy && (gl < kb || gl == K) && !(u_lane >= 0.f && u_lane < 1.f);
+    const bool bad_x = gl < kb && !x_ok_lane;
+    const bool bad_q = model && gl < kb && x_ok_lane && !(q_lane >= 0.f && q_lane <= FLT_MAX);
+    if (Grp<kG>::bits(__ballot(bad_u || bad_x || bad_q), base) != 0ull) ok = false;
+    if (model && kb > 0 && draft_probs == nullptr) ok = false;
   }
-  if (__ballot(lane < kb && !x_ok_lane) != 0ull) ok = false;
 
   // Rows 0..k_b: reduce each, decide each drafted slot, keep the row to draw from.  The next
-  // row's loads are in flight while the current one is reduced.  (Deeper prefetch -- groups of
-  // rows in flight -- measured slower: the extra registers cost more occupancy than the round
-  // trips they save.)
+  // row's loads are in flight while the current one is reduced.  The loop runs to the largest
+  // k_b of the wave; a group past its own k_b (or invalid) recomputes its last row and changes
+  // nothing.  (Deeper prefetch -- groups of rows in flight -- measured slower: the extra
+  // registers cost more occupancy than the round trips they save.)
+  int kb_wave = kb;
+  if constexpr (kG < 64) kb_wave = -Grp<64>::min_i(-kb);  // the largest k_b of the wave
   int A = kb;                 // first rejected slot (k_b: every draft accepted)
   float zs[kQ][4];            // row A's logits
-  RowStat sA{0.f, 0.f, INT_MAX};
-  double num_lane = 0.0, den_lane = 1.0;  // lane i's output probability num / den
-  for (int i = 0; i <= kb && ok; ++i) {    // wave-uniform
+#pragma unroll
+  for (int j = 0; j < kQ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) zs[j][e] = -INFINITY;
+  RowStat sA{0.f, 1.f, INT_MAX};
+  double num_lane = 0.0, den_lane = 1.0;  // slot gl's output probability num / den
+  for (int i = 0; i <= kb_wave; ++i) {     // wave-uniform
+    const bool act = ok && i <= kb;
     float zn[kQ][4];
-    if (i < kb) load_row<LT, kQ, kVec>(zrow0 + static_cast<long long>(i + 1) * V, V, lane, zn);
-    const RowStat st = reduce_row<kQ>(zc, c, greedy, lane);
-    if (!(st.s > 0.f)) {
-      ok = false;
-      break;
+    if (i < kb_wave)  // the next row of this sequence (its last one again past k_b)
+      load_row<LT, kQ, kG, kVec>(zrow0 + static_cast<long long>(min(i + 1, kb)) * V, V, gl, zn);
+    const RowStat st = reduce_row<kQ, kG>(zc, c, gl, base);
+    if (act && !(st.s > 0.f)) ok = false;
+    const bool decide = act && ok && i < kb && A == kb;
+    const int slot = min(i, K > 0 ? K - 1 : 0);
+    const int x = Grp<kG>::at_i(x_lane, base, slot);
+    const int xt = min(max(x, 0), V - 1);
+    const double ex = exp2((static_cast<double>(token_value<kQ, kG>(zc, xt, base)) -
+                            static_cast<double>(st.m)) * static_cast<double>(c));
+    bool acc;
+    double den = static_cast<double>(st.s);
+    if (greedy) {
+      acc = x == st.a;
+    } else if constexpr (kMatch) {
+      // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
+      double S, P;
+      match_sums<kQ, kG>(zc, st.m, c, xt, gl, base, S, P);
+      const double t = static_cast<double>(Grp<kG>::at_f(u_lane, base, slot)) * S;
+      acc = P <= t && t < P + ex;
+      den = S;
+    } else {
+      const double qx = model ? static_cast<double>(Grp<kG>::at_f(q_lane, base, slot)) : 1.0;
+      acc = static_cast<double>(Grp<kG>::at_f(u_lane, base, slot)) * qx *
+                static_cast<double>(st.s) < ex;
     }
-    bool take = false;         // this row is the one to draw from
-    if (i < kb && A == kb) {
-      const int x = __builtin_amdgcn_readlane(x_lane, i);
-      const double ex = exp2((static_cast<double>(token_value<kQ>(zc, x)) -
-                              static_cast<double>(st.m)) * static_cast<double>(c));
-      bool acc;
-      double den = static_cast<double>(st.s);
-      if (greedy) {
-        acc = x == st.a;
-      } else if constexpr (kMatch) {
-        // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
-        double S, P;
-        match_sums<kQ>(zc, st.m, c, x, lane, S, P);
-        const double t = static_cast<double>(read_lane_f(u_lane, i)) * S;
-        acc = P <= t && t < P + ex;
-        den = S;
-      } else {
-        const double qx = model ? static_cast<double>(read_lane_f(q_lane, i)) : 1.0;
-        acc = static_cast<double>(read_lane_f(u_lane, i)) * qx * static_cast<double>(st.s) < ex;
-      }
-      if (acc) {
-        if (lane == i) {
-          num_lane = ex;
-          den_lane = den;
-        }
-      } else {
-        A = i;
-        take = true;
-      }
-    } else if (i == kb && A == kb) {
-      take = true;             // the bonus row
+    if (decide && acc && gl == i) {
+      num_lane = ex;
+      den_lane = den;
     }
+    // This row is the one to draw from: the first rejection, or the bonus row.
+    const bool take = act && ok && A == kb && ((i < kb && !acc) || i == kb);
+    if (decide && !acc) A = i;
     if (take) {
       sA = st;
 #pragma unroll
@@ -282,7 +365,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) zs[j][e] = zc[j][e];
     }
-    if (i < kb) {
+    if (i < kb_wave) {
 #pragma unroll
       for (int j = 0; j < kQ; ++j)
 #pragma unroll
@@ -290,136 +373,142 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     }
   }
 
-  int tok_lane = -1;
-  float prob_lane = 0.f;
-  if (ok) {
-    if (lane < A) {
-      tok_lane = x_lane;
-      prob_lane = static_cast<float>(num_lane / den_lane);
-    }
-    if (greedy) {
-      if (lane == A) {
-        tok_lane = sA.a;       // argmax: exp2(0) / s
-        prob_lane = static_cast<float>(1.0 / static_cast<double>(sA.s));
-      }
-    } else {
-      // The draw: residual s * max(0, p - q) (model draft), p without x_A (one-hot), or p
-      // (the bonus; every match-mode draw, with u[b, A] at a mismatch).
-      const bool residual = !kMatch && A < kb;
-      const int ucol = (kMatch && A < kb) ? A : K;
-      const int excl = (residual && is_onehot) ? __builtin_amdgcn_readlane(x_lane, A) : -1;
-      float qv[kQ][4];
-      if (residual && model)
-        load_q_row<kQ>(draft_probs + (static_cast<long long>(b) * K + A) * V, V, lane,
-                       q_vec != 0, qv);
-      // Weight of token v (lane-local value z, draft probability q); e returns s * p(v).
-      auto weight = [&](float zv, float qq, int v, float& e) {
-        e = v < V ? __builtin_amdgcn_exp2f((zv - sA.m) * c) : 0.f;
-        if (residual && model) return v < V ? fmaxf(0.f, fmaf(-sA.s, qq, e)) : 0.f;
-        if (residual) return v == excl ? 0.f : e;
-        return e;
-      };
-      float gq[kQ], eq[kQ];
+  // The draw (sampled valid sequences; a group-uniform branch: every cross-lane operation
+  // inside stays within the group): residual s * max(0, p - q) (model draft), p without x_A
+  // (one-hot), or p (the bonus; every match-mode draw, with u[b, A] at a mismatch).
+  int yt = -1;
+  float zyt = 0.f;
+  if (ok && !greedy) {
+    const bool residual = !kMatch && A < kb;
+    const int ucol = (kMatch && A < kb) ? A : K;
+    const int xA = Grp<kG>::at_i(x_lane, base, min(A, K > 0 ? K - 1 : 0));
+    const int excl = (residual && is_onehot) ? xA : -1;
+    const bool need_q = residual && model;
+    float qv[kQ][4];
 #pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        gq[j] = 0.f;
-        eq[j] = 0.f;
+    for (int j = 0; j < kQ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[j][e] = 0.f;
+    if (need_q)  // lane-divergent load, no cross-lane operation inside
+      load_q_row<kQ, kG>(draft_probs + (static_cast<long long>(b) * K + A) * V, V, gl, q_vec != 0,
+                         qv);
+    // Weight of token v (lane-local value z, draft probability q); e returns s * p(v).
+    auto weight = [&](float zv, float qq, int v, float& e) {
+      e = v < V ? __builtin_amdgcn_exp2f((zv - sA.m) * c) : 0.f;
+      if (residual && model) return v < V ? fmaxf(0.f, fmaf(-sA.s, qq, e)) : 0.f;
+      if (residual) return v == excl ? 0.f : e;
+      return e;
+    };
+    float gq[kQ], eq[kQ];
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      gq[j] = 0.f;
+      eq[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float ee;
+        gq[j] += weight(zs[j][e], qv[j][e], (j * kG + gl) * 4 + e, ee);
+        eq[j] += ee;
+      }
+    }
+    double tot_w[kQ], tot_e[kQ];
+    double R = 0.0, E = 0.0;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      tot_w[j] = Grp<kG>::total_d(static_cast<double>(gq[j]), base);
+      tot_e[j] = Grp<kG>::total_d(static_cast<double>(eq[j]), base);
+      R += tot_w[j];
+      E += tot_e[j];
+    }
+    const bool plain = !(R > 0.0);  // empty residual: draw from p itself
+    const double total = plain ? E : R;
+    const double t = static_cast<double>(Grp<kG>::at_f(u_lane, base, ucol)) * total;
+    // The register (quad column) whose running total passes t; the last positive one if
+    // rounding left t at the very top.
+    int jh = -1, jlast = -1;
+    double run0 = 0.0, base_last = 0.0, run = 0.0;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      const double tj = plain ? tot_e[j] : tot_w[j];
+      if (tj > 0.0) {
+        if (jh < 0 && run + tj > t) { jh = j; run0 = run; }
+        jlast = j;
+        base_last = run;
+      }
+      run += tj;
+    }
+    if (jh < 0) { jh = jlast >= 0 ? jlast : 0; run0 = base_last; }
+    // Column jh's weights again (same arithmetic as the sums above).
+    float g = 0.f, wq[4] = {0.f, 0.f, 0.f, 0.f}, zq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kQ; ++j)
+      if (j == jh) {
+        g = plain ? eq[j] : gq[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float ee;
-          gq[j] += weight(zs[j][e], (residual && model) ? qv[j][e] : 0.f, (j * 64 + lane) * 4 + e,
-                          ee);
-          eq[j] += ee;
+          const float ww = weight(zs[j][e], qv[j][e], (j * kG + gl) * 4 + e, ee);
+          wq[e] = plain ? ee : ww;
+          zq[e] = zs[j][e];
         }
       }
-      double tot_w[kQ], tot_e[kQ];
-      double R = 0.0, E = 0.0;
+    const double own = static_cast<double>(g);
+    const double inc = Grp<kG>::scan_d(own);
+    const unsigned long long hit = Grp<kG>::bits(__ballot(own > 0.0 && run0 + inc > t), base);
+    const unsigned long long pos = Grp<kG>::bits(__ballot(own > 0.0), base);
+    const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
+                       : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+    // Each lane walks its quad in token order; the hit lane's result is the draw.
+    int y = -1, ylast = -1;
+    float zy = 0.f, zlast = 0.f;
+    double r = run0 + inc - own;
 #pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        tot_w[j] = wave_total(static_cast<double>(gq[j]));
-        tot_e[j] = wave_total(static_cast<double>(eq[j]));
-        R += tot_w[j];
-        E += tot_e[j];
-      }
-      const bool plain = !(R > 0.0);  // empty residual: draw from p itself
-      const double total = plain ? E : R;
-      const double t = static_cast<double>(read_lane_f(u_lane, ucol)) * total;
-      // The register (quad column) whose running total passes t; the last positive one if
-      // rounding left t at the very top.
-      int jh = -1, jlast = -1;
-      double base = 0.0, base_last = 0.0, run = 0.0;
-#pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        const double tj = plain ? tot_e[j] : tot_w[j];
-        if (tj > 0.0) {
-          if (jh < 0 && run + tj > t) { jh = j; base = run; }
-          jlast = j;
-          base_last = run;
-        }
-        run += tj;
-      }
-      if (jh < 0) { jh = jlast >= 0 ? jlast : 0; base = base_last; }
-      // Column jh's weights again (same arithmetic as the sums above).
-      float g = 0.f, wq[4] = {0.f, 0.f, 0.f, 0.f}, zq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < kQ; ++j)
-        if (j == jh) {
-          g = plain ? eq[j] : gq[j];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float ee;
-            const float ww = weight(zs[j][e], (residual && model) ? qv[j][e] : 0.f,
-                                    (j * 64 + lane) * 4 + e, ee);
-            wq[e] = plain ? ee : ww;
-            zq[e] = zs[j][e];
-          }
-        }
-      const double own = static_cast<double>(g);
-      const double inc = wave_inclusive_scan(own);
-      const unsigned long long hit = __ballot(own > 0.0 && base + inc > t);
-      const unsigned long long pos = __ballot(own > 0.0);
-      const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
-                         : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
-      // The hit lane walks its quad in token order.
-      int y = -1, ylast = -1;
-      float zy = 0.f, zlast = 0.f;
-      double r = base + inc - own;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r += static_cast<double>(wq[e]);
-        if (wq[e] > 0.f) {
-          const int v = (jh * 64 + lane) * 4 + e;
-          if (y < 0 && r > t) { y = v; zy = zq[e]; }
-          ylast = v;
-          zlast = zq[e];
-        }
-      }
-      if (y < 0) { y = ylast; zy = zlast; }
-      const int yt = __builtin_amdgcn_readlane(y, hl);
-      const float zyt = read_lane_f(zy, hl);
-      if (lane == A) {
-        tok_lane = yt;
-        prob_lane = static_cast<float>(
-            exp2((static_cast<double>(zyt) - static_cast<double>(sA.m)) * static_cast<double>(c)) /
-            static_cast<double>(sA.s));
+    for (int e = 0; e < 4; ++e) {
+      r += static_cast<double>(wq[e]);
+      if (wq[e] > 0.f) {
+        const int v = (jh * kG + gl) * 4 + e;
+        if (y < 0 && r > t) { y = v; zy = zq[e]; }
+        ylast = v;
+        zlast = zq[e];
       }
     }
+    if (y < 0) { y = ylast; zy = zlast; }
+    yt = Grp<kG>::at_i(y, base, hl);
+    zyt = Grp<kG>::at_f(zy, base, hl);
   }
-  if (lane <= K) {
-    out_tokens[row0 + lane] = ok ? tok_lane : -1;
-    if (out_probs) out_probs[row0 + lane] = ok ? prob_lane : 0.f;
+
+  int tok_lane = -1;
+  float prob_lane = 0.f;
+  if (ok) {
+    if (gl < A) {
+      tok_lane = x_lane;
+      prob_lane = static_cast<float>(num_lane / den_lane);
+    } else if (gl == A && greedy) {
+      tok_lane = sA.a;         // argmax: exp2(0) / s
+      prob_lane = static_cast<float>(1.0 / static_cast<double>(sA.s));
+    } else if (gl == A) {
+      tok_lane = yt;
+      prob_lane = static_cast<float>(
+          exp2((static_cast<double>(zyt) - static_cast<double>(sA.m)) * static_cast<double>(c)) /
+          static_cast<double>(sA.s));
+    }
   }
-  if (lane == 0) accept_len[b] = ok ? A : -1;
+  if (live && gl <= K) {
+    out_tokens[row0 + gl] = ok ? tok_lane : -1;
+    if (out_probs) out_probs[row0 + gl] = ok ? prob_lane : 0.f;
+  }
+  if (live && gl == 0) accept_len[b] = ok ? A : -1;
 }
 
-template <typename LT, int kQ>
+template <typename LT, int kQ, int kG>
 hipError_t launch_q(const LaunchArgs& a, bool vec, bool q_vec) {
   const LT* z = static_cast<const LT*>(a.logits);
-  const unsigned grid = static_cast<unsigned>((a.B + kSmallWaves - 1) / kSmallWaves);
-  auto k = a.match ? (vec ? small_verify_kernel<LT, kQ, true, true>
-                          : small_verify_kernel<LT, kQ, false, true>)
-                   : (vec ? small_verify_kernel<LT, kQ, true, false>
-                          : small_verify_kernel<LT, kQ, false, false>);
+  constexpr int kPerBlock = kSmallWaves * (64 / kG);  // sequences per workgroup
+  const unsigned grid = static_cast<unsigned>((a.B + kPerBlock - 1) / kPerBlock);
+  auto k = a.match ? (vec ? small_verify_kernel<LT, kQ, kG, true, true>
+                          : small_verify_kernel<LT, kQ, kG, false, true>)
+                   : (vec ? small_verify_kernel<LT, kQ, kG, true, false>
+                          : small_verify_kernel<LT, kQ, kG, false, false>);
   if (a.hot_begin || a.hot_end)
     hipExtLaunchKernelGGL(k, dim3(grid), dim3(64 * kSmallWaves), 0, a.stream, a.hot_begin,
                           a.hot_end, 0, z, a.draft_probs, a.onehot, a.proposed, a.num_draft,
@@ -440,9 +529,11 @@ hipError_t launch_small_typed(const LaunchArgs& a) {
   const bool q_vec = a.V % 4 == 0 && (a.draft_probs == nullptr ||
                                       reinterpret_cast<uintptr_t>(a.draft_probs) % 16 == 0);
   const int quads = (a.V + 3) / 4;  // at most 256: V <= kSmallVMax
-  if (quads <= 64) return launch_q<LT, 1>(a, vec, q_vec);
-  if (quads <= 128) return launch_q<LT, 2>(a, vec, q_vec);
-  return launch_q<LT, 4>(a, vec, q_vec);
+  if (quads <= 8 && a.K < 8) return launch_q<LT, 1, 8>(a, vec, q_vec);     // 8 sequences/wave
+  if (quads <= 16 && a.K < 16) return launch_q<LT, 1, 16>(a, vec, q_vec);  // 4 sequences/wave
+  if (quads <= 64) return launch_q<LT, 1, 64>(a, vec, q_vec);
+  if (quads <= 128) return launch_q<LT, 2, 64>(a, vec, q_vec);
+  return launch_q<LT, 4, 64>(a, vec, q_vec);
 }
 
 }  // namespace

@@ -3,9 +3,11 @@
 Rows of at most 1024 tokens take that path by default; every case here also runs on the
 streaming kernels (SPECDEC_PATH_STREAMING), so both paths are held to the same bar: accept
 lengths and tokens bit-exact except on boundary rows, probabilities within 1e-5 relative.  The
-cases cover each register layout (1, 2 and 4 quads per lane), quad-aligned and unaligned
-vocabularies, both dtypes, greedy / one-hot / model-draft rows, ragged counts, K = 0 and K = 63,
-the bonus draw, and the invalid-row rules.
+cases cover each register layout (eight sequences per wave for rows of at most 32 tokens and
+K < 8, four for rows of at most 64 tokens and K < 16; else 1, 2 and 4 quads per lane),
+quad-aligned and unaligned vocabularies, both dtypes, greedy / one-hot / model-draft rows, ragged
+counts, batches that end inside a wave, K = 0, 7, 8, 15, 16 and 63, the bonus draw, and the
+invalid-row rules (also with valid and invalid sequences sharing a wave).
 """
 import numpy as np
 import pytest
@@ -45,6 +47,22 @@ CASES = {
     "K0": lambda: gen.make_batch(16, 0, 700, seed=309),
     "V64_many_sequences": lambda: gen.make_batch(5000, 4, 64, seed=310, dtype="f32",
                                                  greedy_frac=0.1, onehot_frac=0.2, ragged=True),
+    # Four sequences per wave (rows of at most 64 tokens, K < 16): batches that end inside a
+    # wave, unaligned rows, the largest K of that layout, and K = 16 (one sequence per wave).
+    "V50_bf16_mixed_ragged_B7": lambda: gen.make_batch(7, 7, 50, seed=314, greedy_frac=0.25,
+                                                       onehot_frac=0.25, ragged=True),
+    "V64_f32_K15_ragged_B37": lambda: gen.make_batch(37, 15, 64, seed=315, dtype="f32",
+                                                     onehot_frac=0.3, ragged=True),
+    "V61_f32_calibrated_B1001": lambda: gen.make_batch(1001, 3, 61, seed=316, dtype="f32",
+                                                       draft_sigma=0.3, draft_at_row_temp=True),
+    "V64_bf16_K16": lambda: gen.make_batch(30, 16, 64, seed=317, greedy_frac=0.2, ragged=True),
+    # Eight sequences per wave (rows of at most 32 tokens, K < 8), and K = 8 (four per wave).
+    "V29_f32_mixed_ragged_B13": lambda: gen.make_batch(13, 7, 29, seed=318, dtype="f32",
+                                                       greedy_frac=0.2, onehot_frac=0.3,
+                                                       ragged=True),
+    "V32_bf16_many_sequences": lambda: gen.make_batch(4099, 4, 32, seed=319, onehot_frac=0.25,
+                                                      ragged=True),
+    "V32_f32_K8": lambda: gen.make_batch(21, 8, 32, seed=320, dtype="f32", ragged=True),
 }
 
 
@@ -81,9 +99,10 @@ def test_small_vocab_parity_both_paths(name):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("V", [300, 61, 30])  # one, four and eight sequences per wave
 @pytest.mark.parametrize("path", [SPECDEC_PATH_SMALL_VOCAB, SPECDEC_PATH_STREAMING])
-def test_small_vocab_invalid_rows_are_poisoned_alone(path):
-    inp = gen.make_batch(24, 4, 300, seed=311, dtype="f32", onehot_frac=0.25, ragged=True)
+def test_small_vocab_invalid_rows_are_poisoned_alone(path, V):
+    inp = gen.make_batch(24, 4, V, seed=311, dtype="f32", onehot_frac=0.25, ragged=True)
     kb = inp.num_draft
     L, Q, X, T, U, N = (inp.logits, inp.draft_probs, inp.proposed, inp.temperature, inp.uniforms,
                         inp.num_draft)
@@ -96,12 +115,12 @@ def test_small_vocab_invalid_rows_are_poisoned_alone(path):
     L[5, 0, 17] = np.nan               # NaN / +inf / all -inf in a used row
     L[6, kb[6], 3] = np.inf
     L[7, 0, :] = -np.inf
-    X[8, 0] = 300                      # id out of range
+    X[8, 0] = V                        # id out of range
     U[9, 0] = 1.0                      # uniform out of range (accept column / draw column)
     U[10, 4] = np.nan
     b = [m for m in model if m >= 12][-1]
     Q[b, 0, X[b, 0]] = -0.25           # negative gathered q
-    L[11, :, 100:200] = -np.inf        # -inf entries: valid
+    L[11, :, V // 3:2 * V // 3] = -np.inf  # -inf entries: valid
     acc, _, _ = check(inp, path)
     ref = oracle.verify(inp)
     bad = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, b}
@@ -126,7 +145,9 @@ def test_one_wave_path_rejects_a_large_vocabulary():
 
 
 MATCH_CASES = ["V1_f32", "V255_f32_mixed_ragged", "V257_bf16_calibrated", "V1000_bf16_mixed_ragged",
-               "V1024_f32_max_K", "K0", "V64_many_sequences"]
+               "V1024_f32_max_K", "K0", "V64_many_sequences", "V50_bf16_mixed_ragged_B7",
+               "V64_f32_K15_ragged_B37", "V61_f32_calibrated_B1001", "V29_f32_mixed_ragged_B13",
+               "V32_bf16_many_sequences"]
 
 
 @pytest.mark.parametrize("name", MATCH_CASES)

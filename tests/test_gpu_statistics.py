@@ -29,6 +29,7 @@ CASES = {
     "bf16_two_chunks": dict(V=9000, K=2, N=20_000, seed=104, dtype="bf16", z_sigma=1.0,
                             draft_sigma=0.5),
     "onehot_V64": dict(V=64, K=3, N=100_000, seed=105, T=0.8, onehot=True),
+    "bf16_V50_ragged": dict(V=50, K=7, N=100_000, seed=107, dtype="bf16", T=0.9, ragged=True),
     "onehot_bf16_ragged": dict(V=512, K=4, N=100_000, seed=106, dtype="bf16", onehot=True,
                                ragged=True),
 }
