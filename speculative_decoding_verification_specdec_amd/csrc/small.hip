@@ -145,11 +145,12 @@ template <> struct Grp<64> {
   }
 };
 // Row r's quads for this lane (group lane gl): token (j * kG + gl) * 4 + e in z[j][e]; -inf past
-// V.  Loads are unconditional (addresses clamped into the row) and masked afterwards.  kVec:
-// V % 4 == 0 and the row is quad-aligned, so each quad is one load.
+// V (mask_row).  Loads are unconditional (addresses clamped into the row) and masked afterwards,
+// so that several rows' loads can be in flight before the first wait.  kVec: V % 4 == 0 and the
+// row is quad-aligned, so each quad is one load.
 template <typename LT, int kQ, int kG, bool kVec>
-__device__ __forceinline__ void load_row(const LT* __restrict__ row, int V, int gl,
-                                         float (&z)[kQ][4]) {
+__device__ __forceinline__ void load_row_raw(const LT* __restrict__ row, int V, int gl,
+                                             float (&z)[kQ][4]) {
 #pragma unroll
   for (int j = 0; j < kQ; ++j) {
     const int v0 = (j * kG + gl) * 4;
@@ -160,11 +161,22 @@ __device__ __forceinline__ void load_row(const LT* __restrict__ row, int V, int 
       for (int e = 0; e < 4; ++e) z[j][e] = QuadT<LT>::one(row, min(v0 + e, V - 1));
     }
   }
+}
+
+template <int kQ, int kG>
+__device__ __forceinline__ void mask_row(int V, int gl, float (&z)[kQ][4]) {
 #pragma unroll
   for (int j = 0; j < kQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if ((j * kG + gl) * 4 + e >= V) z[j][e] = -INFINITY;
+}
+
+template <typename LT, int kQ, int kG, bool kVec>
+__device__ __forceinline__ void load_row(const LT* __restrict__ row, int V, int gl,
+                                         float (&z)[kQ][4]) {
+  load_row_raw<LT, kQ, kG, kVec>(row, V, gl, z);
+  mask_row<kQ, kG>(V, gl, z);
 }
 
 template <int kQ, int kG>
@@ -180,6 +192,21 @@ __device__ __forceinline__ void load_q_row(const float* __restrict__ q, int V, i
       for (int e = 0; e < 4; ++e) w[j][e] = q[min(v0 + e, V - 1)];
     }
   }
+}
+
+// 2^((z - m) * c) for one token, as a double good to a few parts in 1e7: the exponent r in fp64
+// (z - m is exact there), split as r = rh + rl with rh = (float)r, then 2^rh from the hardware
+// exp2 (about 1 ulp) times 2^rl = 1 + rl ln 2 (|rl| <= ulp(rh) / 2, so the next term is below
+// 1e-14).  The accept test and the emitted probabilities need no more (the sum it is compared
+// with is an fp32 sum), and this costs a dozen instructions where a full fp64 exp2 costs about
+// fifty, once per row per wave.  Exponents at or below -120 (2^r within reach of fp32's
+// subnormals, or -inf logits) take the fp64 exp2.
+__device__ __forceinline__ double exp2_diff(float z, float m, float c) {
+  const double r = (static_cast<double>(z) - static_cast<double>(m)) * static_cast<double>(c);
+  const float rh = static_cast<float>(r);
+  if (!(rh > -120.f)) return exp2(r);
+  const double rl = r - static_cast<double>(rh);
+  return static_cast<double>(__builtin_amdgcn_exp2f(rh)) * fma(rl, 0x1.62e42fefa39efp-1, 1.0);
 }
 
 struct RowStat {
@@ -254,7 +281,7 @@ __device__ __forceinline__ float token_value(const float (&z)[kQ][4], int t, int
   return Grp<kG>::at_f(v, base, l);
 }
 
-template <typename LT, int kQ, int kG, bool kVec, bool kMatch>
+template <typename LT, int kQ, int kG, int kR, bool kVec, bool kMatch>
 __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const uint8_t* __restrict__ onehot, const int32_t* __restrict__ proposed,
@@ -273,10 +300,20 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   const long long row0 = static_cast<long long>(b) * (K + 1);
   const LT* zrow0 = logits + row0 * V;
 
-  // Everything that does not depend on another load goes out first: row 0, the draft count,
-  // the temperature, the drafted ids (group lane i: slot i) and the uniforms (column i).
+  // Everything that does not depend on another load goes out first: row 0 (kR > 0: rows 0..K,
+  // whatever k_b is), the draft count, the temperature, the drafted ids (group lane i: slot i)
+  // and the uniforms (column i).
+  static_assert(kR == 0 || kQ == 1, "rows held at once only for one quad per lane");
   float zc[kQ][4];
-  load_row<LT, kQ, kG, kVec>(zrow0, V, gl, zc);
+  float zr[kR > 0 ? kR : 1][kQ][4];
+  if constexpr (kR > 0) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r)  // (masked where used)
+      if (r <= K)
+        load_row_raw<LT, kQ, kG, kVec>(zrow0 + static_cast<long long>(r) * V, V, gl, zr[r]);
+  } else {
+    load_row<LT, kQ, kG, kVec>(zrow0, V, gl, zc);
+  }
   const int kb_raw = num_draft != nullptr ? num_draft[b] : K;
   const float T = (greedy_all || temperature == nullptr) ? 0.f : temperature[b];
   const int x_lane = (K > 0 && gl < K) ? proposed[static_cast<long long>(b) * K + gl] : -1;
@@ -307,11 +344,12 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     if (model && kb > 0 && draft_probs == nullptr) ok = false;
   }
 
-  // Rows 0..k_b: reduce each, decide each drafted slot, keep the row to draw from.  The next
-  // row's loads are in flight while the current one is reduced.  The loop runs to the largest
-  // k_b of the wave; a group past its own k_b (or invalid) recomputes its last row and changes
-  // nothing.  (Deeper prefetch -- groups of rows in flight -- measured slower: the extra
-  // registers cost more occupancy than the round trips they save.)
+  // Rows 0..k_b: reduce each, decide each drafted slot, keep the row to draw from.  With kR = 0
+  // the next row's loads are in flight while the current one is reduced; with kR > 0 (K < kR)
+  // every row was loaded at the start.  Rows run to the largest k_b of the wave; a group past
+  // its own k_b (or invalid) changes nothing.  (On whole-wave groups, deeper prefetch -- groups
+  // of rows in flight -- measured slower: the extra registers cost more occupancy than the
+  // round trips they save.)
   int kb_wave = kb;
   if constexpr (kG < 64) kb_wave = -Grp<64>::min_i(-kb);  // the largest k_b of the wave
   int A = kb;                 // first rejected slot (k_b: every draft accepted)
@@ -322,19 +360,15 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     for (int e = 0; e < 4; ++e) zs[j][e] = -INFINITY;
   RowStat sA{0.f, 1.f, INT_MAX};
   double num_lane = 0.0, den_lane = 1.0;  // slot gl's output probability num / den
-  for (int i = 0; i <= kb_wave; ++i) {     // wave-uniform
+  auto visit = [&](int i, const float (&z)[kQ][4]) {
     const bool act = ok && i <= kb;
-    float zn[kQ][4];
-    if (i < kb_wave)  // the next row of this sequence (its last one again past k_b)
-      load_row<LT, kQ, kG, kVec>(zrow0 + static_cast<long long>(min(i + 1, kb)) * V, V, gl, zn);
-    const RowStat st = reduce_row<kQ, kG>(zc, c, gl, base);
+    const RowStat st = reduce_row<kQ, kG>(z, c, gl, base);
     if (act && !(st.s > 0.f)) ok = false;
     const bool decide = act && ok && i < kb && A == kb;
     const int slot = min(i, K > 0 ? K - 1 : 0);
     const int x = Grp<kG>::at_i(x_lane, base, slot);
     const int xt = min(max(x, 0), V - 1);
-    const double ex = exp2((static_cast<double>(token_value<kQ, kG>(zc, xt, base)) -
-                            static_cast<double>(st.m)) * static_cast<double>(c));
+    const double ex = exp2_diff(token_value<kQ, kG>(z, xt, base), st.m, c);
     bool acc;
     double den = static_cast<double>(st.s);
     if (greedy) {
@@ -342,7 +376,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     } else if constexpr (kMatch) {
       // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
       double S, P;
-      match_sums<kQ, kG>(zc, st.m, c, xt, gl, base, S, P);
+      match_sums<kQ, kG>(z, st.m, c, xt, gl, base, S, P);
       const double t = static_cast<double>(Grp<kG>::at_f(u_lane, base, slot)) * S;
       acc = P <= t && t < P + ex;
       den = S;
@@ -363,13 +397,29 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
 #pragma unroll
       for (int j = 0; j < kQ; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zs[j][e] = zc[j][e];
+        for (int e = 0; e < 4; ++e) zs[j][e] = z[j][e];
     }
-    if (i < kb_wave) {
+  };
+  if constexpr (kR > 0) {
 #pragma unroll
-      for (int j = 0; j < kQ; ++j)
+    for (int i = 0; i < kR; ++i)
+      if (i <= kb_wave) {  // wave-uniform
+        mask_row<kQ, kG>(V, gl, zr[i]);
+        visit(i, zr[i]);
+      }
+  } else {
+    for (int i = 0; i <= kb_wave; ++i) {  // wave-uniform
+      float zn[kQ][4];
+      if (i < kb_wave)  // the next row of this sequence (its last one again past k_b)
+        load_row<LT, kQ, kG, kVec>(zrow0 + static_cast<long long>(min(i + 1, kb)) * V, V, gl,
+                                   zn);
+      visit(i, zc);
+      if (i < kb_wave) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zc[j][e] = zn[j][e];
+        for (int j = 0; j < kQ; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zc[j][e] = zn[j][e];
+      }
     }
   }
 
@@ -489,7 +539,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     } else if (gl == A) {
       tok_lane = yt;
       prob_lane = static_cast<float>(
-          exp2((static_cast<double>(zyt) - static_cast<double>(sA.m)) * static_cast<double>(c)) /
+          exp2_diff(zyt, sA.m, c) /
           static_cast<double>(sA.s));
     }
   }
@@ -500,15 +550,15 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   if (live && gl == 0) accept_len[b] = ok ? A : -1;
 }
 
-template <typename LT, int kQ, int kG>
+template <typename LT, int kQ, int kG, int kR = 0>
 hipError_t launch_q(const LaunchArgs& a, bool vec, bool q_vec) {
   const LT* z = static_cast<const LT*>(a.logits);
   constexpr int kPerBlock = kSmallWaves * (64 / kG);  // sequences per workgroup
   const unsigned grid = static_cast<unsigned>((a.B + kPerBlock - 1) / kPerBlock);
-  auto k = a.match ? (vec ? small_verify_kernel<LT, kQ, kG, true, true>
-                          : small_verify_kernel<LT, kQ, kG, false, true>)
-                   : (vec ? small_verify_kernel<LT, kQ, kG, true, false>
-                          : small_verify_kernel<LT, kQ, kG, false, false>);
+  auto k = a.match ? (vec ? small_verify_kernel<LT, kQ, kG, kR, true, true>
+                          : small_verify_kernel<LT, kQ, kG, kR, false, true>)
+                   : (vec ? small_verify_kernel<LT, kQ, kG, kR, true, false>
+                          : small_verify_kernel<LT, kQ, kG, kR, false, false>);
   if (a.hot_begin || a.hot_end)
     hipExtLaunchKernelGGL(k, dim3(grid), dim3(64 * kSmallWaves), 0, a.stream, a.hot_begin,
                           a.hot_end, 0, z, a.draft_probs, a.onehot, a.proposed, a.num_draft,
@@ -529,8 +579,10 @@ hipError_t launch_small_typed(const LaunchArgs& a) {
   const bool q_vec = a.V % 4 == 0 && (a.draft_probs == nullptr ||
                                       reinterpret_cast<uintptr_t>(a.draft_probs) % 16 == 0);
   const int quads = (a.V + 3) / 4;  // at most 256: V <= kSmallVMax
-  if (quads <= 8 && a.K < 8) return launch_q<LT, 1, 8>(a, vec, q_vec);     // 8 sequences/wave
-  if (quads <= 16 && a.K < 16) return launch_q<LT, 1, 16>(a, vec, q_vec);  // 4 sequences/wave
+  // Eight or four sequences per wave; with K < 8 every row of a sequence is loaded at once.
+  if (quads <= 8 && a.K < 8) return launch_q<LT, 1, 8, 8>(a, vec, q_vec);
+  if (quads <= 16 && a.K < 8) return launch_q<LT, 1, 16, 8>(a, vec, q_vec);
+  if (quads <= 16 && a.K < 16) return launch_q<LT, 1, 16>(a, vec, q_vec);
   if (quads <= 64) return launch_q<LT, 1, 64>(a, vec, q_vec);
   if (quads <= 128) return launch_q<LT, 2, 64>(a, vec, q_vec);
   return launch_q<LT, 4, 64>(a, vec, q_vec);
