@@ -165,6 +165,7 @@ __device__ __forceinline__ void load_row_raw(const LT* __restrict__ row, int V, 
 
 template <int kQ, int kG>
 __device__ __forceinline__ void mask_row(int V, int gl, float (&z)[kQ][4]) {
+  if (V == kQ * kG * 4) return;  // every lane's tokens are in the row
 #pragma unroll
   for (int j = 0; j < kQ; ++j)
 #pragma unroll
@@ -219,7 +220,8 @@ struct RowStat {
 // streaming kernel), then the lowest argmax.  NaN / +inf logits make s NaN and an all -inf row
 // gives s = 0: both fail the caller's s > 0 check.
 template <int kQ, int kG>
-__device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, int gl, int base) {
+__device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, bool argmax,
+                                              int gl, int base) {
   float lm = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kQ; ++j)
@@ -234,15 +236,19 @@ __device__ __forceinline__ RowStat reduce_row(const float (&z)[kQ][4], float c, 
   for (int j = 0; j < kQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) ls += __builtin_amdgcn_exp2f(fmaf(z[j][e], c, -hi));
-  int a = INT_MAX;
-  if (lm == M) {
+  RowStat r{M, Grp<kG>::sum_f(ls, base) * __builtin_amdgcn_exp2f(-lo), INT_MAX};
+  if (argmax) {  // wave-uniform: some group of the wave is greedy
+    int a = INT_MAX;
+    if (lm == M) {
 #pragma unroll
-    for (int j = kQ - 1; j >= 0; --j)
+      for (int j = kQ - 1; j >= 0; --j)
 #pragma unroll
-      for (int e = 3; e >= 0; --e)
-        if (z[j][e] == M) a = (j * kG + gl) * 4 + e;
+        for (int e = 3; e >= 0; --e)
+          if (z[j][e] == M) a = (j * kG + gl) * 4 + e;
+    }
+    r.a = Grp<kG>::min_i(a);
   }
-  return RowStat{M, Grp<kG>::sum_f(ls, base) * __builtin_amdgcn_exp2f(-lo), Grp<kG>::min_i(a)};
+  return r;
 }
 
 // Match mode: the row's total S and the sum P below token x, both in fp64 from the same
@@ -352,6 +358,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   // round trips they save.)
   int kb_wave = kb;
   if constexpr (kG < 64) kb_wave = -Grp<64>::min_i(-kb);  // the largest k_b of the wave
+  const bool any_greedy = __ballot(greedy) != 0ull;        // rows need their argmax
   int A = kb;                 // first rejected slot (k_b: every draft accepted)
   float zs[kQ][4];            // row A's logits
 #pragma unroll
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   double num_lane = 0.0, den_lane = 1.0;  // slot gl's output probability num / den
   auto visit = [&](int i, const float (&z)[kQ][4]) {
     const bool act = ok && i <= kb;
-    const RowStat st = reduce_row<kQ, kG>(z, c, gl, base);
+    const RowStat st = reduce_row<kQ, kG>(z, c, any_greedy, gl, base);
     if (act && !(st.s > 0.f)) ok = false;
     const bool decide = act && ok && i < kb && A == kb;
     const int slot = min(i, K > 0 ? K - 1 : 0);
