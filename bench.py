@@ -364,7 +364,7 @@ def main():
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the large-batch and ragged workloads")
     ap.add_argument("--small-vocab-only", action="store_true",
-                    help="only the one-wave-path workloads (tiny vocabulary call, one-round "
+                    help="only the small-vocabulary-path workloads (tiny vocabulary call, one-round "
                          "latency): for profiling that kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB (counter calibration)")
@@ -563,7 +563,7 @@ def main():
         res["other_workloads"]["tiny_vocab"] = bench_workload(
             dev, stream, tiny_vocab(),
             "B=100000 rounds of one sequence, k=4, V=32, fp32 logits ~N(0,2^2), q = softmax of "
-            "logits + N(0,1), T=1: one call (one wave per sequence)", steps=100)
+            "logits + N(0,1), T=1: one call (eight sequences per wave)", steps=100)
         print("[bench] batch, calibrated drafter", file=sys.stderr, flush=True)
         res["other_workloads"]["batch64_calibrated"] = bench_workload(
             dev, stream, batch64(calibrated=True),

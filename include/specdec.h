@@ -128,11 +128,12 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Execution paths.  Rows of at most SPECDEC_SMALL_V_MAX tokens fit one wavefront's registers,
- * so by default such calls run one kernel with one wave64 per sequence (every row read once,
+ * so by default such calls run one kernel in which a group of lanes handles each sequence (a
+ * whole wave64, or 16 or 8 lanes of one for rows of at most 64 or 32 tokens; every row read once,
  * the draw taken from registers); larger vocabularies run the streaming kernels (one 256-thread
  * workgroup per 8192-logit chunk of each row, then the accept scan and draw, then the pick).
  * Both paths implement the same rule and pass the same parity tests; SPECDEC_PATH_STREAMING
- * forces the streaming kernels at any V, SPECDEC_PATH_SMALL_VOCAB the one-wave path (an error,
+ * forces the streaming kernels at any V, SPECDEC_PATH_SMALL_VOCAB the small-vocabulary kernel (an error,
  * SPECDEC_ERR_SHAPE, when V > SPECDEC_SMALL_V_MAX).  specdec_verify_greedy and
  * specdec_verify_match take the automatic choice. */
 #define SPECDEC_SMALL_V_MAX 1024
@@ -143,7 +144,7 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
 /* Options of specdec_verify_ex.
  *   hot_event_begin / hot_event_end: measurement hook, HIP events (hipEvent_t, host handles)
  *     recorded by the dispatch of the kernel that reads every target row (the streaming
- *     logit-row kernel, or the one-wave kernel on that path) when it starts and when it
+ *     logit-row kernel, or the small-vocabulary kernel on that path) when it starts and when it
  *     completes, so hipEventElapsedTime gives that kernel's own duration.  Either may be NULL.
  *   path: one of SPECDEC_PATH_*; any other value is SPECDEC_ERR_SHAPE.
  * Passing opts == NULL to specdec_verify_ex is the same as specdec_verify (path AUTO). */

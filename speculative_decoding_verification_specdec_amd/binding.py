@@ -164,8 +164,8 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     (accept_len [B] int32, out_tokens [B, K+1] int32, out_probs [B, K+1] fp32 or None),
     enqueued on ``stream`` (default: torch's current stream) without synchronising.
     ``hot_events``: optional (begin, end) pair of hipEvent_t handles (ints) recorded around the
-    kernel that reads every target row.  ``path``: SPECDEC_PATH_AUTO (one wave per sequence when
-    V <= SPECDEC_SMALL_V_MAX, else the streaming kernels), _STREAMING or _SMALL_VOCAB."""
+    kernel that reads every target row.  ``path``: SPECDEC_PATH_AUTO (the one-kernel small-vocabulary
+    path when V <= SPECDEC_SMALL_V_MAX, else the streaming kernels), _STREAMING or _SMALL_VOCAB."""
     lib = load_library()
     if target_logits.dim() != 3:
         raise SpecdecError("target_logits must be [B, K+1, V]")

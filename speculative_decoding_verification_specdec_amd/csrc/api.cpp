@@ -7,7 +7,7 @@
 #include "kernels.h"
 #include "specdec.h"
 
-static_assert(SPECDEC_SMALL_V_MAX == specdec::kSmallVMax, "one-wave path limit");
+static_assert(SPECDEC_SMALL_V_MAX == specdec::kSmallVMax, "small-vocabulary path limit");
 
 namespace {
 

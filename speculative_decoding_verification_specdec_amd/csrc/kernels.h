@@ -94,10 +94,10 @@ struct LaunchArgs {
   hipStream_t stream;
   hipEvent_t hot_begin;      // optional, recorded around the streaming (or small-vocabulary)
   hipEvent_t hot_end;        // kernel
-  int path;                  // 0: automatic, 1: streaming kernels, 2: one wave per sequence
+  int path;                  // 0: automatic, 1: streaming kernels, 2: small-vocabulary kernel
 };
 
-// Largest vocabulary the one-wave-per-sequence path takes (four 4-token quads per lane).
+// Largest vocabulary the small-vocabulary path takes (four 4-token quads per lane of a wave).
 constexpr int kSmallVMax = 1024;
 
 hipError_t launch_verify(const LaunchArgs& a);

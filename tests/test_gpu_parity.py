@@ -86,7 +86,7 @@ def test_parity_small(name):
     check(SMALL[name]())
 
 
-# The cases with V <= SPECDEC_SMALL_V_MAX take the one-wave path by default; the streaming
+# The cases with V <= SPECDEC_SMALL_V_MAX take the small-vocabulary path by default; the streaming
 # kernels must give the oracle's results on them too.
 @pytest.mark.parametrize("name", ["tiny_vocab_20k", "one_chunk", "vocab_of_one", "max_K"])
 def test_parity_small_vocab_cases_on_the_streaming_path(name):

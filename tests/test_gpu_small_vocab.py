@@ -1,4 +1,4 @@
-"""GPU parity of the one-wave-per-sequence path (V <= SPECDEC_SMALL_V_MAX) against the oracle.
+"""GPU parity of the small-vocabulary path (V <= SPECDEC_SMALL_V_MAX) against the oracle.
 
 Rows of at most 1024 tokens take that path by default; every case here also runs on the
 streaming kernels (SPECDEC_PATH_STREAMING), so both paths are held to the same bar: accept
@@ -95,7 +95,7 @@ def test_small_vocab_parity_both_paths(name):
     a0 = check(inp, SPECDEC_PATH_AUTO, ref)
     a1 = check(inp, SPECDEC_PATH_SMALL_VOCAB, ref)
     check(inp, SPECDEC_PATH_STREAMING, ref)
-    for x, y in zip(a0, a1):  # AUTO is the one-wave path here
+    for x, y in zip(a0, a1):  # AUTO is the small-vocabulary path here
         assert np.array_equal(x, y)
 
 
@@ -128,7 +128,7 @@ def test_small_vocab_invalid_rows_are_poisoned_alone(path, V):
     assert (acc[list(bad)] == -1).all() and (acc[[11]] >= 0).all()
 
 
-def test_greedy_entry_point_on_the_one_wave_path():
+def test_greedy_entry_point_on_the_small_vocab_path():
     inp = gen.make_batch(40, 6, 900, seed=312, greedy_frac=1.0, ragged=True)
     d = inputs_to_device(inp, DEV)
     acc, tok, prb = specdec_verify_greedy(d["logits"], d["proposed"], num_draft=d["num_draft"])
@@ -138,7 +138,7 @@ def test_greedy_entry_point_on_the_one_wave_path():
     assert rep["mismatch"] == 0 and rep["boundary"] == 0, rep
 
 
-def test_one_wave_path_rejects_a_large_vocabulary():
+def test_small_vocab_path_rejects_a_large_vocabulary():
     inp = gen.make_batch(2, 2, SPECDEC_SMALL_V_MAX + 1, seed=313)
     with pytest.raises(SpecdecError):
         run(inp, SPECDEC_PATH_SMALL_VOCAB)
@@ -152,7 +152,7 @@ MATCH_CASES = ["V1_f32", "V255_f32_mixed_ragged", "V257_bf16_calibrated", "V1000
 
 @pytest.mark.parametrize("name", MATCH_CASES)
 def test_small_vocab_match_mode_parity(name):
-    # Sample-and-match on the one-wave path (the automatic choice at these vocabularies).
+    # Sample-and-match on the small-vocabulary path (the automatic choice at these vocabularies).
     inp = CASES[name]()
     print(f"\n[case] match {inp.name} B={inp.B} K={inp.K} V={inp.V}", flush=True)
     d = inputs_to_device(inp, DEV)
