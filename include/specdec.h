@@ -42,9 +42,10 @@
  *     outside [0, V); for a sampled row a used uniform (columns < k_b and column K) is
  *     outside [0, 1); or for a sampled model-draft row a gathered q_i(x_i) is negative or
  *     not finite, or draft_probs is NULL.
- *   - Padded rows and slots never influence a result: logit rows k_b+1..K and draft rows
- *     k_b..K-1 are never read; proposed and uniform columns k_b..K-1 may be loaded (they lie
- *     inside the [B, K] and [B, K+1] buffers) but their values, NaN included, are ignored.
+ *   - Padded rows and slots never influence a result: draft rows k_b..K-1 are never read;
+ *     logit rows k_b+1..K (the small-vocabulary path loads rows 0..K together when K < 8) and
+ *     proposed and uniform columns k_b..K-1 may be loaded (they lie inside the [B, K+1, V],
+ *     [B, K] and [B, K+1] buffers) but their values, NaN included, are ignored.
  *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
  */
 #ifndef SPECDEC_H_
