@@ -1092,8 +1092,8 @@ WorkspaceLayout workspace_layout(int B, int K, int V) {
 }
 
 hipError_t launch_verify(const LaunchArgs& a) {
-  // Rows of at most kSmallVMax tokens fit one wave's registers: one kernel, one wave per
-  // sequence (small.hip), unless the streaming kernels are asked for.
+  // Rows of at most kSmallVMax tokens fit one wave's registers: one kernel, a group of lanes
+  // per sequence (small.hip), unless the streaming kernels are asked for.
   const bool small = a.V <= kSmallVMax && a.path != 1;
   if (small) return launch_small_verify(a);
   return a.logits_bf16 ? launch_typed<uint16_t>(a) : launch_typed<float>(a);

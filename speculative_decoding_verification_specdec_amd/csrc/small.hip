@@ -545,9 +545,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
       prob_lane = static_cast<float>(1.0 / static_cast<double>(sA.s));
     } else if (gl == A) {
       tok_lane = yt;
-      prob_lane = static_cast<float>(
-          exp2_diff(zyt, sA.m, c) /
-          static_cast<double>(sA.s));
+      prob_lane = static_cast<float>(exp2_diff(zyt, sA.m, c) / static_cast<double>(sA.s));
     }
   }
   if (live && gl <= K) {
