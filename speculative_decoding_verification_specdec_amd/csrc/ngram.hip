@@ -13,11 +13,11 @@
 // that occurs is N = max_e m(e) and its earliest occurrence ends at the smallest e with
 // m(e) = N.  Both fall out of one max-reduction of the key (m(e) << 32) | (2^32 - 1 - e).
 //
-// No atomics.  ngram_match_kernel runs one 512-thread workgroup per (8192-position tile,
-// sequence): the tile and a 32-token halo are staged in LDS with 16-byte loads (33 KB: four
-// workgroups fit a CU).  Each thread first tests its 16 positions (consecutive threads on
-// consecutive positions) for h[e-1] == h[L-1] with independent LDS reads, then extends only
-// those candidates, and the workgroup max-reduces the keys.  When one tile covers the whole history capacity the same
+// No atomics.  ngram_match_kernel runs one 512-thread workgroup per (8192-position tile, sequence):
+// the tile and a 32-token halo are staged in LDS with 16-byte loads (33 KB: four workgroups fit a
+// CU).  Each thread first tests its 16 positions (consecutive threads on consecutive positions) for
+// h[e-1] == h[L-1] with independent LDS reads, then extends only those candidates, and the
+// workgroup max-reduces the keys.  When one tile covers the whole history capacity the same
 // workgroup emits the proposal straight from LDS; otherwise each tile writes its key and
 // ngram_emit_kernel (one wave per sequence) takes the max over tiles and copies the proposal.
 #include <hip/hip_runtime.h>
@@ -156,8 +156,10 @@ __global__ __launch_bounds__(kEmitThreads) void ngram_emit_kernel(
     int K, int ntiles, const unsigned long long* __restrict__ partials,
     int32_t* __restrict__ proposed, int32_t* __restrict__ num_draft) {
   const int lane = threadIdx.x & 63;
-  const int b = static_cast<int>(blockIdx.x) * (kEmitThreads / 64) + (threadIdx.x >> 6);
-  if (b >= B) return;
+  const long long bl =
+      static_cast<long long>(blockIdx.x) * (kEmitThreads / 64) + (threadIdx.x >> 6);
+  if (bl >= B) return;
+  const int b = static_cast<int>(bl);
   const int L = lengths[b];
   const bool valid = L >= 0 && L <= capacity;
   unsigned long long key = 0ull;

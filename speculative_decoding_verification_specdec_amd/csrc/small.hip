@@ -11,21 +11,22 @@
 // from p_i with u[b, i] is x_i, decided from the row total and the sum below x_i, and the first
 // mismatch (or the bonus) is a plain draw of p.
 //
-// When a row fits a wave's registers (V <= 1024: at most four 4-token quads per lane) a group of
-// kG lanes runs the whole round of one sequence: the whole wave (kG = 64), or, when a row is at
-// most 64 tokens and K < 16, each 16-lane DPP row of the wave (kG = 16: four sequences per
-// wave), or, for rows of at most 32 tokens and K < 8, each half row (kG = 8: eight per wave).  Quad q of a row sits in group lane q % kG, register q / kG, so every load instruction
-// reads contiguous spans.  The group reads rows 0..k_b once each (the next row's loads are in
-// flight while the current one is reduced), reduces each row's max, sum and lowest argmax with
-// DPP, takes the accept test of each drafted slot (group lane i <-> slot i) as it goes, keeps
-// the row to draw from in registers, and draws: fp64 group totals per register, the register
-// whose running total passes u * total, one fp64 group scan inside it, then the four tokens of
-// the hit lane's quad.  Every cross-lane operation stays within its group and sits under
-// branches that are uniform over the group, so each one sees its whole group active; the loop over rows runs to the
-// largest k_b of the wave (groups past their own k_b change nothing).  One launch, no
-// workspace and no inter-wave communication, where the streaming path would spend a 256-thread
-// workgroup and three launches on rows of at most 1024 tokens.  (Eight quads per lane would need
-// over 256 registers per lane: one wave per SIMD.)
+// When a row fits a wave's registers (V <= 1024: at most four 4-token quads per lane) a group of kG
+// lanes runs the whole round of one sequence: the whole wave (kG = 64), or, when a row is at most
+// 64 tokens and K < 16, each 16-lane DPP row of the wave (kG = 16: four sequences per wave), or,
+// for rows of at most 32 tokens and K < 8, each half row (kG = 8: eight per wave).  Quad q of a row
+// sits in group lane q % kG, register q / kG, so every load instruction reads contiguous spans. The
+// group reads rows 0..k_b once each (with K < 8 in groups of 8 or 16 lanes, rows 0..K all at once;
+// else the next row's loads are in flight while the current one is reduced), reduces each row's
+// max, sum and (in waves holding a greedy row) lowest argmax with DPP, takes the accept test of
+// each drafted slot (group lane i <-> slot i) as it goes, keeps the row to draw from in registers,
+// and draws: fp64 group totals per register, the register whose running total passes u * total, one
+// fp64 group scan inside it, then the four tokens of the hit lane's quad.  Every cross-lane
+// operation stays within its group and sits under branches that are uniform over the group, so each
+// one sees its whole group active; the loop over rows runs to the largest k_b of the wave (groups
+// past their own k_b change nothing).  One launch, no workspace and no inter-wave communication,
+// where the streaming path would spend a 256-thread workgroup and three launches on rows of at most
+// 1024 tokens.  (Eight quads per lane would need over 256 registers per lane: one wave per SIMD.)
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -297,12 +298,12 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     float* __restrict__ out_probs) {
   constexpr int kPerWave = 64 / kG;
   const int lane = threadIdx.x & 63, gl = lane & (kG - 1), base = lane & ~(kG - 1);
-  const int wave_seq = (static_cast<int>(blockIdx.x) * kSmallWaves +
-                        static_cast<int>(threadIdx.x >> 6)) * kPerWave;
+  const long long wave_seq = (static_cast<long long>(blockIdx.x) * kSmallWaves +
+                              static_cast<long long>(threadIdx.x >> 6)) * kPerWave;
   if (wave_seq >= B) return;  // whole wave
-  const int b_raw = wave_seq + lane / kG;
+  const long long b_raw = wave_seq + lane / kG;
   const bool live = b_raw < B;             // groups past the batch compute on sequence B - 1
-  const int b = live ? b_raw : B - 1;     // and write nothing
+  const int b = live ? static_cast<int>(b_raw) : B - 1;  // and write nothing
   const long long row0 = static_cast<long long>(b) * (K + 1);
   const LT* zrow0 = logits + row0 * V;
 

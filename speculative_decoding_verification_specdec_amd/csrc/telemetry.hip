@@ -94,8 +94,9 @@ __global__ __launch_bounds__(256) void apply_k_kernel(int32_t* __restrict__ num_
                                                       const int32_t* __restrict__ route,
                                                       const int32_t* __restrict__ k_table,
                                                       int B, int n_routes) {
-  const int b = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
-  if (b >= B) return;
+  const long long bl = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (bl >= B) return;
+  const int b = static_cast<int>(bl);
   // The route and the draft count are read together; the table read waits only for the route.
   const int r = route ? route[b] : 0;
   const int nd = num_draft[b];
