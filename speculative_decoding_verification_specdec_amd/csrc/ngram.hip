@@ -160,14 +160,15 @@ __global__ __launch_bounds__(kEmitThreads) void ngram_emit_kernel(
       static_cast<long long>(blockIdx.x) * (kEmitThreads / 64) + (threadIdx.x >> 6);
   if (bl >= B) return;
   const int b = static_cast<int>(bl);
+  // The length and the tile keys do not depend on each other: both go out before either is
+  // used (the match kernel wrote every tile's key, 0 for an invalid history).
   const int L = lengths[b];
-  const bool valid = L >= 0 && L <= capacity;
+  const unsigned long long* p = partials + static_cast<long long>(b) * ntiles;
   unsigned long long key = 0ull;
-  if (valid) {
-    const unsigned long long* p = partials + static_cast<long long>(b) * ntiles;
-    for (int t = lane; t < ntiles; t += 64) key = max_u64(key, p[t]);
-    key = wave_max_u64(key);
-  }
+  for (int t = lane; t < ntiles; t += 64) key = max_u64(key, p[t]);
+  key = wave_max_u64(key);
+  const bool valid = L >= 0 && L <= capacity;
+  if (!valid) key = 0ull;
   int e = 0;
   const int cnt = proposal_count(key, L, K, e);
   if (lane < K) {
