@@ -707,7 +707,9 @@ template <> struct DrawVec<float> {
 // wave 0 decides) and the chunk-0 workgroup writes the scan's outputs and the draw state; then
 // wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns 4-token quads
 // l, l + 64, ...), in fp64.  kPhase 1: the scan only (one workgroup per sequence).  kPhase 2:
-// the draw only, from the state kPhase 1 wrote.
+// the draw only, from the state kPhase 1 wrote.  kPhase 3: as kPhase 0, but one workgroup per
+// 2048-token segment, its four waves a quarter each (grids too small to fill the chip: a
+// workgroup alone pulls its bytes through one CU's few outstanding misses).
 // ------------------------------------------------------------------------------------------
 template <typename LT, bool kVec, bool kMatch, int kPhase>
 __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
@@ -718,8 +720,10 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const RowPartial* __restrict__ partials, const Gather* __restrict__ gathers,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs) {
-  constexpr int kGroupsPerLane = kSeg / kGroup / 64;  // 4 (scalar path)
+  constexpr bool kFine = kPhase == 3;
+  constexpr int kGroupsPerLane = kSeg / kGroup / 64 / (kFine ? kWaves : 1);  // scalar path
   __shared__ SeqState sh_st;
+  __shared__ SegSums sh_fine[kFine ? kWaves : 1];
   __shared__ Stat sh_rows[kMaxRows];
   __shared__ StatD sh_rows_d[kMatch ? kMaxRows : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -794,15 +798,20 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
   const float* q = st.mode == kResidual
                        ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
                        : nullptr;
-  const int seg0 = wave * kSeg;  // this wave's segment, relative to the chunk
-  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+  // Work item t: chunk t (kPhase 0, 2: wave w sums segment w) or segment t (kPhase 3: wave w
+  // sums quarter w of it, the quarters added in order in LDS).
+  const int nitems = kFine ? nseg : S;
+  const int span = kFine ? kSeg / kWaves : kSeg;  // tokens per wave
+  for (int t = blockIdx.x; t < nitems; t += gridDim.x) {
+    const int s = kFine ? t / kSegPerChunk : t;
+    const int seg0 = kFine ? (t % kSegPerChunk) * kSeg + wave * span : wave * kSeg;
     const int c0 = s * kChunk, n = min(kChunk, V - c0);
     double lw = 0.0, le = 0.0;
     if constexpr (kVec) {
-      // Lane l owns the 4-token quads l, l + 64, ... of the segment: every load instruction of
-      // the wave reads one contiguous span (4 logits, 8 or 16 bytes, and 4 fp32 draft
+      // Lane l owns the 4-token quads l, l + 64, ... of the wave's span: every load instruction
+      // of the wave reads one contiguous span (4 logits, 8 or 16 bytes, and 4 fp32 draft
       // probabilities, 16 bytes, per lane), and all of them go out before any is unpacked.
-      constexpr int kQuads = kSeg / 4 / 64;  // 8
+      constexpr int kQuads = kSeg / 4 / 64 / (kFine ? kWaves : 1);  // 8, or 2
       DrawVec<LT> zr[kQuads];
       uint4 qr[kQuads];
 #pragma unroll
@@ -843,8 +852,22 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     }
     lw = wave_total(lw);
     le = wave_total(le);
-    if (lane == 0)
+    if constexpr (kFine) {
+      if (lane == 0) sh_fine[wave] = SegSums{lw, le};
+      __syncthreads();
+      if (tid == 0) {
+        SegSums a = sh_fine[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+          a.w += sh_fine[w].w;
+          a.e += sh_fine[w].e;
+        }
+        segs[static_cast<long long>(b) * nseg + t] = a;
+      }
+      __syncthreads();  // sh_fine is reused by the next item
+    } else if (lane == 0) {
       segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
+    }
   }
 }
 
@@ -1036,20 +1059,25 @@ hipError_t launch_typed(const LaunchArgs& a) {
   auto accept_draw = [&](int phase) {
     return phase == 0   ? accept_draw_for<LT, 0>(match, vec_draw)
            : phase == 1 ? accept_draw_for<LT, 1>(match, vec_draw)
-                        : accept_draw_for<LT, 2>(match, vec_draw);
+           : phase == 2 ? accept_draw_for<LT, 2>(match, vec_draw)
+                        : accept_draw_for<LT, 3>(match, vec_draw);
   };
   // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
   // partials): the chunk-0 workgroups that run the scan are enough.
   // Otherwise one workgroup per chunk of the row to draw from.
   // A draw grid of more than one resident round (about six 256-thread workgroups per CU on 256
   // CUs) scans once per sequence in a separate pass instead.
+  // A draw grid smaller than the chip (up to 256 chunks) takes one workgroup per 2048-token
+  // segment instead of one per chunk.
   constexpr long long kDrawRound = 1536;
+  constexpr long long kFineMax = 256;
   const bool draws = !(a.greedy_all || match);
   const bool split = draws && static_cast<long long>(a.B) * S > kDrawRound;
-  const int phases[2] = {split ? 1 : 0, 2};
+  const bool fine = draws && static_cast<long long>(a.B) * S <= kFineMax;
+  const int phases[2] = {split ? 1 : (fine ? 3 : 0), 2};
   for (int ph = 0; ph < (split ? 2 : 1); ++ph) {
     const int phase = phases[ph];
-    const int gx = (phase == 1 || !draws) ? 1 : S;
+    const int gx = (phase == 1 || !draws) ? 1 : (phase == 3 ? S * kSegPerChunk : S);
     for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
       const dim3 grid(gx, min(kMaxZ, a.B - b0));
       accept_draw(phase)<<<grid, kThreads, 0, a.stream>>>(

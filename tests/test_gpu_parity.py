@@ -78,6 +78,10 @@ SMALL = {
     "bonus_peaked_rows": lambda: gen.make_batch(16, 5, 30011, seed=49, z_sigma=4.0,
                                                 boost_frac=0.01, boost=8.0, draft_scale=1.0,
                                                 draft_sigma=0.0, draft_at_row_temp=True),
+    # Draw grids of up to 256 chunks take one workgroup per 2048-token segment (every case
+    # above); these two, of 320 chunks, one per chunk, as the full-size batch does.
+    "chunk_per_workgroup": lambda: gen.batch64(B=40, V=60000),
+    "chunk_per_workgroup_ragged": lambda: gen.ragged_mixed(B=160, V=9000),
 }
 
 
