@@ -3,6 +3,7 @@ host-side arguments before touching the GPU (these calls return before any HIP c
 run without a GPU)."""
 import ctypes
 import os
+import pathlib
 import re
 
 import pytest
@@ -226,3 +227,23 @@ def test_apply_k_host_side_errors(lib):
     assert lib.specdec_apply_k(None, None, FAKE, 4, 2, None) == -1
     assert lib.specdec_apply_k(FAKE + 1, None, FAKE, 4, 2, None) == -4
     assert lib.specdec_apply_k(None, None, None, 0, 2, None) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # No CPU or PyTorch fallback: with the library absent the first call raises SpecdecError.
+    # A fresh interpreter, since this process has the library loaded already.
+    import subprocess
+    import sys
+    code = ("from speculative_decoding_verification_specdec_amd import SpecdecError, "
+            "specdec_workspace_size\n"
+            "try:\n"
+            "    specdec_workspace_size(4, 2, 100)\n"
+            "except SpecdecError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    raise SystemExit('no error')\n")
+    env = dict(os.environ, SPECDEC_LIBRARY=str(tmp_path / "libspecdec_absent.so"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=str(pathlib.Path(__file__).resolve().parents[1]), timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "raised:" in r.stdout and "missing" in r.stdout
