@@ -19,14 +19,15 @@
 // group reads rows 0..k_b once each (with K < 8 in groups of 8 or 16 lanes, rows 0..K all at once;
 // else the next row's loads are in flight while the current one is reduced), reduces each row's
 // max, sum and (in waves holding a greedy row) lowest argmax with DPP, takes the accept test of
-// each drafted slot (group lane i <-> slot i) as it goes, keeps the row to draw from in registers,
-// and draws: fp64 group totals per register, the register whose running total passes u * total, one
-// fp64 group scan inside it, then the four tokens of the hit lane's quad.  Every cross-lane
-// operation stays within its group and sits under branches that are uniform over the group, so each
-// one sees its whole group active; the loop over rows runs to the largest k_b of the wave (groups
-// past their own k_b change nothing).  One launch, no workspace and no inter-wave communication,
-// where the streaming path would spend a 256-thread workgroup and three launches on rows of at most
-// 1024 tokens.  (Eight quads per lane would need over 256 registers per lane: one wave per SIMD.)
+// each drafted slot (group lane i <-> slot i; with every row in registers all slots at once, after
+// the rows, z_i(x_i) gathered from memory), keeps the row to draw from in registers, and draws:
+// fp64 group totals per register, the register whose running total passes u * total, one fp64 group
+// scan inside it, then the four tokens of the hit lane's quad.  Every cross-lane operation stays
+// within its group and sits under branches that are uniform over the group, so each one sees its
+// whole group active; the loop over rows runs to the largest k_b of the wave (groups past their own
+// k_b change nothing).  One launch, no workspace and no inter-wave communication, where the
+// streaming path would spend a 256-thread workgroup and three launches on rows of at most 1024
+// tokens.  (Eight quads per lane would need over 256 registers per lane: one wave per SIMD.)
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -339,6 +340,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   const bool x_ok_lane = x_lane >= 0 && x_lane < V;
   if (seq_ok && model && draft_probs != nullptr && gl < kb && x_ok_lane)
     q_lane = draft_probs[(static_cast<long long>(b) * K + gl) * V + x_lane];
+  // With every row in registers (kR > 0) the slots are decided together, lane i taking slot i:
+  // z_i(x_i) is gathered here (row i was just loaded) instead of read out of the group's
+  // registers row by row.
+  float zx_lane = 0.f;
+  if constexpr (kR > 0) {
+    if (seq_ok && gl < kb && x_ok_lane)
+      zx_lane = QuadT<LT>::one(zrow0 + static_cast<long long>(gl) * V, x_lane);
+  }
 
   bool ok = seq_ok;
   {
@@ -409,11 +418,58 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     }
   };
   if constexpr (kR > 0) {
+    // Reduce every row, row i's statistics kept by group lane i; then every drafted slot is
+    // decided at once (the same tests as visit's) and the first rejection found by a ballot.
+    float m_lane = 0.f, s_lane = 1.f;
+    int a_lane = INT_MAX;
+    double S_lane = 1.0, P_lane = 0.0;
 #pragma unroll
     for (int i = 0; i < kR; ++i)
       if (i <= kb_wave) {  // wave-uniform
         mask_row<kQ, kG>(V, gl, zr[i]);
-        visit(i, zr[i]);
+        const RowStat st = reduce_row<kQ, kG>(zr[i], c, any_greedy, gl, base);
+        if (ok && i <= kb && !(st.s > 0.f)) ok = false;
+        if constexpr (kMatch) {
+          const int x = Grp<kG>::at_i(x_lane, base, min(i, K > 0 ? K - 1 : 0));
+          double S, P;
+          match_sums<kQ, kG>(zr[i], st.m, c, min(max(x, 0), V - 1), gl, base, S, P);
+          if (gl == i) {
+            S_lane = S;
+            P_lane = P;
+          }
+        }
+        if (gl == i) {
+          m_lane = st.m;
+          s_lane = st.s;
+          a_lane = st.a;
+        }
+      }
+    const double ex = exp2_diff(zx_lane, m_lane, c);
+    bool acc;
+    if (greedy) {
+      acc = x_lane == a_lane;
+    } else if constexpr (kMatch) {
+      // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
+      const double t = static_cast<double>(u_lane) * S_lane;
+      acc = P_lane <= t && t < P_lane + ex;
+    } else {
+      const double qx = model ? static_cast<double>(q_lane) : 1.0;
+      acc = static_cast<double>(u_lane) * qx * static_cast<double>(s_lane) < ex;
+    }
+    const unsigned long long rej = Grp<kG>::bits(__ballot(gl < kb && !acc), base);
+    A = rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb;
+    num_lane = ex;
+    den_lane = (kMatch && !greedy) ? S_lane : static_cast<double>(s_lane);
+    // The row to draw from: the first rejection, or the bonus row k_b.
+    sA = RowStat{Grp<kG>::at_f(m_lane, base, A), Grp<kG>::at_f(s_lane, base, A),
+                 Grp<kG>::at_i(a_lane, base, A)};
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+      if (r == A) {
+#pragma unroll
+        for (int j = 0; j < kQ; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zs[j][e] = zr[r][j][e];
       }
   } else {
     for (int i = 0; i <= kb_wave; ++i) {  // wave-uniform
