@@ -12,14 +12,14 @@
 //       issues its 2048-token sub-chunk's 16-byte loads first, reduces the wave max, then sums
 //       exp2((z - max) * log2(e)/T) against it and writes one (max, sum, lowest argmax)
 //       partial per wave; chunk 0 of each drafted row also gathers x_i, z_i[x_i] and q_i(x_i).
-//   accept_draw_kernel  one workgroup per (chunk of the row to draw from, sequence).  Every
-//       wave merges some rows' sub-chunk partials (16 lanes per row, max-first, DPP) and wave 0
-//       runs the sequence's accept scan (lane i <-> target row i, p_i(x_i) in fp64, a 64-bit
-//       ballot finds the first rejection); the chunk-0 workgroup emits every token already
-//       known (accepted drafts, greedy argmaxes) and records what remains to be drawn.  Then
-//       the workgroup sums the draw's weights -- s * max(0, p - q) or p without the rejected
-//       draft -- over each 2048-token segment of its chunk (fp64 DPP wave sums); a plain draw
-//       of p takes those sums from the streaming kernel's partials instead.
+//   accept_draw_kernel  one workgroup per (chunk of the row to draw from, sequence), or per
+//       2048-token segment when the grid is smaller than the chip.  Every wave merges some rows'
+//       sub-chunk partials (16 lanes per row, max-first, DPP) and wave 0 runs the sequence's accept
+//       scan (lane i <-> target row i, p_i(x_i) in fp64, a 64-bit ballot finds the first rejection);
+//       the chunk-0 workgroup emits every token already known (accepted drafts, greedy argmaxes) and
+//       records what remains to be drawn.  Then the workgroup sums the draw's weights -- s * max(0, p
+//       - q) or p without the rejected draft -- over each 2048-token segment of its chunk (fp64 DPP
+//       wave sums); a plain draw of p takes those sums from the streaming kernel's partials instead.
 //   pick_kernel  one workgroup per sequence that needs a draw: one fp64 DPP scan over the
 //       segment sums finds the segment holding u * total, then a scan of that one segment in
 //       ascending token order finds the first running sum above u * total.
