@@ -11,6 +11,7 @@ import ctypes
 import os
 import pathlib
 
+import numpy as np
 import torch
 
 _LIB = None
@@ -398,6 +399,8 @@ def inputs_to_device(inp, device) -> dict:
     def dev(a, dtype=None):
         if a is None:
             return None
+        if not a.flags.writeable:  # e.g. a broadcast view: torch wants a writable buffer
+            a = np.array(a)
         t = torch.from_numpy(a)
         if dtype is not None:
             t = t.view(dtype)
