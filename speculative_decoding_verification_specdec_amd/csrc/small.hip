@@ -197,21 +197,6 @@ __device__ __forceinline__ void load_q_row(const float* __restrict__ q, int V, i
   }
 }
 
-// 2^((z - m) * c) for one token, as a double good to a few parts in 1e7: the exponent r in fp64
-// (z - m is exact there), split as r = rh + rl with rh = (float)r, then 2^rh from the hardware
-// exp2 (about 1 ulp) times 2^rl = 1 + rl ln 2 (|rl| <= ulp(rh) / 2, so the next term is below
-// 1e-14).  The accept test and the emitted probabilities need no more (the sum it is compared
-// with is an fp32 sum), and this costs a dozen instructions where a full fp64 exp2 costs about
-// fifty, once per row per wave.  Exponents at or below -120 (2^r within reach of fp32's
-// subnormals, or -inf logits) take the fp64 exp2.
-__device__ __forceinline__ double exp2_diff(float z, float m, float c) {
-  const double r = (static_cast<double>(z) - static_cast<double>(m)) * static_cast<double>(c);
-  const float rh = static_cast<float>(r);
-  if (!(rh > -120.f)) return exp2(r);
-  const double rl = r - static_cast<double>(rh);
-  return static_cast<double>(__builtin_amdgcn_exp2f(rh)) * fma(rl, 0x1.62e42fefa39efp-1, 1.0);
-}
-
 struct RowStat {
   float m;  // row max
   float s;  // sum of exp2((z - m) * c)

@@ -1,8 +1,10 @@
-// Device building blocks shared by the gfx950 verify kernels: the temperature rules, and wave64
-// DPP reductions and scans within one wavefront (no LDS round trips) with uniform lane reads.
+// Device building blocks shared by the gfx950 verify kernels: the temperature rules, wave64 DPP
+// reductions and scans within one wavefront (no LDS round trips) with uniform lane reads, and the
+// probability weight 2^((z - m) * c) of one token in double precision.
 #pragma once
 
 #include <float.h>
+#include <math.h>
 
 #include <hip/hip_runtime.h>
 
@@ -87,6 +89,21 @@ __device__ __forceinline__ double wave_total(double v) {
 template <int kCtrl>
 __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+
+// 2^((z - m) * c) for one token, as a double good to a few parts in 1e7: the exponent r in fp64 (z
+// - m is exact there), split as r = rh + rl with rh = (float)r, then 2^rh from the hardware exp2
+// (about 1 ulp) times 2^rl = 1 + rl ln 2 (|rl| <= ulp(rh) / 2, so the next term is below 1e-14).
+// The accept tests and the emitted probabilities need no more (the sums it is compared with are
+// built from fp32 terms), and this costs a dozen instructions where a full fp64 exp2 costs about
+// fifty, on the path from the row statistics to the decisions.  Exponents at or below -120 (2^r
+// within reach of fp32's subnormals, or -inf logits) take the fp64 exp2.
+__device__ __forceinline__ double exp2_diff(float z, float m, float c) {
+  const double r = (static_cast<double>(z) - static_cast<double>(m)) * static_cast<double>(c);
+  const float rh = static_cast<float>(r);
+  if (!(rh > -120.f)) return exp2(r);
+  const double rl = r - static_cast<double>(rh);
+  return static_cast<double>(__builtin_amdgcn_exp2f(rh)) * fma(rl, 0x1.62e42fefa39efp-1, 1.0);
 }
 
 }  // namespace specdec
