@@ -43,13 +43,15 @@ def replay_and_check(graph, stream, outs, expected, perturb):
                 assert torch.equal(t, et), f"replay {r} differs from the eager call"
 
 
+# V = 20008: the streaming kernels; V = 32: the small-vocabulary kernel (eight sequences a wave).
+@pytest.mark.parametrize("V", [20008, 32])
 @pytest.mark.parametrize("match", [False, True])
-def test_verify_graph_replays_match_eager(match):
-    print(f"\n[case] graph verify match={match}", flush=True)
-    inps = [gen.make_batch(16, 5, 20008, seed=80 + i, greedy_frac=0.25, onehot_frac=0.25,
+def test_verify_graph_replays_match_eager(match, V):
+    print(f"\n[case] graph verify match={match} V={V}", flush=True)
+    inps = [gen.make_batch(16, 5, V, seed=80 + i, greedy_frac=0.25, onehot_frac=0.25,
                            ragged=True) for i in range(2)]
-    other = inputs_to_device(gen.make_batch(16, 5, 20008, seed=90), DEV)
-    B, K, V = 16, 5, 20008
+    other = inputs_to_device(gen.make_batch(16, 5, V, seed=90), DEV)
+    B, K = 16, 5
     ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=DEV)
     ds = [inputs_to_device(i, DEV) for i in inps]
 
