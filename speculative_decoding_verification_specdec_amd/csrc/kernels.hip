@@ -60,9 +60,16 @@ __device__ __forceinline__ void unpack(const uint4& d, float* o, const float*) {
   o[0] = __uint_as_float(d.x); o[1] = __uint_as_float(d.y);
   o[2] = __uint_as_float(d.z); o[3] = __uint_as_float(d.w);
 }
-// 16-byte streaming load: every logit and draft probability is read once per call, so the
-// loads carry the nontemporal hint.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Plain (cached) 16-byte load: the draw kernel's reads of the row to draw from, which the pick
+// kernel re-reads one segment of (nontemporal loads there measured 3-6 % slower on the large
+// and ragged batches).
+__device__ __forceinline__ uint4 plain_load(const void* p) {
+  const u32x4 t = *static_cast<const u32x4*>(p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+// 16-byte streaming load: the streaming kernel reads every logit once per call, so its loads
+// carry the nontemporal hint.
 __device__ __forceinline__ uint4 stream_load(const void* p) {
   const u32x4 t = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
@@ -676,13 +683,13 @@ __device__ __forceinline__ void group_weights(const float (&zv)[kGroup], const f
 }
 
 
-// Four consecutive logits as one nontemporal load: 8 bytes of bf16 or 16 bytes of fp32.
+// Four consecutive logits as one cached load: 8 bytes of bf16 or 16 bytes of fp32.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <typename LT> struct DrawVec;
 template <> struct DrawVec<uint16_t> {
   uint2 d;
   static __device__ __forceinline__ DrawVec load(const uint16_t* p) {
-    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    const u32x2 t = *reinterpret_cast<const u32x2*>(p);
     return DrawVec{make_uint2(t.x, t.y)};
   }
   static __device__ __forceinline__ DrawVec zero() { return DrawVec{make_uint2(0, 0)}; }
@@ -693,7 +700,7 @@ template <> struct DrawVec<uint16_t> {
 };
 template <> struct DrawVec<float> {
   uint4 d;
-  static __device__ __forceinline__ DrawVec load(const float* p) { return DrawVec{stream_load(p)}; }
+  static __device__ __forceinline__ DrawVec load(const float* p) { return DrawVec{plain_load(p)}; }
   static __device__ __forceinline__ DrawVec zero() { return DrawVec{make_uint4(0, 0, 0, 0)}; }
   __device__ __forceinline__ void unpack(float* o) const {
     o[0] = __uint_as_float(d.x); o[1] = __uint_as_float(d.y);
@@ -819,7 +826,7 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
         const int v0 = c0 + seg0 + (h * 64 + lane) * 4;
         const bool in = v0 < c0 + n;
         zr[h] = in ? DrawVec<LT>::load(z + v0) : DrawVec<LT>::zero();
-        qr[h] = (in && q != nullptr) ? stream_load(q + v0) : make_uint4(0, 0, 0, 0);
+        qr[h] = (in && q != nullptr) ? plain_load(q + v0) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int h = 0; h < kQuads; ++h) {
