@@ -82,14 +82,17 @@ __global__ __launch_bounds__(kNgThreads) void ngram_match_kernel(
       // reads h[0..3] (in the row: L >= 1 here) and is zeroed afterwards.
       constexpr int kVecs = (kNgHalo + kNgramTile) / 4;
       constexpr int kIters = (kVecs + kNgThreads - 1) / kNgThreads;
-      const int4* hv = reinterpret_cast<const int4*>(h);
+      // Each history token is read once per call (halos aside): nontemporal 16-byte loads.
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      const i32x4* hv = reinterpret_cast<const i32x4*>(h);
       int4 d[kIters];
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int v = tid + it * kNgThreads;
         const int idx = i0 + 4 * v;  // a multiple of 4; idx < L <= capacity keeps idx + 3 in the row
         const bool ok = v < kVecs && idx >= 0 && idx < L;
-        d[it] = hv[ok ? idx / 4 : 0];
+        const i32x4 t = __builtin_nontemporal_load(hv + (ok ? idx / 4 : 0));
+        d[it] = make_int4(t.x, t.y, t.z, t.w);
       }
       const int suf = h[L - min(max(tid, 1), nmax)];  // sh_suf[tid] for tid in [1, nmax]
       if (tid >= 1 && tid <= nmax) sh_suf[tid] = suf;
