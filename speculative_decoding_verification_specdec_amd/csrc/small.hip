@@ -16,18 +16,18 @@
 // 64 tokens and K < 16, each 16-lane DPP row of the wave (kG = 16: four sequences per wave), or,
 // for rows of at most 32 tokens and K < 8, each half row (kG = 8: eight per wave).  Quad q of a row
 // sits in group lane q % kG, register q / kG, so every load instruction reads contiguous spans. The
-// group reads rows 0..k_b once each (with K < 8 in groups of 8 or 16 lanes, rows 0..K all at once;
-// else the next row's loads are in flight while the current one is reduced), reduces each row's
-// max, sum and (in waves holding a greedy row) lowest argmax with DPP, takes the accept test of
-// each drafted slot (group lane i <-> slot i; with every row in registers all slots at once, after
-// the rows, z_i(x_i) gathered from memory), keeps the row to draw from in registers, and draws:
-// fp64 group totals per register, the register whose running total passes u * total, one fp64 group
-// scan inside it, then the four tokens of the hit lane's quad.  Every cross-lane operation stays
-// within its group and sits under branches that are uniform over the group, so each one sees its
-// whole group active; the loop over rows runs to the largest k_b of the wave (groups past their own
-// k_b change nothing).  One launch, no workspace and no inter-wave communication, where the
-// streaming path would spend a 256-thread workgroup and three launches on rows of at most 1024
-// tokens.  (Eight quads per lane would need over 256 registers per lane: one wave per SIMD.)
+// group reads rows 0..k_b once each (with K < 8 and at most two quads per lane, rows 0..K all at
+// once; else the next row's loads are in flight while the current one is reduced), reduces each
+// row's max, sum and (in waves holding a greedy row) lowest argmax with DPP, takes the accept test
+// of each drafted slot (group lane i <-> slot i; with every row in registers all slots at once,
+// after the rows, z_i(x_i) gathered from memory), keeps the row to draw from in registers, and
+// draws: fp64 group totals per register, the register whose running total passes u * total, one
+// fp64 group scan inside it, then the four tokens of the hit lane's quad.  Every cross-lane
+// operation stays within its group and sits under branches that are uniform over the group, so each
+// one sees its whole group active; the loop over rows runs to the largest k_b of the wave (groups
+// past their own k_b change nothing).  One launch, no workspace and no inter-wave communication,
+// where the streaming path would spend a 256-thread workgroup and three launches on rows of at most
+// 1024 tokens.  (Eight quads per lane would need over 256 registers per lane: one wave per SIMD.)
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   // Everything that does not depend on another load goes out first: row 0 (kR > 0: rows 0..K,
   // whatever k_b is), the draft count, the temperature, the drafted ids (group lane i: slot i)
   // and the uniforms (column i).
-  static_assert(kR == 0 || kQ == 1, "rows held at once only for one quad per lane");
+  static_assert(kR == 0 || kQ <= 2, "rows held at once only for one or two quads per lane");
   float zc[kQ][4];
   float zr[kR > 0 ? kR : 1][kQ][4];
   if constexpr (kR > 0) {
@@ -626,11 +626,14 @@ hipError_t launch_small_typed(const LaunchArgs& a) {
   const bool q_vec = a.V % 4 == 0 && (a.draft_probs == nullptr ||
                                       reinterpret_cast<uintptr_t>(a.draft_probs) % 16 == 0);
   const int quads = (a.V + 3) / 4;  // at most 256: V <= kSmallVMax
-  // Eight or four sequences per wave; with K < 8 every row of a sequence is loaded at once.
+  // Eight, four or one sequence per wave; with K < 8 and one or two quads per lane every row
+  // of a sequence is loaded at once (and its slots decided together).
   if (quads <= 8 && a.K < 8) return launch_q<LT, 1, 8, 8>(a, vec, q_vec);
   if (quads <= 16 && a.K < 8) return launch_q<LT, 1, 16, 8>(a, vec, q_vec);
   if (quads <= 16 && a.K < 16) return launch_q<LT, 1, 16>(a, vec, q_vec);
+  if (quads <= 64 && a.K < 8) return launch_q<LT, 1, 64, 8>(a, vec, q_vec);
   if (quads <= 64) return launch_q<LT, 1, 64>(a, vec, q_vec);
+  if (quads <= 128 && a.K < 8) return launch_q<LT, 2, 64, 8>(a, vec, q_vec);
   if (quads <= 128) return launch_q<LT, 2, 64>(a, vec, q_vec);
   return launch_q<LT, 4, 64>(a, vec, q_vec);
 }

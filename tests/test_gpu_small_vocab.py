@@ -4,7 +4,8 @@ Rows of at most 1024 tokens take that path by default; every case here also runs
 streaming kernels (SPECDEC_PATH_STREAMING), so both paths are held to the same bar: accept
 lengths and tokens bit-exact except on boundary rows, probabilities within 1e-5 relative.  The
 cases cover each register layout (eight sequences per wave for rows of at most 32 tokens and
-K < 8, four for rows of at most 64 tokens and K < 16; else 1, 2 and 4 quads per lane),
+K < 8, four for rows of at most 64 tokens and K < 16; else 1, 2 and 4 quads per lane; every
+row loaded at once for K < 8 and at most two quads per lane, else one row at a time),
 quad-aligned and unaligned vocabularies, both dtypes, greedy / one-hot / model-draft rows, ragged
 counts, batches that end inside a wave, K = 0, 7, 8, 15, 16 and 63, the bonus draw, and the
 invalid-row rules (also with valid and invalid sequences sharing a wave).
@@ -63,6 +64,9 @@ CASES = {
     "V32_bf16_many_sequences": lambda: gen.make_batch(4099, 4, 32, seed=319, onehot_frac=0.25,
                                                       ragged=True),
     "V32_f32_K8": lambda: gen.make_batch(21, 8, 32, seed=320, dtype="f32", ragged=True),
+    # Two quads per lane with K >= 8: rows one at a time (K < 8 loads them all at once).
+    "V400_bf16_K9_mixed": lambda: gen.make_batch(40, 9, 400, seed=321, greedy_frac=0.2,
+                                                 onehot_frac=0.3, ragged=True),
 }
 
 
@@ -147,7 +151,7 @@ def test_small_vocab_path_rejects_a_large_vocabulary():
 MATCH_CASES = ["V1_f32", "V255_f32_mixed_ragged", "V257_bf16_calibrated", "V1000_bf16_mixed_ragged",
                "V1024_f32_max_K", "K0", "V64_many_sequences", "V50_bf16_mixed_ragged_B7",
                "V64_f32_K15_ragged_B37", "V61_f32_calibrated_B1001", "V29_f32_mixed_ragged_B13",
-               "V32_bf16_many_sequences"]
+               "V32_bf16_many_sequences", "V400_bf16_K9_mixed"]
 
 
 @pytest.mark.parametrize("name", MATCH_CASES)
