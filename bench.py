@@ -404,8 +404,9 @@ def main():
         from speculative_decoding_verification_specdec_amd.inputs import tiny_vocab
         stream = torch.cuda.Stream()
         print(json.dumps({
-            "tiny_vocab": bench_workload(dev, stream, tiny_vocab(), "B=100000, k=4, V=32, fp32",
-                                         steps=100),
+            "tiny_vocab": bench_workload(dev, stream, tiny_vocab(),
+                                         "B=100000, k=4, V=32, fp32; 4 replicas rotated",
+                                         steps=100, replicas=4),
             "tiny_vocab_one_round": bench_workload(dev, stream, tiny_vocab(rounds=1),
                                                    "B=1, k=4, V=32, fp32", steps=400)}))
         return
@@ -563,7 +564,8 @@ def main():
         res["other_workloads"]["tiny_vocab"] = bench_workload(
             dev, stream, tiny_vocab(),
             "B=100000 rounds of one sequence, k=4, V=32, fp32 logits ~N(0,2^2), q = softmax of "
-            "logits + N(0,1), T=1: one call (eight sequences per wave)", steps=100)
+            "logits + N(0,1), T=1: one call (eight sequences per wave); 4 replicas rotated",
+            steps=100, replicas=4)
         print("[bench] batch, calibrated drafter", file=sys.stderr, flush=True)
         res["other_workloads"]["batch64_calibrated"] = bench_workload(
             dev, stream, batch64(calibrated=True),
