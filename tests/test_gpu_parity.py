@@ -66,6 +66,13 @@ SMALL = {
     "all_greedy": lambda: gen.make_batch(16, 6, 9001, seed=45, greedy_frac=1.0),
     "all_onehot": lambda: gen.make_batch(16, 6, 9000, seed=46, onehot_frac=1.0),
     "max_K": lambda: gen.make_batch(3, 63, 700, seed=47, draft_sigma=0.2, draft_at_row_temp=True),
+    "small_temperature_near_min": lambda: gen.make_batch(64, 4, 50, seed=54, dtype="f32",
+                                                         temp_range=(1e-6, 1e-5),
+                                                         draft_at_row_temp=True,
+                                                         onehot_frac=0.25),
+    "small_temperature_flat": lambda: gen.make_batch(64, 4, 300, seed=55,
+                                                     temp_range=(20.0, 100.0),
+                                                     draft_at_row_temp=True, onehot_frac=0.25),
     # 600,011 tokens: 74 chunks, 296 segments (several partials per accept-scan lane and
     # several segments per pick lane), with a ragged last chunk.
     "huge_vocab": lambda: gen.make_batch(3, 3, 600011, seed=50, draft_sigma=0.3,
@@ -82,6 +89,13 @@ SMALL = {
     # above); these two, of 320 chunks, one per chunk, as the full-size batch does.
     "chunk_per_workgroup": lambda: gen.batch64(B=40, V=60000),
     "chunk_per_workgroup_ragged": lambda: gen.ragged_mixed(B=160, V=9000),
+    # Temperatures at the extremes: just above the smallest valid one (each row's mass on a few
+    # tokens, exponents far beyond fp32 range for the rest) and very flat rows.
+    "temperature_near_min": lambda: gen.make_batch(16, 4, 20003, seed=52, dtype="f32",
+                                                   temp_range=(1e-6, 1e-5), draft_at_row_temp=True,
+                                                   onehot_frac=0.25),
+    "temperature_flat": lambda: gen.make_batch(16, 4, 20008, seed=53, temp_range=(20.0, 100.0),
+                                               draft_at_row_temp=True, onehot_frac=0.25),
 }
 
 
@@ -92,7 +106,8 @@ def test_parity_small(name):
 
 # The cases with V <= SPECDEC_SMALL_V_MAX take the small-vocabulary path by default; the streaming
 # kernels must give the oracle's results on them too.
-@pytest.mark.parametrize("name", ["tiny_vocab_20k", "one_chunk", "vocab_of_one", "max_K"])
+@pytest.mark.parametrize("name", ["tiny_vocab_20k", "one_chunk", "vocab_of_one", "max_K",
+                                  "small_temperature_near_min", "small_temperature_flat"])
 def test_parity_small_vocab_cases_on_the_streaming_path(name):
     inp = SMALL[name]()
     assert inp.V <= SPECDEC_SMALL_V_MAX
