@@ -222,3 +222,24 @@ def test_workspace_reuse_across_calls_and_shapes():
         rep = compare(inp, oracle.verify(inp), acc.cpu().numpy(), tok.cpu().numpy(),
                       prb.cpu().numpy())
         assert rep["mismatch"] == 0, rep["details"]
+
+
+@pytest.mark.parametrize("path", [SPECDEC_PATH_AUTO, SPECDEC_PATH_STREAMING])
+@pytest.mark.parametrize("V", [300, 20008])
+def test_zero_mass_drafts(V, path):
+    # Drafted tokens with no target mass (z = -inf: always rejected, and never drawn) or no draft
+    # mass (q(x) = 0: accepted whenever p(x) > 0), on the small-vocabulary path (V = 300, AUTO)
+    # and the streaming kernels.
+    inp = gen.make_batch(32, 4, V, seed=56, dtype="f32", onehot_frac=0.25)
+    L, Q, X = inp.logits, inp.draft_probs, inp.proposed
+    model = [b for b in range(inp.B) if not inp.draft_onehot[b]]
+    for b in range(0, inp.B, 3):                     # no target mass at x_0 (and x_1)
+        L[b, 0, X[b, 0]] = -np.inf
+        L[b, 1, X[b, 1]] = -np.inf
+    for b in model[1::2]:                            # no draft mass at x_0 .. x_2
+        for i in range(3):
+            Q[b, i, X[b, i]] = 0.0
+    check(inp, path=path)
+    acc, tok, _ = run_gpu(inp, path=path)
+    for b in range(0, inp.B, 3):
+        assert acc[b] == 0 and tok[b, 0] != X[b, 0]  # rejected at slot 0, x_0 not redrawn
