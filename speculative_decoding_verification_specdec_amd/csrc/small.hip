@@ -348,9 +348,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
   // Rows 0..k_b: reduce each, decide each drafted slot, keep the row to draw from.  With kR = 0
   // the next row's loads are in flight while the current one is reduced; with kR > 0 (K < kR)
   // every row was loaded at the start.  Rows run to the largest k_b of the wave; a group past
-  // its own k_b (or invalid) changes nothing.  (On whole-wave groups, deeper prefetch -- groups
-  // of rows in flight -- measured slower: the extra registers cost more occupancy than the
-  // round trips they save.)
+  // its own k_b (or invalid) changes nothing.  (In the rolling schedule, a deeper prefetch --
+  // several rows in flight with per-row decisions -- measured slower: its registers cost more
+  // occupancy than the round trips it saved.)
   int kb_wave = kb;
   if constexpr (kG < 64) kb_wave = -Grp<64>::min_i(-kb);  // the largest k_b of the wave
   const bool any_greedy = __ballot(greedy) != 0ull;        // rows need their argmax
@@ -362,6 +362,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     for (int e = 0; e < 4; ++e) zs[j][e] = -INFINITY;
   RowStat sA{0.f, 1.f, INT_MAX};
   double num_lane = 0.0, den_lane = 1.0;  // slot gl's output probability num / den
+  // The rolling schedule's step for row i: reduce it, decide slot i, and keep the row when it is
+  // the one to draw from.
   auto visit = [&](int i, const float (&z)[kQ][4]) {
     const bool act = ok && i <= kb;
     const RowStat st = reduce_row<kQ, kG>(z, c, any_greedy, gl, base);
