@@ -1,0 +1,53 @@
+"""GPU parity on seeded random shapes: batch size, draft length, vocabulary (both sides of the
+small-vocabulary limit), dtype and row mix drawn per case, each compared with the oracle on the
+default path and, for V <= SPECDEC_SMALL_V_MAX, on the streaming kernels too.  Same bar as the
+other parity tests (oracle/parity.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.parity import compare
+from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
+                                                           SPECDEC_PATH_STREAMING,
+                                                           SPECDEC_SMALL_V_MAX, inputs_to_device,
+                                                           specdec_verify)
+from speculative_decoding_verification_specdec_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+N_CASES = 64
+
+
+def case(seed):
+    g = np.random.default_rng(1000 + seed)
+    V = int(g.choice([int(g.integers(1, 70)), int(g.integers(70, 1025)),
+                      int(g.integers(1025, 30000))]))
+    K = int(g.integers(0, 13))
+    B = int(g.integers(1, max(2, min(200, 3_000_000 // ((K + 1) * V)))))
+    return gen.make_batch(B, K, V, seed=2000 + seed, dtype=str(g.choice(["bf16", "f32"])),
+                          greedy_frac=float(g.choice([0.0, 0.2, 1.0])),
+                          onehot_frac=float(g.choice([0.0, 0.3])),
+                          ragged=K > 0 and bool(g.integers(0, 2)),
+                          draft_at_row_temp=bool(g.integers(0, 2)),
+                          draft_sigma=float(g.choice([0.2, 1.5])))
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape_parity(seed):
+    inp = case(seed)
+    ref = oracle.verify(inp)
+    paths = [SPECDEC_PATH_AUTO] + ([SPECDEC_PATH_STREAMING] if inp.V <= SPECDEC_SMALL_V_MAX else [])
+    for path in paths:
+        print(f"\n[case] seed={seed} B={inp.B} K={inp.K} V={inp.V} {inp.logits_dtype} path={path}",
+              flush=True)
+        d = inputs_to_device(inp, DEV)
+        acc, tok, prb = specdec_verify(d["logits"], d["draft_probs"], d["proposed"],
+                                       d["temperature"], d["uniforms"],
+                                       draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
+                                       path=path)
+        torch.cuda.synchronize()
+        rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+        print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
+        assert rep["mismatch"] == 0, rep["details"]
+        assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
