@@ -1,7 +1,8 @@
 """GPU parity on seeded random shapes: batch size, draft length, vocabulary (both sides of the
 small-vocabulary limit), dtype and row mix drawn per case, each compared with the oracle on the
-default path and, for V <= SPECDEC_SMALL_V_MAX, on the streaming kernels too.  Same bar as the
-other parity tests (oracle/parity.py)."""
+default path and, for V <= SPECDEC_SMALL_V_MAX, on the streaming kernels too; every other case
+also through the sample-and-match entry point.  Same bar as the other parity tests
+(oracle/parity.py)."""
 import numpy as np
 import pytest
 import torch
@@ -51,3 +52,21 @@ def test_random_shape_parity(seed):
         print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
         assert rep["mismatch"] == 0, rep["details"]
         assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+
+
+@pytest.mark.parametrize("seed", range(0, N_CASES, 2))
+def test_random_shape_match_mode_parity(seed):
+    # The same shapes through the sample-and-match entry point (no draft distribution).
+    from speculative_decoding_verification_specdec_amd import specdec_verify_match
+    inp = case(seed)
+    ref = oracle.verify_match(inp)
+    print(f"\n[case] match seed={seed} B={inp.B} K={inp.K} V={inp.V} {inp.logits_dtype}",
+          flush=True)
+    d = inputs_to_device(inp, DEV)
+    acc, tok, prb = specdec_verify_match(d["logits"], d["proposed"], d["temperature"],
+                                         d["uniforms"], num_draft=d["num_draft"])
+    torch.cuda.synchronize()
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
+    assert rep["mismatch"] == 0, rep["details"]
+    assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
