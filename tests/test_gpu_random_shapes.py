@@ -1,8 +1,8 @@
 """GPU parity on seeded random shapes: batch size, draft length, vocabulary (both sides of the
 small-vocabulary limit), dtype and row mix drawn per case, each compared with the oracle on the
 default path and, for V <= SPECDEC_SMALL_V_MAX, on the streaming kernels too; every other case
-also through the sample-and-match entry point.  Same bar as the other parity tests
-(oracle/parity.py)."""
+also through the sample-and-match entry point and, the others, through the greedy entry point
+(every row at temperature 0, bit-exact).  Same bar as the other parity tests (oracle/parity.py)."""
 import numpy as np
 import pytest
 import torch
@@ -70,3 +70,19 @@ def test_random_shape_match_mode_parity(seed):
     print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
     assert rep["mismatch"] == 0, rep["details"]
     assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+
+
+@pytest.mark.parametrize("seed", range(1, N_CASES, 2))
+def test_random_shape_greedy_entry_point(seed):
+    # The same shapes through specdec_verify_greedy: every row at temperature 0, bit-exact.
+    from speculative_decoding_verification_specdec_amd import specdec_verify_greedy
+    inp = case(seed)
+    inp.temperature[:] = 0.0
+    ref = oracle.verify(inp)
+    print(f"\n[case] greedy seed={seed} B={inp.B} K={inp.K} V={inp.V} {inp.logits_dtype}",
+          flush=True)
+    d = inputs_to_device(inp, DEV)
+    acc, tok, prb = specdec_verify_greedy(d["logits"], d["proposed"], num_draft=d["num_draft"])
+    torch.cuda.synchronize()
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    assert rep["mismatch"] == 0 and rep["boundary"] == 0, rep
