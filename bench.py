@@ -276,7 +276,7 @@ def bench_workload(dev, stream, inp, description, steps=60, replicas=1):
                                                                specdec_workspace_size)
     from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
     B, K, V = inp.B, inp.K, inp.V
-    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
     calls = []
     for _ in range(replicas):
         d = inputs_to_device(inp, dev)
@@ -308,7 +308,7 @@ def bench_match(dev, stream, steps=300, replicas=6):
     from speculative_decoding_verification_specdec_amd.inputs import batch64
     inp = batch64()
     B, K, V = inp.B, inp.K, inp.V
-    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
     out = (torch.empty(B, dtype=torch.int32, device=dev),
            torch.empty((B, K + 1), dtype=torch.int32, device=dev),
            torch.empty((B, K + 1), dtype=torch.float32, device=dev))
@@ -357,6 +357,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["auto", "one_launch"], default="auto",
+                    help="streaming path of the headline call: the default three launches, or the "
+                         "one-launch alternative kept for comparison")
     ap.add_argument("--cpu-budget", type=float, default=6.0,
                     help="seconds of the single-thread oracle leg")
     ap.add_argument("--no-next-rows", action="store_true",
@@ -399,7 +402,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 20}))
         return
-    from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
+    from speculative_decoding_verification_specdec_amd.binding import (SPECDEC_PATH_AUTO,
+                                                                       SPECDEC_PATH_ONE_LAUNCH,
+                                                                       PreparedVerify)
+    path = SPECDEC_PATH_ONE_LAUNCH if args.path == "one_launch" else SPECDEC_PATH_AUTO
     if args.small_vocab_only:
         from speculative_decoding_verification_specdec_amd.inputs import tiny_vocab
         stream = torch.cuda.Stream()
@@ -424,7 +430,7 @@ def main():
         calls.append(PreparedVerify(d["logits"], d["draft_probs"], d["proposed"],
                                     d["temperature"], d["uniforms"],
                                     draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
-                                    out=(acc, tok, prb), workspace=ws))
+                                    out=(acc, tok, prb), workspace=ws, path=path))
     R = len(calls)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()

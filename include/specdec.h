@@ -77,12 +77,12 @@ typedef enum {
 #define SPECDEC_MAX_K 63                  /* drafts per sequence (K+1 rows fit one wave64) */
 #define SPECDEC_TEMPERATURE_MIN 1e-6f     /* smallest non-zero temperature accepted       */
 
-/* Bytes of device workspace specdec_verify / specdec_verify_greedy need for these sizes
- * (a pure function of B, K, V; 0 for B == 0 or invalid sizes).  The workspace holds
- * per-row partial statistics, the gathered drafted ids / logits / draft probabilities,
- * per-sequence draw state and per-segment weight sums; it needs
- * no initialisation and its contents are meaningless after the call.  Calls that overlap
- * in time (different streams) need separate workspaces. */
+/* Bytes of device workspace specdec_verify / specdec_verify_greedy / specdec_verify_match need
+ * for these sizes (a pure function of B, K, V; 0 for B == 0 or invalid sizes).  The workspace
+ * holds per-row partial statistics, the gathered drafted ids / logits / draft probabilities,
+ * per-sequence draw state and per-segment weight sums; it needs no initialisation and its
+ * contents are meaningless after the call.  Calls that overlap in time (different streams) need
+ * separate workspaces. */
 size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V);
 
 /* Batched rejection-sampling verify (sampled and greedy rows mixed by temperature).
@@ -131,16 +131,20 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
 /* Execution paths.  Rows of at most SPECDEC_SMALL_V_MAX tokens fit one wavefront's registers,
  * so by default such calls run one kernel in which a group of lanes handles each sequence (a
  * whole wave64, or 16 or 8 lanes of one for rows of at most 64 or 32 tokens; every row read once,
- * the draw taken from registers); larger vocabularies run the streaming kernels (one 256-thread
- * workgroup per 8192-logit chunk of each row, then the accept scan and draw, then the pick).
- * Both paths implement the same rule and pass the same parity tests; SPECDEC_PATH_STREAMING
- * forces the streaming kernels at any V, SPECDEC_PATH_SMALL_VOCAB the small-vocabulary kernel (an error,
- * SPECDEC_ERR_SHAPE, when V > SPECDEC_SMALL_V_MAX).  specdec_verify_greedy and
+ * the draw taken from registers); larger vocabularies run the streaming kernels (three launches:
+ * one 256-thread workgroup per 8192-logit chunk of each row, then the accept scan and draw, then
+ * the pick).  SPECDEC_PATH_STREAMING forces the streaming kernels at any V,
+ * SPECDEC_PATH_SMALL_VOCAB the small-vocabulary kernel (an error, SPECDEC_ERR_SHAPE, when
+ * V > SPECDEC_SMALL_V_MAX), and SPECDEC_PATH_ONE_LAUNCH the same streaming work in a single launch
+ * whose workgroups hand partial results to each other through the workspace (plus a small
+ * zero-fill launch before it); it is slower on MI355X and kept for comparison.  Every path
+ * implements the same rule and passes the same parity tests.  specdec_verify_greedy and
  * specdec_verify_match take the automatic choice. */
 #define SPECDEC_SMALL_V_MAX 1024
 #define SPECDEC_PATH_AUTO 0
 #define SPECDEC_PATH_STREAMING 1
 #define SPECDEC_PATH_SMALL_VOCAB 2
+#define SPECDEC_PATH_ONE_LAUNCH 3
 
 /* Options of specdec_verify_ex.
  *   hot_event_begin / hot_event_end: measurement hook, HIP events (hipEvent_t, host handles)
@@ -148,11 +152,17 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
  *     logit-row kernel, or the small-vocabulary kernel on that path) when it starts and when it
  *     completes, so hipEventElapsedTime gives that kernel's own duration.  Either may be NULL.
  *   path: one of SPECDEC_PATH_*; any other value is SPECDEC_ERR_SHAPE.
+ *   spin_limit: SPECDEC_PATH_ONE_LAUNCH only: polls a workgroup makes while it waits for a
+ *     hand-off from another workgroup of the launch (0 = the default, 2^20 polls, about a second;
+ *     negative = SPECDEC_ERR_SHAPE).  A wait that gives up reports its sequence as invalid
+ *     (accept_len -1) instead of waiting longer, so the launch always completes; a small limit
+ *     exercises that path in tests.
  * Passing opts == NULL to specdec_verify_ex is the same as specdec_verify (path AUTO). */
 typedef struct {
   void* hot_event_begin;
   void* hot_event_end;
   int32_t path;
+  int32_t spin_limit;
 } specdec_options;
 
 specdec_status specdec_verify_ex(const void* target_logits, int32_t logits_dtype,

@@ -7,6 +7,7 @@ CPU or PyTorch fallback, and a missing library raises ``SpecdecError``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import pathlib
@@ -27,18 +28,19 @@ class SpecdecError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("hot_event_begin", ctypes.c_void_p), ("hot_event_end", ctypes.c_void_p),
-                ("path", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("spin_limit", ctypes.c_int32)]
 
 
 # Execution paths of specdec_verify (include/specdec.h).
 SPECDEC_SMALL_V_MAX = 1024
 SPECDEC_PATH_AUTO, SPECDEC_PATH_STREAMING, SPECDEC_PATH_SMALL_VOCAB = 0, 1, 2
+SPECDEC_PATH_ONE_LAUNCH = 3
 
 
-def _options(hot_events, path):
+def _options(hot_events, path, spin_limit=0):
     ev = (None, None) if hot_events is None else tuple(
         e if isinstance(e, int) or e is None else e.cuda_event for e in hot_events)
-    return _Options(ev[0], ev[1], int(path))
+    return _Options(ev[0], ev[1], int(path), int(spin_limit))
 
 
 def library_path() -> pathlib.Path:
@@ -131,20 +133,36 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream)
 
 
-def _outputs(B, K, device, out, want_probs):
+def _on(stream):
+    """Allocation context for buffers a call creates itself: they belong to the stream the call
+    is enqueued on, so torch's caching allocator does not hand them to other work on its current
+    stream while the library's kernels still use them."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _outputs(B, K, device, out, want_probs, stream=None):
     if out is not None:
         return out
-    acc = torch.empty(B, dtype=torch.int32, device=device)
-    tok = torch.empty((B, K + 1), dtype=torch.int32, device=device)
-    prb = torch.empty((B, K + 1), dtype=torch.float32, device=device) if want_probs else None
+    with _on(stream):
+        acc = torch.empty(B, dtype=torch.int32, device=device)
+        tok = torch.empty((B, K + 1), dtype=torch.int32, device=device)
+        prb = (torch.empty((B, K + 1), dtype=torch.float32, device=device) if want_probs
+               else None)
     return acc, tok, prb
 
 
-def _workspace(B, K, V, device, workspace):
+def new_workspace(B: int, K: int, V: int, device, stream=None) -> torch.Tensor:
+    """A verify workspace for these sizes (uninitialised: the library needs none), allocated
+    for ``stream``."""
+    need = specdec_workspace_size(B, K, V)
+    with _on(stream):
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
+def _workspace(B, K, V, device, workspace, stream=None):
     need = specdec_workspace_size(B, K, V)
     if workspace is None:
-        # The library needs no initialised workspace.
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        workspace = new_workspace(B, K, V, device, stream)
     return workspace, need
 
 
@@ -158,7 +176,7 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
                    uniforms: torch.Tensor, *, draft_onehot: torch.Tensor | None = None,
                    num_draft: torch.Tensor | None = None, out=None, workspace=None,
                    want_probs: bool = True, stream=None, hot_events=None,
-                   path: int = SPECDEC_PATH_AUTO):
+                   path: int = SPECDEC_PATH_AUTO, spin_limit: int = 0):
     """Batched verify.  Shapes: target_logits [B, K+1, V] (bf16 or fp32), draft_probs
     [B, K, V] fp32 or None, proposed [B, K] int32, temperature [B] fp32, uniforms [B, K+1]
     fp32, draft_onehot [B] uint8 or None, num_draft [B] int32 or None.  Returns
@@ -166,7 +184,11 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     enqueued on ``stream`` (default: torch's current stream) without synchronising.
     ``hot_events``: optional (begin, end) pair of hipEvent_t handles (ints) recorded around the
     kernel that reads every target row.  ``path``: SPECDEC_PATH_AUTO (the one-kernel small-vocabulary
-    path when V <= SPECDEC_SMALL_V_MAX, else the streaming kernels), _STREAMING or _SMALL_VOCAB."""
+    path when V <= SPECDEC_SMALL_V_MAX, else the streaming kernels), _STREAMING, _SMALL_VOCAB
+    or _ONE_LAUNCH.
+    ``workspace``: a uint8 tensor of at least specdec_workspace_size(B, K, V) bytes
+    (``new_workspace``), reusable across calls; None allocates one for this call.
+    ``spin_limit``: SPECDEC_PATH_ONE_LAUNCH only, polls of a bounded wait (0 = the default)."""
     lib = load_library()
     if target_logits.dim() != 3:
         raise SpecdecError("target_logits must be [B, K+1, V]")
@@ -187,15 +209,15 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     _check(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
     _check(draft_onehot, "draft_onehot", torch.uint8, (B,), dev, optional=True)
     _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
-    acc, tok, prb = _outputs(B, K, dev, out, want_probs)
-    ws, need = _workspace(B, K, V, dev, workspace)
+    acc, tok, prb = _outputs(B, K, dev, out, want_probs, stream)
+    ws, need = _workspace(B, K, V, dev, workspace, stream)
     args = (_ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_onehot), _ptr(proposed),
             _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc), _ptr(tok),
             _ptr(prb), _ptr(ws), ws.numel(), _stream_handle(stream))
-    if hot_events is None and path == SPECDEC_PATH_AUTO:
+    if hot_events is None and path == SPECDEC_PATH_AUTO and spin_limit == 0:
         status = lib.specdec_verify(*args)
     else:
-        opts = _options(hot_events, path)
+        opts = _options(hot_events, path, spin_limit)
         status = lib.specdec_verify_ex(*args, ctypes.byref(opts))
     _raise(status, "specdec_verify")
     return acc, tok, prb
@@ -222,8 +244,8 @@ def specdec_verify_greedy(target_logits: torch.Tensor, proposed: torch.Tensor | 
         raise SpecdecError("target_logits must be contiguous")
     _check(proposed, "proposed", torch.int32, (B, K), dev, optional=(K == 0))
     _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
-    acc, tok, prb = _outputs(B, K, dev, out, want_probs)
-    ws, need = _workspace(B, K, V, dev, workspace)
+    acc, tok, prb = _outputs(B, K, dev, out, want_probs, stream)
+    ws, need = _workspace(B, K, V, dev, workspace, stream)
     status = lib.specdec_verify_greedy(_ptr(target_logits), dt, _ptr(proposed), _ptr(num_draft),
                                        B, K, V, _ptr(acc), _ptr(tok), _ptr(prb), _ptr(ws),
                                        ws.numel(), _stream_handle(stream))
@@ -255,8 +277,8 @@ def specdec_verify_match(target_logits: torch.Tensor, proposed: torch.Tensor | N
     _check(temperature, "temperature", torch.float32, (B,), dev)
     _check(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
     _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
-    acc, tok, prb = _outputs(B, K, dev, out, want_probs)
-    ws, need = _workspace(B, K, V, dev, workspace)
+    acc, tok, prb = _outputs(B, K, dev, out, want_probs, stream)
+    ws, need = _workspace(B, K, V, dev, workspace, stream)
     status = lib.specdec_verify_match(_ptr(target_logits), dt, _ptr(proposed), _ptr(num_draft),
                                       _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc),
                                       _ptr(tok), _ptr(prb), _ptr(ws), ws.numel(),
@@ -281,14 +303,16 @@ def specdec_ngram_propose(tokens: torch.Tensor, lengths: torch.Tensor, K: int, *
     _check(tokens, "tokens", torch.int32, (B, cap), dev)
     _check(lengths, "lengths", torch.int32, (B,), dev)
     if out is None:
-        out = (torch.empty((B, K), dtype=torch.int32, device=dev),
-               torch.empty(B, dtype=torch.int32, device=dev))
+        with _on(stream):
+            out = (torch.empty((B, K), dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev))
     proposed, num_draft = out
     _check(proposed, "proposed", torch.int32, (B, K), dev)
     _check(num_draft, "num_draft", torch.int32, (B,), dev)
     need = specdec_ngram_workspace_size(B, cap)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        with _on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     status = lib.specdec_ngram_propose(_ptr(tokens), _ptr(lengths), B, cap, int(n_min), int(n_max),
                                        int(K), _ptr(proposed) if K > 0 else None, _ptr(num_draft),
                                        _ptr(workspace), workspace.numel(), _stream_handle(stream))
@@ -329,8 +353,9 @@ def specdec_commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, seq_len: 
     pk = off = None
     if packed:
         if out is None:
-            out = (torch.empty(max(B * K1, 1), dtype=torch.int32, device=dev),
-                   torch.empty(B + 1, dtype=torch.int32, device=dev))
+            with _on(stream):
+                out = (torch.empty(max(B * K1, 1), dtype=torch.int32, device=dev),
+                       torch.empty(B + 1, dtype=torch.int32, device=dev))
         pk, off = out
     status = lib.specdec_commit(_ptr(accept_len), _ptr(out_tokens), B, K1 - 1, _ptr(tokens), cap,
                                 _ptr(seq_len), _ptr(target_kv_len), _ptr(draft_kv_len), _ptr(pk),

@@ -8,6 +8,7 @@
 #include "specdec.h"
 
 static_assert(SPECDEC_SMALL_V_MAX == specdec::kSmallVMax, "small-vocabulary path limit");
+static_assert(SPECDEC_PATH_ONE_LAUNCH == 3, "path numbering shared with kernels.h");
 
 namespace {
 
@@ -44,8 +45,7 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
       misaligned(uniforms, 4) || misaligned(accept_len, 4) || misaligned(out_tokens, 4) ||
       misaligned(out_probs, 4) || misaligned(workspace, 16))
     return SPECDEC_ERR_ALIGN;
-  const specdec::WorkspaceLayout L = specdec::workspace_layout(B, K, V);
-  if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE;
+  if (workspace_bytes < specdec::workspace_bytes(B, K, V)) return SPECDEC_ERR_WORKSPACE;
 
   specdec::LaunchArgs a{};
   a.logits = target_logits;
@@ -64,17 +64,15 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.accept_len = accept_len;
   a.out_tokens = out_tokens;
   a.out_probs = out_probs;
-  char* base = static_cast<char*>(workspace);
-  a.ws.partials = reinterpret_cast<specdec::RowPartial*>(base + L.partials);
-  a.ws.gathers = reinterpret_cast<specdec::Gather*>(base + L.gathers);
-  a.ws.states = reinterpret_cast<specdec::SeqState*>(base + L.states);
-  a.ws.segs = reinterpret_cast<specdec::SegSums*>(base + L.segs);
+  a.workspace = workspace;
   a.stream = static_cast<hipStream_t>(stream);
   a.hot_begin = opts ? static_cast<hipEvent_t>(opts->hot_event_begin) : nullptr;
   a.hot_end = opts ? static_cast<hipEvent_t>(opts->hot_event_end) : nullptr;
   a.path = opts ? opts->path : SPECDEC_PATH_AUTO;
+  a.spin_limit = opts ? opts->spin_limit : 0;
+  if (a.spin_limit < 0) return SPECDEC_ERR_SHAPE;
   if (a.path != SPECDEC_PATH_AUTO && a.path != SPECDEC_PATH_STREAMING &&
-      a.path != SPECDEC_PATH_SMALL_VOCAB)
+      a.path != SPECDEC_PATH_SMALL_VOCAB && a.path != SPECDEC_PATH_ONE_LAUNCH)
     return SPECDEC_ERR_SHAPE;
   if (a.path == SPECDEC_PATH_SMALL_VOCAB && V > SPECDEC_SMALL_V_MAX)
     return SPECDEC_ERR_SHAPE;
@@ -129,7 +127,7 @@ specdec_status specdec_ngram_propose(const int32_t* tokens, const int32_t* lengt
 
 size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V) {
   if (check_sizes(B, K, V, SPECDEC_F32) != SPECDEC_OK || B == 0) return 0;
-  return specdec::workspace_layout(B, K, V).total;
+  return specdec::workspace_bytes(B, K, V);
 }
 
 specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,

@@ -57,8 +57,10 @@ struct alignas(16) SegSums {
   double e;       // exp2((z - m) * c), i.e. s * p (fallback when the residual is empty)
 };
 
-// Caller-provided device workspace (no initialisation needed; contents are meaningless
-// between calls).
+inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Caller-provided device workspace of the three-launch path (no initialisation needed;
+// contents are meaningless between calls).
 struct Workspace {
   RowPartial* partials;  // [B*(K+1)*S*4], 4 sub-chunks per chunk
   Gather* gathers;       // [B*K]
@@ -66,14 +68,39 @@ struct Workspace {
   SegSums* segs;         // [B*S*kSegPerChunk]
 };
 
-inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
-
 struct WorkspaceLayout {
   size_t partials, gathers, states, segs, total;
 };
 
-// Byte layout of the caller's workspace for these sizes.
+// Byte layout of the three-launch path's workspace for these sizes.
 WorkspaceLayout workspace_layout(int B, int K, int V);
+
+// Per-sequence record of the one-launch path (fused.hip), in 64-bit words: the hand-off words of one
+// sequence's round (see kernels.hip).  Zero between calls: every completed call puts back to zero
+// every word it set, so the workspace must be zero-filled before its first use with given K, V.
+struct RecordLayout {
+  long long partials;  // (K+1) rows x S chunks x 4 waves x 4 words (max, sum, argmax, sum below x_i)
+  long long gathers;   // K slots x 4 words (x_i, z_i[x_i], q_i(x_i), unused)
+  long long segs;      // S*4 segments x 4 words (two doubles, in halves)
+  long long done;      // one word per closing tile (at most 4 S)
+  long long pick;      // 2 words: the drawn token and its probability
+  long long words;     // record size, a multiple of 32 words (256 bytes)
+};
+
+__host__ __device__ inline RecordLayout record_layout(int K, int V) {
+  const long long S = (V + kChunk - 1) / kChunk;
+  RecordLayout L;
+  L.partials = 0;
+  L.gathers = L.partials + static_cast<long long>(K + 1) * S * 4 * 4;
+  L.segs = L.gathers + static_cast<long long>(K) * 4;
+  L.done = L.segs + S * kSegPerChunk * 4;
+  L.pick = L.done + S * kSegPerChunk;
+  L.words = (L.pick + 2 + 31) & ~31LL;
+  return L;
+}
+
+// Bytes of workspace a verify call needs: enough for either streaming path.
+size_t workspace_bytes(int B, int K, int V);
 
 struct LaunchArgs {
   const void* logits;
@@ -90,11 +117,13 @@ struct LaunchArgs {
   int32_t* accept_len;
   int32_t* out_tokens;
   float* out_probs;
-  Workspace ws;
+  void* workspace;           // B records, zero between calls
   hipStream_t stream;
   hipEvent_t hot_begin;      // optional, recorded around the streaming (or small-vocabulary)
   hipEvent_t hot_end;        // kernel
-  int path;                  // 0: automatic, 1: streaming kernels, 2: small-vocabulary kernel
+  int path;                  // 0: automatic, 1: three launches, 2: small-vocabulary kernel,
+                             // 3: one launch
+  int spin_limit;            // polls of the one-launch path's bounded waits (0: the default)
 };
 
 // Largest vocabulary the small-vocabulary path takes (four 4-token quads per lane of a wave).
@@ -102,6 +131,7 @@ constexpr int kSmallVMax = 1024;
 
 hipError_t launch_verify(const LaunchArgs& a);
 hipError_t launch_small_verify(const LaunchArgs& a);  // small.hip; V <= kSmallVMax
+hipError_t launch_one_launch(const LaunchArgs& a);    // fused.hip
 
 // ---- n-gram drafter (ngram.hip) ----
 constexpr int kNgramTile = 8192;   // candidate positions per workgroup

@@ -1,4 +1,4 @@
-// gfx950 (CDNA4) kernels of the batched speculative-decoding verify step.
+// gfx950 (CDNA4) kernels of the batched speculative-decoding verify step, three launches.
 //
 // The step (draft-then-verify with rejection sampling) is the one the three source pages
 // define: "Decodificação especulativa explicada" (gsantana.dev), section "A regra de
@@ -31,215 +31,16 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
+#include "verify_dev.h"
 #include "wave_ops.h"
 
 namespace specdec {
 namespace {
-
-constexpr int kWaves = kThreads / 64;
-constexpr int kSub = kChunk / kWaves;          // tokens per wave sub-chunk (2048)
-constexpr int kPerThread = kSub / 64;          // logits per lane per sub-chunk (32)
-constexpr int kMaxRows = 64;           // K + 1 <= 64 target rows per sequence
-
-__device__ __forceinline__ float load_logit(const uint16_t* p, long long i) {
-  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
-__device__ __forceinline__ float load_logit(const float* p, long long i) { return p[i]; }
-
-// 16-byte vector -> floats (bf16: shift / mask into the upper half of a binary32).
-__device__ __forceinline__ void unpack(const uint4& d, float* o, const uint16_t*) {
-  o[0] = __uint_as_float(d.x << 16); o[1] = __uint_as_float(d.x & 0xffff0000u);
-  o[2] = __uint_as_float(d.y << 16); o[3] = __uint_as_float(d.y & 0xffff0000u);
-  o[4] = __uint_as_float(d.z << 16); o[5] = __uint_as_float(d.z & 0xffff0000u);
-  o[6] = __uint_as_float(d.w << 16); o[7] = __uint_as_float(d.w & 0xffff0000u);
-}
-__device__ __forceinline__ void unpack(const uint4& d, float* o, const float*) {
-  o[0] = __uint_as_float(d.x); o[1] = __uint_as_float(d.y);
-  o[2] = __uint_as_float(d.z); o[3] = __uint_as_float(d.w);
-}
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// Plain (cached) 16-byte load: the draw kernel's reads of the row to draw from, which the pick
-// kernel re-reads one segment of (nontemporal loads there measured 3-6 % slower on the large
-// and ragged batches).
-__device__ __forceinline__ uint4 plain_load(const void* p) {
-  const u32x4 t = *static_cast<const u32x4*>(p);
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-// 16-byte streaming load: the streaming kernel reads every logit once per call, so its loads
-// carry the nontemporal hint.
-__device__ __forceinline__ uint4 stream_load(const void* p) {
-  const u32x4 t = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-template <typename LT> struct Vec;
-template <> struct Vec<uint16_t> {
-  static constexpr int kPer = 8;
-  static constexpr uint32_t kNegInf = 0xff80ff80u;  // two bf16 -inf
-};
-template <> struct Vec<float> {
-  static constexpr int kPer = 4;
-  static constexpr uint32_t kNegInf = 0xff800000u;
-};
-
-// Running (max, sum of exp2((z - max) * c), lowest argmax) of a set of logits.
-struct Stat {
-  float m;
-  float s;
-  int a;
-};
-
-
-// ------------------------------------------------------------------------------------------
-// Streaming statistics of one wave's sub-chunk.  The wave's max is reduced first and every lane
-// exponentiates against it, so the sum is a plain wave sum: one exp per logit plus one, instead
-// of a rescaling (m, s) merge at every reduction step.
-// ------------------------------------------------------------------------------------------
-struct MaxSum {
-  float m;
-  float s;
-};
-
-template <typename LT, bool kVec>
-__device__ __forceinline__ int tok_of(int c0, int lane, int j);
-
-// (max, sum of exp2((z - max) * c)) of the wave's logits, and with kPre the same sum over the
-// tokens below `xid` (match mode).  exp2((z - m) * c) is taken as exp2(fma(z, c, -hi)) * exp2(-lo)
-// with m * c = hi + lo split exactly: one fma per logit and an exponent exact up to the fma's
-// rounding.  An all -inf (or NaN) sub-chunk keeps the reference at 0 so -inf maps to 0; NaN and
-// +inf logits make the sum NaN, which marks the row invalid.
-template <typename LT, bool kVec, bool kPre>
-__device__ __forceinline__ MaxSum fold_wave(const float (&x)[kPerThread], float c, int c0,
-                                           int lane, int xid, float& lane_max, float& pre) {
-  float bm = x[0];
-#pragma unroll
-  for (int j = 1; j < kPerThread; ++j) bm = fmaxf(bm, x[j]);
-  lane_max = bm;
-  const float M = wave_max_f(bm);
-  const float ref = (M == -INFINITY) ? 0.f : M;
-  const float hi = ref * c;
-  const float lo = fmaf(ref, c, -hi);
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-  for (int j = 0; j < kPerThread; j += 4) {
-    const float e0 = __builtin_amdgcn_exp2f(fmaf(x[j], c, -hi));
-    const float e1 = __builtin_amdgcn_exp2f(fmaf(x[j + 1], c, -hi));
-    const float e2 = __builtin_amdgcn_exp2f(fmaf(x[j + 2], c, -hi));
-    const float e3 = __builtin_amdgcn_exp2f(fmaf(x[j + 3], c, -hi));
-    s0 += e0; s1 += e1; s2 += e2; s3 += e3;
-    if constexpr (kPre) {
-      p0 += tok_of<LT, kVec>(c0, lane, j) < xid ? e0 : 0.f;
-      p1 += tok_of<LT, kVec>(c0, lane, j + 1) < xid ? e1 : 0.f;
-      p2 += tok_of<LT, kVec>(c0, lane, j + 2) < xid ? e2 : 0.f;
-      p3 += tok_of<LT, kVec>(c0, lane, j + 3) < xid ? e3 : 0.f;
-    }
-  }
-  const float f = __builtin_amdgcn_exp2f(-lo);
-  if constexpr (kPre) pre = wave_sum_f((p0 + p1) + (p2 + p3)) * f;
-  return MaxSum{M, wave_sum_f((s0 + s1) + (s2 + s3)) * f};
-}
-
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-// Load one lane's logits of the wave's sub-chunk [c0, c0 + n) (n <= kSub, possibly <= 0):
-// 16-byte vectors u * 64 + lane (scalar path: tokens u * 64 + lane), all issued before any
-// value is used.  Slots past n read as -inf.
-template <typename LT, bool kVec>
-__device__ __forceinline__ void load_sub(const LT* __restrict__ row, int c0, int n, int lane,
-                                         float (&x)[kPerThread]) {
-  if constexpr (kVec) {
-    constexpr int P = Vec<LT>::kPer;
-    constexpr int U = kPerThread / P;
-    const uint4* vrow = reinterpret_cast<const uint4*>(row + c0);
-    const int nvec = n / P;
-    uint4 d[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int vi = u * 64 + lane;
-      constexpr uint32_t ni = Vec<LT>::kNegInf;
-      d[u] = vi < nvec ? stream_load(vrow + vi) : make_uint4(ni, ni, ni, ni);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) unpack(d[u], &x[u * P], static_cast<const LT*>(nullptr));
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int vi = j * 64 + lane;
-      x[j] = vi < n ? load_logit(row, c0 + vi) : -INFINITY;
-    }
-  }
-}
-
-template <typename LT, bool kVec>
-__device__ __forceinline__ int tok_of(int c0, int lane, int j) {
-  if constexpr (kVec) {
-    constexpr int P = Vec<LT>::kPer;
-    return c0 + ((j / P) * 64 + lane) * P + (j % P);
-  } else {
-    return c0 + j * 64 + lane;
-  }
-}
-
-// Max-first merges of the row partials for the accept scan: the maximum is found first and each
-// sum is rescaled once against it (independent exps, no dependent chain of pairwise merges).
-// The lowest index attaining the maximum is kept for greedy rows.
-__device__ __forceinline__ Stat merge4(const Stat& v, const RowPartial (&p)[4], float c) {
-  float M = v.m;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) M = fmaxf(M, p[t].m);
-  Stat r{M, 0.f, INT_MAX};
-  if (M == -INFINITY) {  // nothing but empty sub-chunks (NaN sums stay NaN)
-    r.s = v.s;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) r.s += p[t].s;
-    return r;
-  }
-  r.s = v.s * __builtin_amdgcn_exp2f((v.m - M) * c);
-  r.a = v.m == M ? v.a : INT_MAX;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    r.s += p[t].s * __builtin_amdgcn_exp2f((p[t].m - M) * c);
-    if (p[t].m == M) r.a = min(r.a, p[t].arg);
-  }
-  return r;
-}
-
-// The same over each 16-lane row (every lane of a row ends with its row's result).
-__device__ __forceinline__ Stat row16_reduce_mf(const Stat& v, float c) {
-  float M = v.m;
-  M = fmaxf(M, dpp_f<0xB1>(M));
-  M = fmaxf(M, dpp_f<0x4E>(M));
-  M = fmaxf(M, dpp_f<0x124>(M));
-  M = fmaxf(M, dpp_f<0x128>(M));
-  float sum = M == -INFINITY ? v.s : v.s * __builtin_amdgcn_exp2f((v.m - M) * c);
-  sum += dpp_f<0xB1>(sum);
-  sum += dpp_f<0x4E>(sum);
-  sum += dpp_f<0x124>(sum);
-  sum += dpp_f<0x128>(sum);
-  int a = v.m == M ? v.a : INT_MAX;
-  a = min(a, dpp_i<0xB1>(a));
-  a = min(a, dpp_i<0x4E>(a));
-  a = min(a, dpp_i<0x124>(a));
-  a = min(a, dpp_i<0x128>(a));
-  return Stat{M, sum, a};
-}
-
-// Inputs of the accept scan that need neither the row statistics nor the temperature: the
-// drafted ids with their gathered logit and q (recorded by the streaming kernel), the uniforms
-// and the one-hot flag.  Lane i holds slot i.
-struct ScanIn {
-  Gather g;
-  float u;
-  float uk;
-  int onehot;
-};
 
 // Their loads, issued unconditionally so that all of them -- and the partials after them -- are
 // in flight together: an absent operand (null pointer, or no drafted slot) is read from `any`, a
@@ -275,17 +76,6 @@ __device__ __forceinline__ ScanIn finish_scan_in(const ScanLoads& r, const uint8
   return in;
 }
 
-// What an accept scan decides: the draw state (the same in every lane), the accept length and
-// lane i's output slot i: its token (-1 where the draw or nothing goes) and its probability as
-// num / den, divided only when the outputs are written (after the state is published).
-struct ScanOut {
-  SeqState st;
-  int A;
-  int tok;
-  double num;
-  double den;
-};
-
 // The scan's global writes, made after the workgroup barrier that publishes the state in LDS
 // (a barrier waits for every outstanding store of the workgroup).
 __device__ __forceinline__ void write_scan_out(const ScanOut& o, int b, int K,
@@ -300,131 +90,6 @@ __device__ __forceinline__ void write_scan_out(const ScanOut& o, int b, int K,
     accept_len[b] = o.A;
     states[b] = o.st;
   }
-}
-
-// Accept scan of sequence b by one wave64 (lane i <-> target row i), given its raw draft count,
-// temperature, exp2 scale c (temp_scale(T) for a valid sequence, else log2(e)) and the row
-// statistics in LDS (an invalid count or temperature poisons the sequence).  Returns what
-// remains to be drawn and the tokens already known.  The test u * q(x) < p(x) = e / s is taken
-// as u * q(x) * s < e in fp64, so no division stands before the decision.
-__device__ __forceinline__ ScanOut accept_sequence(const ScanIn& in, bool have_q, int kb_raw,
-                                                   float T, float c, int K, int V,
-                                                   const Stat* sh_rows, int lane) {
-  const Gather g = in.g;
-  const float u = in.u, uk = in.uk;
-  const bool seq_ok = kb_raw >= 0 && kb_raw <= K && temp_valid(T);
-  const int kb = seq_ok ? kb_raw : 0;
-  const bool greedy = (T == 0.f);
-  const bool is_onehot = !greedy && in.onehot;
-  const Stat st = lane <= K ? sh_rows[lane] : Stat{-INFINITY, 0.f, INT_MAX};
-
-  const bool drafted = lane < kb;
-  const int x = g.x;
-  const bool x_ok = x >= 0 && x < V;
-  bool lane_ok = true;
-  double ex = 0.0;  // exp2((z_i[x_i] - m_i) * c) = s_i * p_i(x_i)
-  bool acc = true;
-  if (lane <= kb) {
-    lane_ok = st.s > 0.f;  // NaN / +inf logit -> NaN; all -inf -> 0
-    if (drafted) {
-      if (!x_ok) {
-        lane_ok = false;
-      } else {
-        ex = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
-                  static_cast<double>(c));
-        if (greedy) {
-          acc = (x == st.a);
-        } else {
-          if (!(u >= 0.f && u < 1.f)) lane_ok = false;
-          double qx = 1.0;  // one-hot drafter: q(x) = 1
-          if (!is_onehot) {
-            if (!have_q) lane_ok = false;
-            else if (!(g.q >= 0.f && g.q <= FLT_MAX)) lane_ok = false;
-            qx = g.q;
-          }
-          acc = static_cast<double>(u) * qx * static_cast<double>(st.s) < ex;
-        }
-      }
-    }
-  }
-  if (!greedy && lane == 0 && !(uk >= 0.f && uk < 1.f)) lane_ok = false;
-  const bool ok = seq_ok && (__ballot(!lane_ok) == 0ull);
-  const unsigned long long rej = __ballot(lane < kb && !acc);
-  const int A = ok ? (rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb) : -1;
-
-  SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
-  if (ok && !greedy) {  // A is wave-uniform: lane A's row is the one to draw from
-    const int mode = (A == kb) ? kBonus : (is_onehot ? kResidualOnehot : kResidual);
-    out = SeqState{mode, A, __builtin_amdgcn_readlane(x, A), K, c, read_lane_f(st.m, A),
-                   read_lane_f(st.s, A), 0.f};
-  }
-  ScanOut o{out, A, -1, 0.0, 1.0};                  // a sampled slot is filled by the draw
-  if (ok && lane < A) {
-    o.tok = x;
-    o.num = ex;
-    o.den = static_cast<double>(st.s);
-  } else if (ok && lane == A && greedy) {
-    o.tok = st.a;                                    // argmax: exp2(0) / s
-    o.num = 1.0;
-    o.den = static_cast<double>(st.s);
-  }
-  return o;
-}
-
-// ------------------------------------------------------------------------------------------
-// Match mode ("Decodificação especulativa explicada", section "A regra de amostragem por
-// rejeição", the simpler exact scheme): position i draws y_i from p_i with u[b, i] (the bonus
-// position with u[b, K]) and the draft is kept while y_i == x_i.  The inverse-CDF draw picks x_i
-// exactly when its interval [C(x_i - 1), C(x_i)) of the running sum holds t = u * total, so the
-// scan decides every position from the row's total S_i, the sum P_i below x_i and x_i's own
-// weight -- no pass over the row.  Only the first mismatching position (or the bonus) is then
-// drawn by the draw kernels, as a plain sample of p with its own uniform column.
-// ------------------------------------------------------------------------------------------
-struct StatD {
-  float m;
-  double s;  // sum of exp2((z - m) * c)
-  double p;  // the same sum below the drafted id
-};
-
-__device__ __forceinline__ StatD merge4_d(const StatD& v, const RowPartial (&p)[4], float c) {
-  float M = v.m;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) M = fmaxf(M, p[t].m);
-  StatD r{M, v.s, v.p};
-  if (M == -INFINITY) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) { r.s += p[t].s; r.p += p[t].pre; }
-    return r;
-  }
-  const double fv = __builtin_amdgcn_exp2f((v.m - M) * c);
-  r.s = v.s * fv;
-  r.p = v.p * fv;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const double f = __builtin_amdgcn_exp2f((p[t].m - M) * c);
-    r.s += static_cast<double>(p[t].s) * f;
-    r.p += static_cast<double>(p[t].pre) * f;
-  }
-  return r;
-}
-
-__device__ __forceinline__ StatD row16_reduce_d(const StatD& v, float c) {
-  float M = v.m;
-  M = fmaxf(M, dpp_f<0xB1>(M));
-  M = fmaxf(M, dpp_f<0x4E>(M));
-  M = fmaxf(M, dpp_f<0x124>(M));
-  M = fmaxf(M, dpp_f<0x128>(M));
-  const double f = M == -INFINITY ? 1.0 : static_cast<double>(__builtin_amdgcn_exp2f((v.m - M) * c));
-  double sum = v.s * f, pre = v.p * f;
-  sum += dpp_move_d<0xB1, 0xf>(sum);
-  pre += dpp_move_d<0xB1, 0xf>(pre);
-  sum += dpp_move_d<0x4E, 0xf>(sum);
-  pre += dpp_move_d<0x4E, 0xf>(pre);
-  sum += dpp_move_d<0x124, 0xf>(sum);
-  pre += dpp_move_d<0x124, 0xf>(pre);
-  sum += dpp_move_d<0x128, 0xf>(sum);
-  pre += dpp_move_d<0x128, 0xf>(pre);
-  return StatD{M, sum, pre};
 }
 
 // Row statistics of rows 0..K of one sequence, by every wave of the workgroup: 16 lanes per
@@ -507,48 +172,6 @@ __device__ __forceinline__ void row_stats(const RowPartial* __restrict__ partial
   }
 }
 
-// The match-mode scan of one sampled sequence with a valid draft count (greedy and
-// invalid-count sequences take the rejection-rule scan, which treats them identically).  Same
-// layout and outputs as accept_sequence.
-__device__ __forceinline__ ScanOut accept_sequence_match(const ScanIn& in, int kb, float T,
-                                                         float c, int K, int V,
-                                                         const StatD* sh_rows, int lane) {
-  const Gather g = in.g;
-  const float u = in.u, uk = in.uk;
-  const bool seq_ok = temp_valid(T);  // T != 0 and k_b in range here
-  const StatD st = lane <= K ? sh_rows[lane] : StatD{-INFINITY, 0.0, 0.0};
-
-  const bool drafted = lane < kb;
-  const int x = g.x;
-  bool lane_ok = true, keep = true;
-  double ex = 0.0;
-  if (lane <= kb) {
-    lane_ok = st.s > 0.0;  // NaN / +inf logit -> NaN; all -inf -> 0
-    if (drafted) {
-      if (!(x >= 0 && x < V) || !(u >= 0.f && u < 1.f)) {
-        lane_ok = false;
-      } else {
-        // y_i == x_i  <=>  P_i <= u * S_i < P_i + e(x_i)
-        ex = exp2((static_cast<double>(g.z) - static_cast<double>(st.m)) *
-                  static_cast<double>(c));
-        const double t = static_cast<double>(u) * st.s;
-        keep = st.p <= t && t < st.p + ex;
-      }
-    }
-  }
-  if (lane == 0 && !(uk >= 0.f && uk < 1.f)) lane_ok = false;
-  const bool ok = seq_ok && (__ballot(!lane_ok) == 0ull);
-  const unsigned long long rej = __ballot(lane < kb && !keep);
-  const int A = ok ? (rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb) : -1;
-
-  SeqState out{kNone, 0, 0, 0, 0.f, 0.f, 0.f, 0.f};
-  if (ok)  // a plain draw of p_A with u[b, A] (mismatch) or u[b, K] (bonus)
-    out = SeqState{kBonus, A, -1, A < kb ? A : K, c, read_lane_f(st.m, A),
-                   static_cast<float>(read_lane_d(st.s, A)), 0.f};
-  const bool kept = ok && lane < A;                  // slot A is filled by the draw
-  return ScanOut{out, A, kept ? x : -1, kept ? ex : 0.0, kept ? st.s : 1.0};
-}
-
 // ------------------------------------------------------------------------------------------
 // Streaming row statistics.
 // ------------------------------------------------------------------------------------------
@@ -619,94 +242,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   if (lane == 0)
     partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, pre};
 }
-
-// ------------------------------------------------------------------------------------------
-// Kernel B: draw weights per segment + the inverse-CDF pick of each completed sequence.
-// ------------------------------------------------------------------------------------------
-__device__ __forceinline__ float draw_weight(float z, float q, int v, const SeqState& st,
-                                             bool plain, float& e_out) {
-  const float e = __builtin_amdgcn_exp2f((z - st.m) * st.c);
-  e_out = e;
-  if (plain || st.mode == kBonus) return e;
-  if (st.mode == kResidualOnehot) return v == st.excl ? 0.f : e;
-  return fmaxf(0.f, fmaf(-st.s, q, e));  // s * max(0, p - q)
-}
-
-// Loads of the kGroup tokens [v0, v0 + cnt) (cnt <= 0: none); -inf / 0 past cnt.  The vector
-// path loads unconditionally -- from `any`, a valid 16-byte-aligned stand-in of at least 32
-// bytes, when there is nothing to read -- and then selects, so the target and draft loads are
-// in flight together.
-template <typename LT, bool kVec>
-__device__ __forceinline__ void load_group(const LT* __restrict__ z, const float* __restrict__ q,
-                                           const void* any, int v0, int cnt,
-                                           float (&zv)[kGroup], float (&qv)[kGroup]) {
-  if constexpr (kVec) {  // cnt is kGroup or <= 0; 16-byte aligned
-    const bool in = cnt > 0, inq = in && q != nullptr;
-    const LT* zp = in ? z + v0 : static_cast<const LT*>(any);
-    const float* qp = inq ? q + v0 : static_cast<const float*>(any);
-    const uint4 z0 = stream_load(zp);
-    uint4 z1 = make_uint4(0, 0, 0, 0);
-    if constexpr (sizeof(LT) == 4) z1 = stream_load(zp + 4);
-    const uint4 q0 = stream_load(qp), q1 = stream_load(qp + 4);
-    unpack(z0, zv, static_cast<const LT*>(nullptr));
-    if constexpr (sizeof(LT) == 4) unpack(z1, zv + 4, static_cast<const LT*>(nullptr));
-    unpack(q0, qv, static_cast<const float*>(nullptr));
-    unpack(q1, qv + 4, static_cast<const float*>(nullptr));
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      if (!in) zv[j] = -INFINITY;
-      if (!inq) qv[j] = 0.f;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      zv[j] = j < cnt ? load_logit(z, v0 + j) : -INFINITY;
-      qv[j] = (q != nullptr && j < cnt) ? q[v0 + j] : 0.f;
-    }
-  }
-}
-
-// Weights of one group and their sums (sequential in token order, fp32).
-__device__ __forceinline__ void group_weights(const float (&zv)[kGroup], const float (&qv)[kGroup],
-                                              int v0, int cnt, const SeqState& st, bool plain,
-                                              float (&w)[kGroup], float& gw, float& ge) {
-  gw = 0.f;
-  ge = 0.f;
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    float e = 0.f;
-    w[j] = j < cnt ? draw_weight(zv[j], qv[j], v0 + j, st, plain, e) : 0.f;
-    if (j >= cnt) e = 0.f;
-    gw += w[j];
-    ge += e;
-  }
-}
-
-
-// Four consecutive logits as one cached load: 8 bytes of bf16 or 16 bytes of fp32.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-template <typename LT> struct DrawVec;
-template <> struct DrawVec<uint16_t> {
-  uint2 d;
-  static __device__ __forceinline__ DrawVec load(const uint16_t* p) {
-    const u32x2 t = *reinterpret_cast<const u32x2*>(p);
-    return DrawVec{make_uint2(t.x, t.y)};
-  }
-  static __device__ __forceinline__ DrawVec zero() { return DrawVec{make_uint2(0, 0)}; }
-  __device__ __forceinline__ void unpack(float* o) const {
-    o[0] = __uint_as_float(d.x << 16); o[1] = __uint_as_float(d.x & 0xffff0000u);
-    o[2] = __uint_as_float(d.y << 16); o[3] = __uint_as_float(d.y & 0xffff0000u);
-  }
-};
-template <> struct DrawVec<float> {
-  uint4 d;
-  static __device__ __forceinline__ DrawVec load(const float* p) { return DrawVec{plain_load(p)}; }
-  static __device__ __forceinline__ DrawVec zero() { return DrawVec{make_uint4(0, 0, 0, 0)}; }
-  __device__ __forceinline__ void unpack(float* o) const {
-    o[0] = __uint_as_float(d.x); o[1] = __uint_as_float(d.y);
-    o[2] = __uint_as_float(d.z); o[3] = __uint_as_float(d.w);
-  }
-};
 
 // ------------------------------------------------------------------------------------------
 // Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
@@ -1033,6 +568,13 @@ auto accept_draw_for(bool match, bool vec) -> decltype(&accept_draw_kernel<LT, t
 
 template <typename LT>
 hipError_t launch_typed(const LaunchArgs& a) {
+  const WorkspaceLayout L = workspace_layout(a.B, a.K, a.V);
+  char* base = static_cast<char*>(a.workspace);
+  Workspace ws;
+  ws.partials = reinterpret_cast<RowPartial*>(base + L.partials);
+  ws.gathers = reinterpret_cast<Gather*>(base + L.gathers);
+  ws.states = reinterpret_cast<SeqState*>(base + L.states);
+  ws.segs = reinterpret_cast<SegSums*>(base + L.segs);
   const LT* logits = static_cast<const LT*>(a.logits);
   const int S = num_chunks(a.V);
   const bool vec_stats = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
@@ -1053,11 +595,11 @@ hipError_t launch_typed(const LaunchArgs& a) {
     if (ev0 || ev1)
       hipExtLaunchKernelGGL(stats, grid, dim3(kThreads), 0, a.stream, ev0, ev1, 0, logits,
                             a.draft_probs, a.proposed, a.num_draft, a.temperature, b0, a.K, a.V,
-                            S, a.greedy_all, a.ws.partials, a.ws.gathers);
+                            S, a.greedy_all, ws.partials, ws.gathers);
     else
       stats<<<grid, kThreads, 0, a.stream>>>(logits, a.draft_probs, a.proposed, a.num_draft,
                                              a.temperature, b0, a.K, a.V, S, a.greedy_all,
-                                             a.ws.partials, a.ws.gathers);
+                                             ws.partials, ws.gathers);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // Accept scan + draw sums: one workgroup per (chunk, sequence); greedy-only calls need just
@@ -1089,19 +631,19 @@ hipError_t launch_typed(const LaunchArgs& a) {
       const dim3 grid(gx, min(kMaxZ, a.B - b0));
       accept_draw(phase)<<<grid, kThreads, 0, a.stream>>>(
           logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms,
-          b0, a.K, a.V, S, a.greedy_all, a.ws.partials, a.ws.gathers, a.accept_len,
-          a.out_tokens, a.out_probs, a.ws.states, a.ws.segs);
+          b0, a.K, a.V, S, a.greedy_all, ws.partials, ws.gathers, a.accept_len,
+          a.out_tokens, a.out_probs, ws.states, ws.segs);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
   if (a.greedy_all) return hipSuccess;
   if (vec_draw)
     pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
+        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
         a.out_tokens, a.out_probs);
   else
     pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, a.ws.states, a.ws.segs,
+        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
         a.out_tokens, a.out_probs);
   return hipGetLastError();
 }
@@ -1126,7 +668,13 @@ WorkspaceLayout workspace_layout(int B, int K, int V) {
   return L;
 }
 
+size_t workspace_bytes(int B, int K, int V) {
+  const size_t one = static_cast<size_t>(B) * static_cast<size_t>(record_layout(K, V).words) * 8;
+  return std::max(workspace_layout(B, K, V).total, one);
+}
+
 hipError_t launch_verify(const LaunchArgs& a) {
+  if (a.path == 3) return launch_one_launch(a);
   // Rows of at most kSmallVMax tokens fit one wave's registers: one kernel, a group of lanes
   // per sequence (small.hip), unless the streaming kernels are asked for.
   const bool small = a.V <= kSmallVMax && a.path != 1;

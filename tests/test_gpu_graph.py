@@ -52,7 +52,7 @@ def test_verify_graph_replays_match_eager(match, V):
                            ragged=True) for i in range(2)]
     other = inputs_to_device(gen.make_batch(16, 5, V, seed=90), DEV)
     B, K = 16, 5
-    ws = torch.empty(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=DEV)
     ds = [inputs_to_device(i, DEV) for i in inps]
 
     def call(d, out):

@@ -205,13 +205,13 @@ def test_empty_batch():
 
 
 def test_workspace_reuse_across_calls_and_shapes():
-    """One zero-filled workspace serves consecutive calls of different shapes: every call
-    leaves its arrival counters at zero again."""
+    """One uninitialised workspace (filled with garbage first) serves consecutive calls of
+    different shapes: no call depends on what an earlier one left in it."""
     from speculative_decoding_verification_specdec_amd import specdec_workspace_size
     big = gen.ragged_mixed(B=80, V=20000, seed=61)
     small = gen.batch64(B=12, V=9000, seed=62)
     need = max(specdec_workspace_size(x.B, x.K, x.V) for x in (big, small))
-    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV)
     for inp in (big, small, big, small):
         d = inputs_to_device(inp, DEV)
         acc, tok, prb = specdec_verify(d["logits"], d["draft_probs"], d["proposed"],
@@ -243,3 +243,24 @@ def test_zero_mass_drafts(V, path):
     acc, tok, _ = run_gpu(inp, path=path)
     for b in range(0, inp.B, 3):
         assert acc[b] == 0 and tok[b, 0] != X[b, 0]  # rejected at slot 0, x_0 not redrawn
+
+
+def test_call_on_a_side_stream_keeps_its_temporaries():
+    """A call enqueued on another stream than torch's current one, with the workspace and outputs
+    allocated by the binding: those buffers belong to the call's stream, so an allocation made
+    and written on the current stream right after the call cannot take them over while the
+    kernels still run."""
+    inp = gen.batch64(B=32, V=60000, seed=63)
+    d = inputs_to_device(inp, DEV)
+    ref = oracle.verify(inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda._sleep(int(5e7))                       # keep the current stream busy meanwhile
+    acc, tok, prb = specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
+                                   d["uniforms"], draft_onehot=d["draft_onehot"],
+                                   num_draft=d["num_draft"], stream=side)
+    junk = [torch.full((1 << 22,), 0x7f, dtype=torch.uint8, device=DEV) for _ in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    assert rep["mismatch"] == 0, rep["details"]
