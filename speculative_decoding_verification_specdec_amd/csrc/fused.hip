@@ -64,19 +64,6 @@ __device__ __forceinline__ void write_round_out(const ScanOut& o, bool deferred,
 // the same workspace (same K and V) starts from zeros again.  Each 64-bit store is single-copy
 // atomic, so a marked word never pairs a new mark with stale data.
 // ------------------------------------------------------------------------------------------
-typedef unsigned long long u64;
-constexpr uint32_t kMark = 0x5ec0da7au;
-
-__device__ __forceinline__ u64 marked(uint32_t v) { return (static_cast<u64>(kMark) << 32) | v; }
-__device__ __forceinline__ bool is_marked(u64 w) { return static_cast<uint32_t>(w >> 32) == kMark; }
-__device__ __forceinline__ uint32_t bits_of(u64 w) { return static_cast<uint32_t>(w); }
-__device__ __forceinline__ u64 load_word(const u64* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_word(u64* p, u64 v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 struct KArgs {
   const void* logits;
   const float* draft_probs;

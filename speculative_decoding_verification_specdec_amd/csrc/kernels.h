@@ -66,10 +66,11 @@ struct Workspace {
   Gather* gathers;       // [B*K]
   SeqState* states;      // [B]
   SegSums* segs;         // [B*S*kSegPerChunk]
+  unsigned long long* segw;  // [B*S*kSegPerChunk*4] segment sums as marked words (in-kernel pick)
 };
 
 struct WorkspaceLayout {
-  size_t partials, gathers, states, segs, total;
+  size_t partials, gathers, states, segs, segw, total;
 };
 
 // Byte layout of the three-launch path's workspace for these sizes.

@@ -180,11 +180,16 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const int32_t* __restrict__ proposed, const int32_t* __restrict__ num_draft,
     const float* __restrict__ temperature, int b0, int K, int V, int S, int greedy_all,
-    RowPartial* __restrict__ partials, Gather* __restrict__ gathers) {
+    RowPartial* __restrict__ partials, Gather* __restrict__ gathers, u64* __restrict__ segw) {
   // Grid: x = chunk, y = row within the sequence, z = sequence (offset by b0).  Each wave
   // reduces its own 2048-token sub-chunk and writes its own partial: no LDS, no barrier.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = blockIdx.x, i = blockIdx.y, b = b0 + static_cast<int>(blockIdx.z);
+  if (s == 0 && i == 0 && segw != nullptr) {
+    // The draw kernel's segment-sum words start from zero in every call.
+    u64* w = segw + static_cast<long long>(b) * S * kSegPerChunk * 4;
+    for (int j = threadIdx.x; j < S * kSegPerChunk * 4; j += kThreads) w[j] = 0;
+  }
   int kb = K;
   if (num_draft != nullptr) {
     kb = num_draft[b];
@@ -244,6 +249,149 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// Inverse-CDF draw ("Decodificação especulativa explicada", section "Amostragem especulativa em
+// numpy, com prova": the first running sum above u times the total, over ascending token id),
+// from per-segment weight sums: one fp64 DPP scan over the segment sums finds the segment holding
+// u * total (plain p when the draw's total is not positive), then a workgroup scan of that one
+// segment finds the token.
+// ------------------------------------------------------------------------------------------
+struct PickLds {
+  int seg, plain, flag, hit[kWaves], lastpos[kWaves];
+  float zhit[kWaves], zlast[kWaves];
+  double t, base, wtot[kWaves];
+};
+
+// First step, in wave 0: lane l holds the sums (lw: the draw's weights; le: those of p) of its
+// segments [l * P, l * P + P); seg_at(j, plain) gives segment j's sum again.  Leaves the segment,
+// the target u * total and the running sum before the segment in ps.
+template <typename SegAt>
+__device__ __forceinline__ void find_draw_segment(double lw, double le, float u, int nseg, int P,
+                                                  SegAt seg_at, PickLds& ps, int lane) {
+  const int j0 = lane * P;
+  const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
+  const bool plain = !(read_lane_d(iw, 63) > 0.0);  // empty residual: draw from p itself
+  const double inc = plain ? ie : iw;
+  const double own = plain ? le : lw;
+  const double R = read_lane_d(inc, 63);
+  const double t = static_cast<double>(u) * R;
+  // The first lane whose running total passes t holds the segment; if rounding left t at the
+  // very top, the last lane with positive weight does.
+  const unsigned long long hit = __ballot(own > 0.0 && inc > t);
+  const unsigned long long pos = __ballot(own > 0.0);
+  const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
+                     : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+  if (lane == hl) {
+    double run = inc - own;  // running sum before the lane's segments
+    int seg = -1, lastpos = -1;
+    double base_seg = 0.0, base_last = 0.0;
+    for (int q = 0; q < P && j0 + q < nseg; ++q) {
+      const double v = seg_at(j0 + q, plain);
+      if (v > 0.0) {
+        if (run + v > t) { seg = j0 + q; base_seg = run; break; }
+        lastpos = j0 + q;
+        base_last = run;
+      }
+      run += v;
+    }
+    if (seg < 0) { seg = lastpos >= 0 ? lastpos : j0; base_seg = base_last; }
+    ps.seg = seg; ps.plain = plain; ps.t = t; ps.base = base_seg;
+  }
+}
+
+// Second step, the whole workgroup (after a barrier): scan segment ps.seg of row z (draft row
+// q_row for a residual, else null) in ascending token order; thread 0 writes the token and its
+// probability.  `any`: a valid 16-byte-aligned stand-in address for absent loads.
+template <typename LT, bool kVec>
+__device__ __forceinline__ void scan_draw_segment(const LT* __restrict__ z,
+                                                  const float* __restrict__ q_row, const void* any,
+                                                  int V, const SeqState& st, bool force_plain,
+                                                  PickLds& ps, int32_t* tok, float* prob) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = ps.seg;
+  const bool plain = force_plain || ps.plain != 0;
+  const double t = ps.t;
+  const int sc = seg / kSegPerChunk, sg = seg % kSegPerChunk;
+  const int cc0 = sc * kChunk, cn = min(kChunk, V - cc0);
+  const int v0 = sg * kSeg + tid * kGroup;
+  const int cnt = min(kGroup, cn - v0);
+  const float* qs = (st.mode == kResidual && !plain) ? q_row : nullptr;
+  float zg[kGroup], qg[kGroup], w[kGroup], gw, ge;
+  load_group<LT, kVec>(z, qs, any, cc0 + v0, cnt, zg, qg);
+  group_weights(zg, qg, cc0 + v0, cnt, st, plain, w, gw, ge);
+  const double inc = wave_inclusive_scan(static_cast<double>(gw));
+  if (lane == 63) ps.wtot[wave] = inc;
+  __syncthreads();
+  double before = ps.base;
+  for (int k = 0; k < wave; ++k) before += ps.wtot[k];
+  before += inc - static_cast<double>(gw);
+  int hit = -1, lastpos = -1;
+  float zhit = 0.f, zlast = 0.f, run = 0.f;
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    run += w[j];
+    if (w[j] > 0.f) {
+      lastpos = cc0 + v0 + j;
+      zlast = zg[j];
+      if (hit < 0 && before + static_cast<double>(run) > t) { hit = cc0 + v0 + j; zhit = zg[j]; }
+    }
+  }
+  const unsigned long long hm = __ballot(hit >= 0);
+  const unsigned long long pm = __ballot(lastpos >= 0);
+  const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 0;
+  const int ll = pm ? 63 - __clzll(static_cast<long long>(pm)) : 0;
+  // hl and ll are wave-uniform: readlane, not a cross-lane shuffle through LDS.
+  const int wave_hit = hm ? __builtin_amdgcn_readlane(hit, hl) : -1;
+  const float wave_zhit = read_lane_f(zhit, hl);
+  const int wave_last = pm ? __builtin_amdgcn_readlane(lastpos, ll) : -1;
+  const float wave_zlast = read_lane_f(zlast, ll);
+  if (lane == 0) {
+    ps.hit[wave] = wave_hit; ps.zhit[wave] = wave_zhit;
+    ps.lastpos[wave] = wave_last; ps.zlast[wave] = wave_zlast;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int y = -1, lp = -1;
+    float zy = 0.f, zl = 0.f;
+    for (int k = 0; k < kWaves; ++k) {
+      if (y < 0 && ps.hit[k] >= 0) { y = ps.hit[k]; zy = ps.zhit[k]; }
+      if (ps.lastpos[k] >= 0) { lp = ps.lastpos[k]; zl = ps.zlast[k]; }
+    }
+    // Rounding left t at the very top of the segment: take its last positive token.
+    if (y < 0) {
+      y = lp >= 0 ? lp : cc0 + sg * kSeg;
+      zy = lp >= 0 ? zl : load_logit(z, y);
+    }
+    const double p = exp2((static_cast<double>(zy) - static_cast<double>(st.m)) *
+                          static_cast<double>(st.c)) / static_cast<double>(st.s);
+    *tok = y;
+    if (prob) *prob = static_cast<float>(p);
+  }
+  __syncthreads();
+}
+
+// Segment j's plain weight sum of row `prow`'s partials: s_j * exp2((m_j - m) * c), the partial's
+// sum rescaled to the row max.
+__device__ __forceinline__ double partial_seg_sum(const RowPartial* __restrict__ prow, int j,
+                                                  const SeqState& st) {
+  const RowPartial pj = prow[j];
+  const float f = pj.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((pj.m - st.m) * st.c);
+  return static_cast<double>(pj.s) * static_cast<double>(f);
+}
+
+// Segment j's sums published by a draw workgroup as four marked words (two doubles in halves);
+// false if they are not all there yet.
+__device__ __forceinline__ bool seg_words(const u64* __restrict__ w, double& sw, double& se) {
+  const u64 w0 = load_word(w), w1 = load_word(w + 1), e0 = load_word(w + 2), e1 = load_word(w + 3);
+  if (!(is_marked(w0) && is_marked(w1) && is_marked(e0) && is_marked(e1))) return false;
+  sw = __longlong_as_double(static_cast<long long>((static_cast<u64>(bits_of(w1)) << 32) | bits_of(w0)));
+  se = __longlong_as_double(static_cast<long long>((static_cast<u64>(bits_of(e1)) << 32) | bits_of(e0)));
+  return true;
+}
+
+// Polls of the pick's bounded wait for the other draw workgroups of its sequence.
+constexpr int kPickSpinLimit = 1 << 20;
+
+// ------------------------------------------------------------------------------------------
 // Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
 // by b0).  kPhase 0: every workgroup runs its sequence's accept scan (all waves merge partials,
 // wave 0 decides) and the chunk-0 workgroup writes the scan's outputs and the draw state; then
@@ -261,13 +409,18 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const float* __restrict__ uniforms, int b0, int K, int V, int S, int greedy_all,
     const RowPartial* __restrict__ partials, const Gather* __restrict__ gathers,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs) {
+    float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs,
+    u64* __restrict__ segw) {
   constexpr bool kFine = kPhase == 3;
+  // Grids of one resident round (phases 0 and 3) pick in this kernel; the split phases 1 and 2
+  // leave it to the pick kernel.
+  constexpr bool pick_here = kPhase == 0 || kPhase == 3;
   constexpr int kGroupsPerLane = kSeg / kGroup / 64 / (kFine ? kWaves : 1);  // scalar path
   __shared__ SeqState sh_st;
   __shared__ SegSums sh_fine[kFine ? kWaves : 1];
   __shared__ Stat sh_rows[kMaxRows];
   __shared__ StatD sh_rows_d[kMatch ? kMaxRows : 1];
+  __shared__ PickLds sh_pick;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Workgroup x of a sequence draws chunks x, x + gridDim.x, ...  Phase 0 scans and draws;
   // phase 1 only scans (one workgroup per sequence) and phase 2 only draws, reading the state
@@ -320,23 +473,40 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
   if (kPhase == 1 || st.mode == kNone) return;
   const long long row = static_cast<long long>(b) * (K + 1) + st.row;
   const int nseg = S * kSegPerChunk;
+  const LT* z = logits + row * V;
+  const int P = (nseg + 63) / 64;  // pick: lane l owns segments [l * P, l * P + P)
+  const int j0 = lane * P;
+  const long long slot = static_cast<long long>(b) * (K + 1) + st.row;
   if (st.mode == kBonus) {
     // A bonus draw (plain p, also every match-mode draw) needs no pass over the row: its weight
     // sum over 2048-token segment j is the streaming kernel's partial j of that row rescaled to
-    // the row max, s_j * exp2((m_j - m) * c).  The sequence's workgroups write them in parallel
-    // (one segment per thread) for the pick kernel.  Residuals are summed below exactly (a
-    // one-hot residual taken from the partials would subtract e(x) from its segment's sum and
-    // cancel when x dominates the row).
+    // the row max, s_j * exp2((m_j - m) * c).  Residuals are summed below exactly (a one-hot
+    // residual taken from the partials would subtract e(x) from its segment's sum and cancel when
+    // x dominates the row).
     const RowPartial* prow = partials + row * nseg;
+    if constexpr (pick_here) {
+      // The chunk-0 workgroup draws it right away.
+      if (!first) return;
+      if (wave == 0) {
+        double lw = 0.0;
+        for (int q = 0; q < P && j0 + q < nseg; ++q) lw += partial_seg_sum(prow, j0 + q, st);
+        find_draw_segment(lw, lw, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol], nseg,
+                          P, [&](int j, bool) { return partial_seg_sum(prow, j, st); }, sh_pick,
+                          lane);
+      }
+      __syncthreads();
+      scan_draw_segment<LT, kVec>(z, nullptr, partials, V, st, true, sh_pick, out_tokens + slot,
+                                  out_probs ? out_probs + slot : nullptr);
+      return;
+    }
+    // Otherwise the sequence's workgroups write them in parallel (one segment per thread) for
+    // the pick kernel.
     for (int j = blockIdx.x * kThreads + tid; j < nseg; j += gridDim.x * kThreads) {
-      const RowPartial pj = prow[j];
-      const float f = pj.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((pj.m - st.m) * st.c);
-      const double e = static_cast<double>(pj.s) * static_cast<double>(f);
+      const double e = partial_seg_sum(prow, j, st);
       segs[static_cast<long long>(b) * nseg + j] = SegSums{e, e};
     }
     return;
   }
-  const LT* z = logits + row * V;
   const float* q = st.mode == kResidual
                        ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
                        : nullptr;
@@ -394,38 +564,92 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     }
     lw = wave_total(lw);
     le = wave_total(le);
+    int segi = s * kSegPerChunk + wave;  // the wave's segment (coarse items)
     if constexpr (kFine) {
       if (lane == 0) sh_fine[wave] = SegSums{lw, le};
       __syncthreads();
-      if (tid == 0) {
-        SegSums a = sh_fine[0];
+      SegSums tot = sh_fine[0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-          a.w += sh_fine[w].w;
-          a.e += sh_fine[w].e;
-        }
-        segs[static_cast<long long>(b) * nseg + t] = a;
+      for (int w = 1; w < kWaves; ++w) {
+        tot.w += sh_fine[w].w;
+        tot.e += sh_fine[w].e;
       }
+      lw = tot.w;
+      le = tot.e;
+      segi = t;
       __syncthreads();  // sh_fine is reused by the next item
-    } else if (lane == 0) {
-      segs[(static_cast<long long>(b) * S + s) * kSegPerChunk + wave] = SegSums{lw, le};
     }
+    if (kFine ? tid < 4 : lane < 4) {
+      if constexpr (pick_here) {
+        // Four marked words for the sequence's picking workgroup: the two sums in halves.
+        const u64 bits = static_cast<u64>(__double_as_longlong((lane & 2) ? le : lw));
+        store_word(segw + (static_cast<long long>(b) * nseg + segi) * 4 + lane,
+                   marked(static_cast<uint32_t>((lane & 1) ? bits >> 32 : bits)));
+      } else if (lane == 0) {
+        segs[static_cast<long long>(b) * nseg + segi] = SegSums{lw, le};
+      }
+    }
+  }
+  if constexpr (!pick_here) return;
+  if (!first) return;
+  // The chunk-0 workgroup picks: it waits (bounded) for every segment's sums, finds the segment
+  // holding u * total and scans it.
+  if (wave == 0) {
+    const u64* sw = segw + static_cast<long long>(b) * nseg * 4;
+    double lw = 0.0, le = 0.0;
+    bool got = false;
+    for (int n = 0;; ++n) {
+      bool mine = true;
+      lw = le = 0.0;
+      for (int q = 0; q < P && j0 + q < nseg; ++q) {
+        double w, e;
+        if (seg_words(sw + (j0 + q) * 4, w, e)) {
+          lw += w;
+          le += e;
+        } else {
+          mine = false;
+        }
+      }
+      if (__ballot(!mine) == 0ull) { got = true; break; }
+      if (n >= kPickSpinLimit) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (got)
+      find_draw_segment(lw, le, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol], nseg, P,
+                        [&](int j, bool plain) {
+                          double w, e;
+                          seg_words(sw + j * 4, w, e);
+                          return plain ? e : w;
+                        },
+                        sh_pick, lane);
+    if (lane == 0) sh_pick.flag = got;
+  }
+  __syncthreads();
+  if (sh_pick.flag) {
+    scan_draw_segment<LT, kVec>(z, q, partials, V, st, false, sh_pick, out_tokens + slot,
+                                out_probs ? out_probs + slot : nullptr);
+  } else {
+    // The wait gave up (a sibling workgroup never ran): the sequence is reported invalid.
+    for (int i = tid; i <= K; i += kThreads) {
+      out_tokens[static_cast<long long>(b) * (K + 1) + i] = -1;
+      if (out_probs) out_probs[static_cast<long long>(b) * (K + 1) + i] = 0.f;
+    }
+    if (tid == 0) accept_len[b] = -1;
   }
 }
 
+// The pick of large draw grids (several resident rounds), one workgroup per sequence, after the
+// draw kernel has written every segment's sums.
 template <typename LT, bool kVec>
 __global__ __launch_bounds__(kThreads) void pick_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const float* __restrict__ uniforms, int B, int K, int V, int S,
     const SeqState* __restrict__ states, const SegSums* __restrict__ all_segs,
     int32_t* __restrict__ out_tokens, float* __restrict__ out_probs) {
-  __shared__ int sh_seg, sh_plain, sh_hit[kWaves], sh_lastpos[kWaves];
-  __shared__ float sh_zhit[kWaves], sh_zlast[kWaves];
-  __shared__ double sh_t, sh_base, sh_wtot[kWaves];
+  __shared__ PickLds ps;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nseg = S * kSegPerChunk;
-  // Lane l owns the contiguous segments [l * P, l * P + P).
-  const int P = (nseg + 63) / 64;
+  const int P = (nseg + 63) / 64;  // lane l owns the contiguous segments [l * P, l * P + P)
   const int j0 = lane * P;
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     const SegSums* segs = all_segs + static_cast<long long>(b) * nseg;
@@ -448,106 +672,17 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
       }
     }
     if (st.mode == kNone) continue;
+    if (wave == 0)
+      find_draw_segment(lw, le, read_lane_f(u_lane, st.ucol), nseg, P,
+                        [&](int j, bool plain) { return plain ? segs[j].e : segs[j].w; }, ps,
+                        lane);
+    __syncthreads();
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
-    const LT* z = logits + row * V;
-    // ---- The segment holding t = u * total: one fp64 scan of the lane totals. ----
-    if (wave == 0) {
-      const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
-      const bool plain = !(read_lane_d(iw, 63) > 0.0);  // empty residual: draw from p itself
-      const double inc = plain ? ie : iw;
-      const double own = plain ? le : lw;
-      const double R = read_lane_d(inc, 63);
-      const float u = read_lane_f(u_lane, st.ucol);
-      const double t = static_cast<double>(u) * R;
-      // The first lane whose running total passes t holds the segment; if rounding left t at
-      // the very top, the last lane with positive weight does.
-      const unsigned long long hit = __ballot(own > 0.0 && inc > t);
-      const unsigned long long pos = __ballot(own > 0.0);
-      const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
-                         : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
-      if (lane == hl) {
-        double run = inc - own;                   // running sum before the lane's segments
-        int seg = -1, lastpos = -1;
-        double base_seg = 0.0, base_last = 0.0;
-        for (int q = 0; q < P && j0 + q < nseg; ++q) {
-          const SegSums sq = segs[j0 + q];        // L1-resident: loaded above
-          const double v = plain ? sq.e : sq.w;
-          if (v > 0.0) {
-            if (run + v > t) { seg = j0 + q; base_seg = run; break; }
-            lastpos = j0 + q;
-            base_last = run;
-          }
-          run += v;
-        }
-        if (seg < 0) { seg = lastpos >= 0 ? lastpos : j0; base_seg = base_last; }
-        sh_seg = seg; sh_plain = plain; sh_t = t; sh_base = base_seg;
-      }
-    }
-    __syncthreads();
-    // ---- Scan the chosen segment in ascending token order. ----
-    const int seg = sh_seg;
-    const bool plain = sh_plain != 0;
-    const double t = sh_t;
-    const int sc = seg / kSegPerChunk, sg = seg % kSegPerChunk;
-    const int cc0 = sc * kChunk, cn = min(kChunk, V - cc0);
-    const int v0 = sg * kSeg + tid * kGroup;
-    const int cnt = min(kGroup, cn - v0);
-    const float* qs = (st.mode == kResidual && !plain)
-                          ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
-                          : nullptr;
-    float zg[kGroup], qg[kGroup], w[kGroup], gw, ge;
-    load_group<LT, kVec>(z, qs, segs, cc0 + v0, cnt, zg, qg);
-    group_weights(zg, qg, cc0 + v0, cnt, st, plain, w, gw, ge);
-    const double inc = wave_inclusive_scan(static_cast<double>(gw));
-    if (lane == 63) sh_wtot[wave] = inc;
-    __syncthreads();
-    double before = sh_base;
-    for (int k = 0; k < wave; ++k) before += sh_wtot[k];
-    before += inc - static_cast<double>(gw);
-    int hit = -1, lastpos = -1;
-    float zhit = 0.f, zlast = 0.f, run = 0.f;
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      run += w[j];
-      if (w[j] > 0.f) {
-        lastpos = cc0 + v0 + j;
-        zlast = zg[j];
-        if (hit < 0 && before + static_cast<double>(run) > t) { hit = cc0 + v0 + j; zhit = zg[j]; }
-      }
-    }
-    const unsigned long long hm = __ballot(hit >= 0);
-    const unsigned long long pm = __ballot(lastpos >= 0);
-    const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 0;
-    const int ll = pm ? 63 - __clzll(static_cast<long long>(pm)) : 0;
-    // hl and ll are wave-uniform: readlane, not a cross-lane shuffle through LDS.
-    const int wave_hit = hm ? __builtin_amdgcn_readlane(hit, hl) : -1;
-    const float wave_zhit = read_lane_f(zhit, hl);
-    const int wave_last = pm ? __builtin_amdgcn_readlane(lastpos, ll) : -1;
-    const float wave_zlast = read_lane_f(zlast, ll);
-    if (lane == 0) {
-      sh_hit[wave] = wave_hit; sh_zhit[wave] = wave_zhit;
-      sh_lastpos[wave] = wave_last; sh_zlast[wave] = wave_zlast;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int y = -1, lp = -1;
-      float zy = 0.f, zl = 0.f;
-      for (int k = 0; k < kWaves; ++k) {
-        if (y < 0 && sh_hit[k] >= 0) { y = sh_hit[k]; zy = sh_zhit[k]; }
-        if (sh_lastpos[k] >= 0) { lp = sh_lastpos[k]; zl = sh_zlast[k]; }
-      }
-      // Rounding left t at the very top of the segment: take its last positive token.
-      if (y < 0) {
-        y = lp >= 0 ? lp : cc0 + sg * kSeg;
-        zy = lp >= 0 ? zl : load_logit(z, y);
-      }
-      const double p = exp2((static_cast<double>(zy) - static_cast<double>(st.m)) *
-                            static_cast<double>(st.c)) / static_cast<double>(st.s);
-      const long long slot = static_cast<long long>(b) * (K + 1) + st.row;
-      out_tokens[slot] = y;
-      if (out_probs) out_probs[slot] = static_cast<float>(p);
-    }
-    __syncthreads();
+    const float* q = st.mode == kResidual
+                         ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
+                         : nullptr;
+    scan_draw_segment<LT, kVec>(logits + row * V, q, all_segs, V, st, false, ps, out_tokens + row,
+                                out_probs ? out_probs + row : nullptr);
   }
 }
 
@@ -575,6 +710,7 @@ hipError_t launch_typed(const LaunchArgs& a) {
   ws.gathers = reinterpret_cast<Gather*>(base + L.gathers);
   ws.states = reinterpret_cast<SeqState*>(base + L.states);
   ws.segs = reinterpret_cast<SegSums*>(base + L.segs);
+  ws.segw = reinterpret_cast<u64*>(base + L.segw);
   const LT* logits = static_cast<const LT*>(a.logits);
   const int S = num_chunks(a.V);
   const bool vec_stats = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
@@ -583,9 +719,25 @@ hipError_t launch_typed(const LaunchArgs& a) {
                         (a.draft_probs == nullptr ||
                          reinterpret_cast<uintptr_t>(a.draft_probs) % 16 == 0);
   hipError_t err;
+  // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
+  // partials): the chunk-0 workgroups that run the scan are enough.
+  // Otherwise one workgroup per chunk of the row to draw from.
+  // A draw grid of more than one resident round (about six 256-thread workgroups per CU on 256
+  // CUs) scans once per sequence in a separate pass instead, and a pick kernel draws after it.
+  // Smaller grids pick inside the draw kernel: the chunk-0 workgroup of a sequence waits for its
+  // siblings' segment sums (at most one waiting workgroup per sequence, so never more than the
+  // chip holds) and draws.
+  // A draw grid smaller than the chip (up to 256 chunks) takes one workgroup per 2048-token
+  // segment instead of one per chunk.
+  constexpr long long kDrawRound = 1536;
+  constexpr long long kFineMax = 256;
+  const bool match = a.match && !a.greedy_all;
+  const bool draws = !(a.greedy_all || match);
+  const bool split = draws && static_cast<long long>(a.B) * S > kDrawRound;
+  const bool fine = draws && static_cast<long long>(a.B) * S <= kFineMax;
+  u64* segw = split ? nullptr : ws.segw;
   // The streaming kernel: grid (chunk, row within sequence, sequence), at most 65535 sequences
   // per launch.  With measurement events, the dispatches record them (first start, last end).
-  const bool match = a.match && !a.greedy_all;
   auto stats = match ? (vec_stats ? stats_kernel<LT, true, true> : stats_kernel<LT, false, true>)
                      : (vec_stats ? stats_kernel<LT, true, false> : stats_kernel<LT, false, false>);
   for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
@@ -595,11 +747,11 @@ hipError_t launch_typed(const LaunchArgs& a) {
     if (ev0 || ev1)
       hipExtLaunchKernelGGL(stats, grid, dim3(kThreads), 0, a.stream, ev0, ev1, 0, logits,
                             a.draft_probs, a.proposed, a.num_draft, a.temperature, b0, a.K, a.V,
-                            S, a.greedy_all, ws.partials, ws.gathers);
+                            S, a.greedy_all, ws.partials, ws.gathers, segw);
     else
       stats<<<grid, kThreads, 0, a.stream>>>(logits, a.draft_probs, a.proposed, a.num_draft,
                                              a.temperature, b0, a.K, a.V, S, a.greedy_all,
-                                             ws.partials, ws.gathers);
+                                             ws.partials, ws.gathers, segw);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // Accept scan + draw sums: one workgroup per (chunk, sequence); greedy-only calls need just
@@ -611,18 +763,6 @@ hipError_t launch_typed(const LaunchArgs& a) {
            : phase == 2 ? accept_draw_for<LT, 2>(match, vec_draw)
                         : accept_draw_for<LT, 3>(match, vec_draw);
   };
-  // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
-  // partials): the chunk-0 workgroups that run the scan are enough.
-  // Otherwise one workgroup per chunk of the row to draw from.
-  // A draw grid of more than one resident round (about six 256-thread workgroups per CU on 256
-  // CUs) scans once per sequence in a separate pass instead.
-  // A draw grid smaller than the chip (up to 256 chunks) takes one workgroup per 2048-token
-  // segment instead of one per chunk.
-  constexpr long long kDrawRound = 1536;
-  constexpr long long kFineMax = 256;
-  const bool draws = !(a.greedy_all || match);
-  const bool split = draws && static_cast<long long>(a.B) * S > kDrawRound;
-  const bool fine = draws && static_cast<long long>(a.B) * S <= kFineMax;
   const int phases[2] = {split ? 1 : (fine ? 3 : 0), 2};
   for (int ph = 0; ph < (split ? 2 : 1); ++ph) {
     const int phase = phases[ph];
@@ -632,11 +772,11 @@ hipError_t launch_typed(const LaunchArgs& a) {
       accept_draw(phase)<<<grid, kThreads, 0, a.stream>>>(
           logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms,
           b0, a.K, a.V, S, a.greedy_all, ws.partials, ws.gathers, a.accept_len,
-          a.out_tokens, a.out_probs, ws.states, ws.segs);
+          a.out_tokens, a.out_probs, ws.states, ws.segs, ws.segw);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
-  if (a.greedy_all) return hipSuccess;
+  if (!split) return hipSuccess;
   if (vec_draw)
     pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
@@ -664,6 +804,8 @@ WorkspaceLayout workspace_layout(int B, int K, int V) {
   off = align16(off + static_cast<size_t>(B) * sizeof(SeqState));
   L.segs = off;
   off = align16(off + static_cast<size_t>(B) * S * kSegPerChunk * sizeof(SegSums));
+  L.segw = off;
+  off = align16(off + static_cast<size_t>(B) * S * kSegPerChunk * 4 * sizeof(unsigned long long));
   L.total = off;
   return L;
 }

@@ -539,4 +539,22 @@ template <> struct DrawVec<float> {
   }
 };
 
+// Hand-off words.  A value one workgroup hands to another inside a launch travels in a 64-bit word
+// whose upper half is kMark: the producer issues a coherent store and goes on, the consumer polls
+// (bounded) until every word it needs carries the mark.  A 64-bit store is single-copy atomic, so
+// a marked word never pairs a new mark with stale data.  Whoever consumes the words puts them back
+// to zero (or a kernel that runs before the producers does).
+typedef unsigned long long u64;
+constexpr uint32_t kMark = 0x5ec0da7au;
+
+__device__ __forceinline__ u64 marked(uint32_t v) { return (static_cast<u64>(kMark) << 32) | v; }
+__device__ __forceinline__ bool is_marked(u64 w) { return static_cast<uint32_t>(w >> 32) == kMark; }
+__device__ __forceinline__ uint32_t bits_of(u64 w) { return static_cast<uint32_t>(w); }
+__device__ __forceinline__ u64 load_word(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_word(u64* p, u64 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace specdec
