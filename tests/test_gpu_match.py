@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.parity import compare
+from oracle.parity import boundary_limit, compare, expected_boundary
 from speculative_decoding_verification_specdec_amd import inputs_to_device, specdec_verify_match
 from speculative_decoding_verification_specdec_amd import inputs as gen
 
@@ -33,10 +33,11 @@ def check(inp, rows=None, d=None):
     if rows is not None:
         rows = np.asarray(rows)
         acc, tok, prb, sub = acc[rows], tok[rows], prb[rows], inp.subset(rows)
-    rep = compare(sub, ref, acc, tok, prb)
+    rep = compare(sub, ref, acc, tok, prb, mode="match")
     print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
     assert rep["mismatch"] == 0, rep["details"]
-    assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+    limit = boundary_limit(expected_boundary(sub, ref, mode="match"))
+    assert rep["boundary"] <= limit, (rep, limit)
     return rep, acc
 
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.parity import compare
+from oracle.parity import boundary_limit, compare, expected_boundary
 from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
                                                            SPECDEC_PATH_STREAMING,
                                                            SPECDEC_SMALL_V_MAX, inputs_to_device,
@@ -42,10 +42,11 @@ def check(inp, rows=None, max_boundary=None, path=SPECDEC_PATH_AUTO):
     rep = compare(sub, ref, acc, tok, prb)
     print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
     assert rep["mismatch"] == 0, rep["details"]
-    # A draw lands within 1e-6 of a CDF break with probability ~2e-6 / (its token's share of
-    # the mass); with 1e5-token rows that is a few percent of sampled rows.
-    limit = max_boundary if max_boundary is not None else max(3, rep["rows"] // 20)
-    assert rep["boundary"] <= limit, rep
+    # Boundary rows are as rare as chance makes them: the measure of the uniforms within 1e-6 of
+    # the thresholds each row evaluates, summed over the rows, bounds their count.
+    limit = (max_boundary if max_boundary is not None
+             else boundary_limit(expected_boundary(sub, ref)))
+    assert rep["boundary"] <= limit, (rep, limit)
     return rep
 
 
@@ -264,3 +265,27 @@ def test_call_on_a_side_stream_keeps_its_temporaries():
     del junk
     rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
     assert rep["mismatch"] == 0, rep["details"]
+
+
+# A drafter almost equal to the target: q = softmax((z + N(0, 0.05^2)) / T) at the row's own
+# temperature, so each draft survives with probability about 0.98 and the few rejections draw
+# from a residual max(0, p - q) whose total is a few hundredths of p's.  That is where the
+# residual weights cancel the most; the draws must still land on the oracle's tokens.
+NEAR_IDENTICAL = {
+    "near_identical_batch": lambda: gen.make_batch(256, 5, 128256, seed=71, draft_scale=1.0,
+                                                   draft_sigma=0.05, draft_at_row_temp=True,
+                                                   name="near_identical_batch"),
+    "near_identical_small_vocab": lambda: gen.make_batch(4096, 5, 500, seed=72, draft_scale=1.0,
+                                                         draft_sigma=0.05, draft_at_row_temp=True,
+                                                         name="near_identical_small_vocab"),
+}
+
+
+@pytest.mark.parametrize("name", list(NEAR_IDENTICAL))
+def test_parity_near_identical_drafter(name):
+    inp = NEAR_IDENTICAL[name]()
+    rep = check(inp)
+    ref = oracle.verify(inp)
+    rejected = int(((ref.accept_len >= 0) & (ref.accept_len < inp.draft_counts())).sum())
+    print("[rejections]", rejected, flush=True)
+    assert rejected >= 20

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.parity import compare
+from oracle.parity import boundary_limit, compare, expected_boundary
 from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
                                                            SPECDEC_PATH_STREAMING,
                                                            SPECDEC_SMALL_V_MAX, inputs_to_device,
@@ -52,7 +52,8 @@ def test_random_shape_parity(seed):
         rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
         print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
         assert rep["mismatch"] == 0, rep["details"]
-        assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+        limit = boundary_limit(expected_boundary(inp, ref))
+        assert rep["boundary"] <= limit, (rep, limit)
 
 
 @pytest.mark.parametrize("seed", range(0, N_CASES, 2))
@@ -67,10 +68,11 @@ def test_random_shape_match_mode_parity(seed):
     acc, tok, prb = specdec_verify_match(d["logits"], d["proposed"], d["temperature"],
                                          d["uniforms"], num_draft=d["num_draft"])
     torch.cuda.synchronize()
-    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy(), mode="match")
     print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
     assert rep["mismatch"] == 0, rep["details"]
-    assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+    limit = boundary_limit(expected_boundary(inp, ref, mode="match"))
+    assert rep["boundary"] <= limit, (rep, limit)
 
 
 @pytest.mark.parametrize("seed", range(1, N_CASES, 2))

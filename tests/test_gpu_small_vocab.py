@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.parity import compare
+from oracle.parity import boundary_limit, compare, expected_boundary
 from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
                                                            SPECDEC_PATH_SMALL_VOCAB,
                                                            SPECDEC_PATH_STREAMING,
@@ -87,7 +87,8 @@ def check(inp, path, ref=None):
     rep = compare(inp, ref, acc, tok, prb)
     print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
     assert rep["mismatch"] == 0, rep["details"]
-    assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+    limit = boundary_limit(expected_boundary(inp, ref))
+    assert rep["boundary"] <= limit, (rep, limit)
     return acc, tok, prb
 
 
@@ -164,7 +165,8 @@ def test_small_vocab_match_mode_parity(name):
                                          d["uniforms"], num_draft=d["num_draft"])
     torch.cuda.synchronize()
     ref = oracle.verify_match(inp)
-    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy(), mode="match")
     print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
     assert rep["mismatch"] == 0, rep["details"]
-    assert rep["boundary"] <= max(3, rep["rows"] // 20), rep
+    limit = boundary_limit(expected_boundary(inp, ref, mode="match"))
+    assert rep["boundary"] <= limit, (rep, limit)

@@ -111,3 +111,33 @@ def test_invalid_rows():
     assert ref.accept_len[1:5].tolist() == [-1] * 4
     assert (ref.out_tokens[1:5] == -1).all() and (ref.out_probs[1:5] == 0).all()
     assert ref.accept_len[0] >= 0 and ref.accept_len[5] >= 0
+
+
+def test_out_probs_are_the_target_probability_of_each_emitted_token():
+    # Every emitted slot reports softmax(z_i / T)(token_i) of its own row i -- scipy's softmax
+    # of the raw logit row, at T = 1 for greedy rows -- and unused slots report 0.  A kept draft
+    # and a mismatch token are both pinned, so reporting p(x_i) instead of p(y_i) at a mismatch,
+    # or another row's p, fails here.
+    import scipy.special
+    inp = gen.make_batch(40, 4, 400, seed=611, dtype="f32", greedy_frac=0.25, ragged=True,
+                         draft_sigma=0.3, draft_at_row_temp=True)
+    ref = verify_match(inp)
+    kept = mismatch = 0
+    for b in range(inp.B):
+        A = int(ref.accept_len[b])
+        assert A >= 0
+        T = float(inp.temperature[b]) or 1.0
+        for i in range(inp.K + 1):
+            if i > A:
+                assert ref.out_tokens[b, i] == -1 and ref.out_probs[b, i] == 0.0
+                continue
+            y = int(ref.out_tokens[b, i])
+            want = scipy.special.softmax(inp.logits[b, i].astype(np.float64) / T)[y]
+            assert ref.out_probs[b, i] == pytest.approx(want, rel=1e-12, abs=0.0)
+            if i < A:
+                kept += 1
+                assert y == int(inp.proposed[b, i])
+            elif A < inp.draft_counts()[b]:
+                mismatch += 1
+                assert y != int(inp.proposed[b, i])
+    assert kept > 10 and mismatch > 10
