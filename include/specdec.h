@@ -66,7 +66,9 @@ typedef enum {
   SPECDEC_ERR_DTYPE = -3,     /* logits_dtype is not a specdec_dtype                      */
   SPECDEC_ERR_ALIGN = -4,     /* a tensor base is not aligned to its element size         */
   SPECDEC_ERR_WORKSPACE = -5, /* workspace NULL or smaller than specdec_workspace_size()  */
-  SPECDEC_ERR_LAUNCH = -6     /* a kernel launch or event record failed                   */
+  SPECDEC_ERR_LAUNCH = -6,    /* a kernel launch or event record failed                   */
+  SPECDEC_ERR_SCRATCH = -7    /* specdec_verify_noalloc: the sizes need more workspace    */
+                              /* than its built-in scratch (SPECDEC_NOALLOC_SCRATCH_BYTES) */
 } specdec_status;
 
 typedef enum {
@@ -117,6 +119,29 @@ specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
                               int32_t B, int32_t K, int32_t V,
                               int32_t* accept_len, int32_t* out_tokens, float* out_probs,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* specdec_verify without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP-graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * workspace is a file-scope device array of SPECDEC_NOALLOC_SCRATCH_BYTES (32 MiB) that each
+ * device holds for the life of the process; its address is looked up once per device, on the
+ * first call made with that device current.  The call allocates nothing (no hipMalloc, no
+ * library allocation).  Arguments, outputs, data errors and results are those of
+ * specdec_verify (automatic path) with the same inputs.  Returns SPECDEC_ERR_SCRATCH, before
+ * any launch, when specdec_workspace_size(B, K, V) exceeds the scratch (for example B = 64,
+ * K = 5, V = 128256 needs about 1.0 MB; B = 512, K = 8, V = 128256 about 11 MB).  Every call
+ * on one device shares that device's scratch: calls that overlap in time on one device (other
+ * streams, other threads) race; consecutive calls on one stream do not. */
+#define SPECDEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+size_t specdec_noalloc_scratch_bytes(void);
+
+specdec_status specdec_verify_noalloc(const void* target_logits, int32_t logits_dtype,
+                                      const float* draft_probs, const uint8_t* draft_onehot,
+                                      const int32_t* proposed, const int32_t* num_draft,
+                                      const float* temperature, const float* uniforms,
+                                      int32_t B, int32_t K, int32_t V,
+                                      int32_t* accept_len, int32_t* out_tokens, float* out_probs,
+                                      void* stream);
 
 /* Greedy-only verify: every row is treated as temperature 0 (accept x_i iff it is the
  * lowest-index argmax of z_i; emit the argmax at the first mismatch or as the bonus).

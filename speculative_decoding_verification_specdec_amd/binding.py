@@ -69,6 +69,11 @@ def load_library():
     lib.specdec_verify_match.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp,
                                          sz, vp]
     lib.specdec_verify_match.restype = i32
+    lib.specdec_verify_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp,
+                                           vp, vp]
+    lib.specdec_verify_noalloc.restype = i32
+    lib.specdec_noalloc_scratch_bytes.argtypes = []
+    lib.specdec_noalloc_scratch_bytes.restype = sz
     lib.specdec_workspace_size.argtypes = [i32, i32, i32]
     lib.specdec_workspace_size.restype = sz
     lib.specdec_ngram_workspace_size.argtypes = [i32, i32]
@@ -220,6 +225,45 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
         opts = _options(hot_events, path, spin_limit)
         status = lib.specdec_verify_ex(*args, ctypes.byref(opts))
     _raise(status, "specdec_verify")
+    return acc, tok, prb
+
+
+def specdec_verify_noalloc(target_logits: torch.Tensor, draft_probs: torch.Tensor | None,
+                           proposed: torch.Tensor | None, temperature: torch.Tensor,
+                           uniforms: torch.Tensor, *, draft_onehot: torch.Tensor | None = None,
+                           num_draft: torch.Tensor | None = None, out, stream=None):
+    """specdec_verify through the entry point that allocates nothing: its workspace is the
+    library's built-in device scratch (``out`` = (accept_len, out_tokens, out_probs or None) is
+    required, so that this call creates no tensor either).  Shapes as for specdec_verify."""
+    lib = load_library()
+    if target_logits.dim() != 3:
+        raise SpecdecError("target_logits must be [B, K+1, V]")
+    B, K1, V = (int(s) for s in target_logits.shape)
+    K = K1 - 1
+    dev = target_logits.device
+    if target_logits.dtype == torch.bfloat16:
+        dt = SPECDEC_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = SPECDEC_F32
+    else:
+        raise SpecdecError(f"target_logits dtype {target_logits.dtype} is not bf16/fp32")
+    if not target_logits.is_contiguous():
+        raise SpecdecError("target_logits must be contiguous")
+    _check(draft_probs, "draft_probs", torch.float32, (B, K, V), dev, optional=True)
+    _check(proposed, "proposed", torch.int32, (B, K), dev, optional=(K == 0))
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    _check(draft_onehot, "draft_onehot", torch.uint8, (B,), dev, optional=True)
+    _check(num_draft, "num_draft", torch.int32, (B,), dev, optional=True)
+    acc, tok, prb = out
+    _check(acc, "accept_len", torch.int32, (B,), dev)
+    _check(tok, "out_tokens", torch.int32, (B, K + 1), dev)
+    _check(prb, "out_probs", torch.float32, (B, K + 1), dev, optional=True)
+    status = lib.specdec_verify_noalloc(_ptr(target_logits), dt, _ptr(draft_probs),
+                                        _ptr(draft_onehot), _ptr(proposed), _ptr(num_draft),
+                                        _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc),
+                                        _ptr(tok), _ptr(prb), _stream_handle(stream))
+    _raise(status, "specdec_verify_noalloc")
     return acc, tok, prb
 
 

@@ -212,6 +212,8 @@ const char* specdec_status_string(int32_t status) {
     case SPECDEC_ERR_ALIGN: return "a tensor is not aligned to its element size";
     case SPECDEC_ERR_WORKSPACE: return "workspace too small";
     case SPECDEC_ERR_LAUNCH: return "kernel launch failed";
+    case SPECDEC_ERR_SCRATCH:
+      return "sizes need more workspace than specdec_verify_noalloc's built-in scratch";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,65 @@
+// specdec_verify_noalloc: specdec_verify with the workspace in a file-scope device array instead
+// of a caller buffer, for callers that cannot allocate device memory (code under HIP-graph capture,
+// tight serving loops, harnesses that forbid allocation).  Declared in include/specdec.h.
+//
+// The array `scratch` holds SPECDEC_NOALLOC_SCRATCH_BYTES per device for the life of the process.
+// In host code its name is only a host-side stand-in, so each device's address is looked up once
+// (hipGetSymbolAddress, with that device current, on the first call there) and only that address
+// is handed to the kernels.  Every call on a device shares that device's array: calls that
+// overlap in time on one device race (the verify kernels need no initialised workspace, so
+// consecutive calls do not).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "specdec.h"
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[SPECDEC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+// This device's address of `scratch`, looked up on the first call on the device; null on error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t specdec_noalloc_scratch_bytes(void) { return SPECDEC_NOALLOC_SCRATCH_BYTES; }
+
+specdec_status specdec_verify_noalloc(const void* target_logits, int32_t logits_dtype,
+                                      const float* draft_probs, const uint8_t* draft_onehot,
+                                      const int32_t* proposed, const int32_t* num_draft,
+                                      const float* temperature, const float* uniforms, int32_t B,
+                                      int32_t K, int32_t V, int32_t* accept_len,
+                                      int32_t* out_tokens, float* out_probs, void* stream) {
+  // Sizes first: a call whose workspace would not fit the array is refused before anything
+  // touches the device.
+  const size_t need = specdec_workspace_size(B, K, V);
+  if (B > 0 && need == 0) return SPECDEC_ERR_SHAPE;
+  if (need > SPECDEC_NOALLOC_SCRATCH_BYTES) return SPECDEC_ERR_SCRATCH;
+  if (B == 0) return SPECDEC_OK;
+  void* ws = scratch_address();
+  if (ws == nullptr) return SPECDEC_ERR_LAUNCH;
+  return specdec_verify(target_logits, logits_dtype, draft_probs, draft_onehot, proposed,
+                        num_draft, temperature, uniforms, B, K, V, accept_len, out_tokens,
+                        out_probs, ws, SPECDEC_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"

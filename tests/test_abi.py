@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.specdec_version() >= 100
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert lib.specdec_status_string(s)
     assert lib.specdec_status_string(-99) == b"unknown status"
 
