@@ -41,7 +41,9 @@
  *     (rows 0..k_b) holds a NaN or +inf or is all -inf; a proposed id in slots < k_b is
  *     outside [0, V); for a sampled row a used uniform (columns < k_b and column K) is
  *     outside [0, 1); or for a sampled model-draft row a gathered q_i(x_i) is negative or
- *     not finite, or draft_probs is NULL.
+ *     not finite, draft_probs is NULL, or -- at a rejection -- the rejected slot's draft row
+ *     q_j (the one row the residual draw reads) holds an entry that is negative or not
+ *     finite.
  *   - Padded rows and slots never influence a result: draft rows k_b..K-1 are never read;
  *     logit rows k_b+1..K (the small-vocabulary path loads rows 0..K together when K < 8) and
  *     proposed and uniform columns k_b..K-1 may be loaded (they lie inside the [B, K+1, V],

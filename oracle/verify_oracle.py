@@ -52,7 +52,10 @@ Readings where the pages leave a step open:
       a used logit row (0..k_b) with a NaN or +inf entry, or with every entry
       -inf; a proposed id outside [0, V) in slots < k_b; for sampled rows a
       used uniform outside [0, 1); for sampled model-draft rows a gathered
-      q_i(x_i) that is negative or not finite, or no draft tensor at all.
+      q_i(x_i) that is negative or not finite, or no draft tensor at all; and,
+      at a model-draft rejection, any entry of the rejected slot's draft row
+      q_i (the row the residual draw reads) that is negative or not finite.
+      Draft rows the round never reads are never checked.
       -inf logits are zero-mass tokens.
   R11 k_b = 0 is allowed: one plain sample (or argmax) from row 0.
   R12 out_probs of a greedy row report softmax at T = 1 of the raw logits.
@@ -184,7 +187,10 @@ def verify_row(logits, logits_dtype, draft_probs, draft_onehot, proposed, num_dr
         if u * qx < px:
             tokens[i], probs[i] = x, px
             continue
-        # First rejection: replacement from norm(max(0, p - q)); the round ends.
+        # First rejection: replacement from norm(max(0, p - q)); the round ends.  The draft row
+        # read here must be a vector of probabilities (R10).
+        if not onehot and not bool(np.all(np.isfinite(q) & (q >= 0.0))):
+            return _row_invalid(K + 1)
         r = p.copy() if buggy else np.maximum(p - q, 0.0)
         if not r.sum() > 0.0:            # R6
             r = p

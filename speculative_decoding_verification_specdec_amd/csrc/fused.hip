@@ -356,7 +356,8 @@ __device__ __forceinline__ bool segment_sums(const KArgs& a, const u64* rec, con
 // section "Amostragem especulativa em numpy, com prova": the first running sum above u times the
 // total, over ascending token id), first step: one fp64 DPP scan over the segment sums (wave 0)
 // finds the segment holding u * total (plain p when a residual's total is not positive); the
-// result is left in sh.  False (in every thread) if a segment sum did not arrive in time.
+// result is left in sh.  False (in every thread) if a segment sum did not arrive in time, or if
+// the residual's total is NaN.
 __device__ bool find_segment(const KArgs& a, Shared& sh, const u64* rec, int b, const SeqState& st,
                              bool from_partials) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -376,7 +377,11 @@ __device__ bool find_segment(const KArgs& a, Shared& sh, const u64* rec, int b, 
     }
     const bool all_got = __ballot(!got) == 0ull;
     const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
-    const bool plain = !(read_lane_d(iw, 63) > 0.0);  // empty residual: draw from p itself
+    const double total_w = read_lane_d(iw, 63);
+    // A NaN total (a draft row holding a value that is not a probability): nothing to draw, the
+    // sequence is reported invalid.
+    const bool drawable = total_w == total_w;
+    const bool plain = !(total_w > 0.0);  // empty residual: draw from p itself
     const double inc = plain ? ie : iw;
     const double own = plain ? le : lw;
     const double R = read_lane_d(inc, 63);
@@ -387,7 +392,7 @@ __device__ bool find_segment(const KArgs& a, Shared& sh, const u64* rec, int b, 
     const unsigned long long pos = __ballot(own > 0.0);
     const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
                        : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
-    if (lane == hl) {
+    if (drawable && lane == hl) {
       double run = inc - own;  // running sum before the lane's segments
       int seg = -1, lastpos = -1;
       double base_seg = 0.0, base_last = 0.0;
@@ -405,7 +410,7 @@ __device__ bool find_segment(const KArgs& a, Shared& sh, const u64* rec, int b, 
       if (seg < 0) { seg = lastpos >= 0 ? lastpos : j0; base_seg = base_last; }
       sh.seg = seg; sh.plain = plain; sh.t = t; sh.base = base_seg;
     }
-    if (lane == 0) sh.flag = all_got;
+    if (lane == 0) sh.flag = all_got && drawable;
   }
   __syncthreads();
   return sh.flag != 0;

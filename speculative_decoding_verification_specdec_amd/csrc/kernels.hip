@@ -263,13 +263,17 @@ struct PickLds {
 
 // First step, in wave 0: lane l holds the sums (lw: the draw's weights; le: those of p) of its
 // segments [l * P, l * P + P); seg_at(j, plain) gives segment j's sum again.  Leaves the segment,
-// the target u * total and the running sum before the segment in ps.
+// the target u * total and the running sum before the segment in ps.  Returns false (in every
+// lane) when the weights' total is NaN -- a draft row holding a value that is not a probability
+// -- and the sequence is to be reported invalid.
 template <typename SegAt>
-__device__ __forceinline__ void find_draw_segment(double lw, double le, float u, int nseg, int P,
+__device__ __forceinline__ bool find_draw_segment(double lw, double le, float u, int nseg, int P,
                                                   SegAt seg_at, PickLds& ps, int lane) {
   const int j0 = lane * P;
   const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
-  const bool plain = !(read_lane_d(iw, 63) > 0.0);  // empty residual: draw from p itself
+  const double total_w = read_lane_d(iw, 63);
+  if (total_w != total_w) return false;
+  const bool plain = !(total_w > 0.0);  // empty residual: draw from p itself
   const double inc = plain ? ie : iw;
   const double own = plain ? le : lw;
   const double R = read_lane_d(inc, 63);
@@ -296,6 +300,7 @@ __device__ __forceinline__ void find_draw_segment(double lw, double le, float u,
     if (seg < 0) { seg = lastpos >= 0 ? lastpos : j0; base_seg = base_last; }
     ps.seg = seg; ps.plain = plain; ps.t = t; ps.base = base_seg;
   }
+  return true;
 }
 
 // Second step, the whole workgroup (after a barrier): scan segment ps.seg of row z (draft row
@@ -490,9 +495,10 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
       if (wave == 0) {
         double lw = 0.0;
         for (int q = 0; q < P && j0 + q < nseg; ++q) lw += partial_seg_sum(prow, j0 + q, st);
-        find_draw_segment(lw, lw, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol], nseg,
-                          P, [&](int j, bool) { return partial_seg_sum(prow, j, st); }, sh_pick,
-                          lane);
+        // (Sums of p, rescaled partials of a validated row: never NaN.)
+        (void)find_draw_segment(lw, lw, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol],
+                                nseg, P, [&](int j, bool) { return partial_seg_sum(prow, j, st); },
+                                sh_pick, lane);
       }
       __syncthreads();
       scan_draw_segment<LT, kVec>(z, nullptr, partials, V, st, true, sh_pick, out_tokens + slot,
@@ -614,22 +620,25 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
       if (n >= kPickSpinLimit) break;
       __builtin_amdgcn_s_sleep(1);
     }
+    bool drawable = false;
     if (got)
-      find_draw_segment(lw, le, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol], nseg, P,
-                        [&](int j, bool plain) {
-                          double w, e;
-                          seg_words(sw + j * 4, w, e);
-                          return plain ? e : w;
-                        },
-                        sh_pick, lane);
-    if (lane == 0) sh_pick.flag = got;
+      drawable = find_draw_segment(lw, le, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol],
+                                   nseg, P,
+                                   [&](int j, bool plain) {
+                                     double w, e;
+                                     seg_words(sw + j * 4, w, e);
+                                     return plain ? e : w;
+                                   },
+                                   sh_pick, lane);
+    if (lane == 0) sh_pick.flag = drawable;
   }
   __syncthreads();
   if (sh_pick.flag) {
     scan_draw_segment<LT, kVec>(z, q, partials, V, st, false, sh_pick, out_tokens + slot,
                                 out_probs ? out_probs + slot : nullptr);
   } else {
-    // The wait gave up (a sibling workgroup never ran): the sequence is reported invalid.
+    // The wait gave up (a sibling workgroup never ran), or the draft row holds a value that is
+    // not a probability: the sequence is reported invalid.
     for (int i = tid; i <= K; i += kThreads) {
       out_tokens[static_cast<long long>(b) * (K + 1) + i] = -1;
       if (out_probs) out_probs[static_cast<long long>(b) * (K + 1) + i] = 0.f;
@@ -645,7 +654,8 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     const LT* __restrict__ logits, const float* __restrict__ draft_probs,
     const float* __restrict__ uniforms, int B, int K, int V, int S,
     const SeqState* __restrict__ states, const SegSums* __restrict__ all_segs,
-    int32_t* __restrict__ out_tokens, float* __restrict__ out_probs) {
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ out_probs) {
   __shared__ PickLds ps;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nseg = S * kSegPerChunk;
@@ -672,11 +682,25 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
       }
     }
     if (st.mode == kNone) continue;
-    if (wave == 0)
-      find_draw_segment(lw, le, read_lane_f(u_lane, st.ucol), nseg, P,
-                        [&](int j, bool plain) { return plain ? segs[j].e : segs[j].w; }, ps,
-                        lane);
+    if (wave == 0) {
+      const bool ok = find_draw_segment(lw, le, read_lane_f(u_lane, st.ucol), nseg, P,
+                                        [&](int j, bool plain) {
+                                          return plain ? segs[j].e : segs[j].w;
+                                        },
+                                        ps, lane);
+      if (lane == 0) ps.flag = ok;
+    }
     __syncthreads();
+    if (!ps.flag) {
+      // The draft row holds a value that is not a probability: the sequence is invalid.
+      for (int i = tid; i <= K; i += kThreads) {
+        out_tokens[static_cast<long long>(b) * (K + 1) + i] = -1;
+        if (out_probs) out_probs[static_cast<long long>(b) * (K + 1) + i] = 0.f;
+      }
+      if (tid == 0) accept_len[b] = -1;
+      __syncthreads();  // ps is rewritten for the next sequence
+      continue;
+    }
     const long long row = static_cast<long long>(b) * (K + 1) + st.row;
     const float* q = st.mode == kResidual
                          ? draft_probs + (static_cast<long long>(b) * K + st.row) * V
@@ -780,11 +804,11 @@ hipError_t launch_typed(const LaunchArgs& a) {
   if (vec_draw)
     pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
-        a.out_tokens, a.out_probs);
+        a.accept_len, a.out_tokens, a.out_probs);
   else
     pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
         logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
-        a.out_tokens, a.out_probs);
+        a.accept_len, a.out_tokens, a.out_probs);
   return hipGetLastError();
 }
 

@@ -496,7 +496,12 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
     // Weight of token v (lane-local value z, draft probability q); e returns s * p(v).
     auto weight = [&](float zv, float qq, int v, float& e) {
       e = v < V ? __builtin_amdgcn_exp2f((zv - sA.m) * c) : 0.f;
-      if (residual && model) return v < V ? fmaxf(0.f, fmaf(-sA.s, qq, e)) : 0.f;
+      // A draft probability that is negative, infinite or NaN gives a NaN weight (and total):
+      // the sequence is reported invalid below.
+      if (residual && model)
+        return v < V ? ((qq >= 0.f && qq <= __FLT_MAX__) ? fmaxf(0.f, fmaf(-sA.s, qq, e))
+                                                         : __builtin_nanf(""))
+                     : 0.f;
       if (residual) return v == excl ? 0.f : e;
       return e;
     };
@@ -521,6 +526,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_verify_kernel(
       R += tot_w[j];
       E += tot_e[j];
     }
+    if (R != R) ok = false;         // a draft row that is not a probability: invalid
     const bool plain = !(R > 0.0);  // empty residual: draw from p itself
     const double total = plain ? E : R;
     const double t = static_cast<double>(Grp<kG>::at_f(u_lane, base, ucol)) * total;

@@ -460,7 +460,10 @@ __device__ __forceinline__ float draw_weight(float z, float q, int v, const SeqS
   e_out = e;
   if (plain || st.mode == kBonus) return e;
   if (st.mode == kResidualOnehot) return v == st.excl ? 0.f : e;
-  return fmaxf(0.f, fmaf(-st.s, q, e));  // s * max(0, p - q)
+  // A draft probability that is negative, infinite or NaN makes the weight NaN, so the draw's
+  // total is NaN and the pick reports the sequence invalid.
+  const float w = fmaxf(0.f, fmaf(-st.s, q, e));  // s * max(0, p - q)
+  return (q >= 0.f && q <= __FLT_MAX__) ? w : __builtin_nanf("");
 }
 
 // Loads of the kGroup tokens [v0, v0 + cnt) (cnt <= 0: none); -inf / 0 past cnt.  The vector

@@ -570,6 +570,45 @@ def test_invalid_rows_and_untouched_padding():
     assert out.accept_len[0] == -1 and out.accept_len[1] >= 0 and out.accept_len[2] >= 0
 
 
+def test_bad_entries_in_draft_rows_matter_only_where_the_draw_reads():
+    # Slot 0 is always accepted (u = 0 and p(x_0) > 0) and slot 1 always rejected (z_1(x_1) =
+    # -inf), so the residual draw reads exactly draft row 1.  A negative or non-finite entry there
+    # (away from x_1) makes the sequence invalid (R10); the same entry in row 0 away from x_0, or
+    # in row 2, is never read and changes nothing; -0.0 is a valid zero.
+    rng = np.random.default_rng(16)
+    K, V = 3, 24
+    z = rng.standard_normal((K + 1, V))
+    q = scipy.special.softmax(rng.standard_normal((K, V)), axis=-1)
+    x = np.array([2, 5, 7])
+    z[1, x[1]] = -np.inf
+    U = np.array([0.0, 0.5, 0.5, 0.37])
+    plants = [(None, None, True)]
+    for val in (np.nan, np.inf, -np.inf, -0.5, -1e-30):
+        plants += [((1, 11), val, False), ((0, 11), val, True), ((2, 11), val, True)]
+    plants += [((1, 11), 0.0, True), ((1, 11), -0.0, True)]
+    zs, qs = [], []
+    for at, val, _ in plants:
+        qq = q.copy()
+        if at is not None:
+            qq[at] = val
+        zs.append(z)
+        qs.append(qq)
+    n = len(plants)
+    out = verify(mk(np.stack(zs), np.stack(qs), np.tile(x, (n, 1)), np.ones(n), np.tile(U, (n, 1))))
+    assert out.accept_len[0] == 1 and out.out_tokens[0, 0] == x[0]
+    for j, (at, val, valid) in enumerate(plants):
+        # Same round as the clean row, except that a zero in row 1 is a different (valid) q:
+        # -0.0 must then give what +0.0 gives.
+        same = n - 2 if (at == (1, 11) and val == 0.0) else 0
+        if valid:
+            assert out.accept_len[j] == 1, j
+            assert np.array_equal(out.out_tokens[j], out.out_tokens[same]), j
+            assert np.array_equal(out.out_probs[j], out.out_probs[same]), j
+        else:
+            assert out.accept_len[j] == -1, j
+            assert (out.out_tokens[j] == -1).all() and (out.out_probs[j] == 0).all(), j
+
+
 # ---------------------------------------------------------------------------------------------
 # Invariants on the workloads' own row mixes
 # ---------------------------------------------------------------------------------------------
