@@ -12,9 +12,11 @@ import torch
 import oracle
 from oracle.parity import boundary_limit, compare, expected_boundary
 from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
+                                                           SPECDEC_PATH_ONE_LAUNCH,
                                                            SPECDEC_PATH_STREAMING,
                                                            SPECDEC_SMALL_V_MAX, inputs_to_device,
-                                                           specdec_verify, specdec_verify_greedy)
+                                                           specdec_verify, specdec_verify_greedy,
+                                                           specdec_workspace_size)
 from speculative_decoding_verification_specdec_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
@@ -244,6 +246,112 @@ def test_zero_mass_drafts(V, path):
     acc, tok, _ = run_gpu(inp, path=path)
     for b in range(0, inp.B, 3):
         assert acc[b] == 0 and tok[b, 0] != X[b, 0]  # rejected at slot 0, x_0 not redrawn
+
+
+# Draft rows with an entry that is not a probability (NaN, +-inf, negative), on every route the
+# draw can take: the streaming kernels with a fine draw grid (B * chunks <= 256), one resident
+# round (<= 1536) and the split draw + pick kernel (more), the small-vocabulary kernel, and the
+# one-launch path.
+BAD_Q_CASES = {
+    "streaming_fine": (24, 4, 3000, SPECDEC_PATH_STREAMING),
+    "streaming_one_round": (400, 3, 3000, SPECDEC_PATH_STREAMING),
+    "streaming_split": (1600, 2, 3000, SPECDEC_PATH_STREAMING),
+    "small_vocab": (64, 4, 300, SPECDEC_PATH_AUTO),
+    "one_launch": (24, 4, 3000, SPECDEC_PATH_ONE_LAUNCH),
+}
+
+
+@pytest.mark.parametrize("name", list(BAD_Q_CASES))
+def test_bad_entries_in_draft_rows(name):
+    # In half the rejected model-draft sequences, one entry of the rejected slot's draft row (the
+    # row the residual draw reads), away from the drafted token, is NaN, +inf, -inf or -0.5: the
+    # sequence is invalid.  In the other half the same values sit in rows the round never reads
+    # in full (the accepted slot before the rejection and the slot after it, away from their
+    # drafted tokens): nothing changes.
+    B, K, V, path = BAD_Q_CASES[name]
+    inp = gen.make_batch(B, K, V, seed=57, dtype="f32", onehot_frac=0.25, ragged=True)
+    clean = oracle.verify(inp)
+    kb = inp.draft_counts()
+    rej = [b for b in range(B) if not inp.draft_onehot[b] and 0 <= clean.accept_len[b] < kb[b]]
+    assert len(rej) >= 8
+    vals = [np.nan, np.inf, -np.inf, -0.5]
+    bad, unread = [], []
+    for j, b in enumerate(rej[::max(1, len(rej) // 40)]):
+        A = int(clean.accept_len[b])
+        val = vals[(j // 2) % 4]
+        if j % 2 == 0:
+            inp.draft_probs[b, A, (int(inp.proposed[b, A]) + 1 + j) % V] = val
+            bad.append(b)
+        else:
+            for i in (A - 1, A + 1):
+                if 0 <= i < K:
+                    inp.draft_probs[b, i, (int(inp.proposed[b, i]) + 1 + j) % V] = val
+            unread.append(b)
+    ref = oracle.verify(inp)
+    assert set(np.flatnonzero(ref.accept_len < 0)) == set(bad)
+    assert np.array_equal(ref.accept_len[unread], clean.accept_len[unread])
+    check(inp, path=path)
+    acc, _, _ = run_gpu(inp, path=path)
+    assert (acc[bad] == -1).all() and (acc[unread] >= 0).all()
+
+
+# The workspace's first region: one 16-byte record per (row, 2048-token sub-chunk) written by the
+# streaming row-statistics kernel -- the sub-chunk's max logit m, its sum of exp2((z - m) * c)
+# with c = log2(e) / T (fp32), the lowest index attaining m (greedy rows) and a match-mode sum.
+PARTIAL = np.dtype([("m", "<f4"), ("s", "<f4"), ("arg", "<i4"), ("pre", "<f4")])
+SUB, CHUNK = 2048, 8192
+
+
+@pytest.mark.parametrize("name,maker", [
+    ("batch64_full_V", lambda: gen.batch64(B=6, seed=64)),
+    ("greedy_mix_ragged_V", lambda: gen.make_batch(12, 3, 20003, seed=65, greedy_frac=0.5,
+                                                   ragged=True)),
+])
+def test_row_statistics_match_the_oracle(name, maker):
+    """Per-row log-sum-exp of z / T merged from the streaming kernel's partials (in fp64 on the
+    host) within 1e-6 relative of the oracle's (z_max / T - log p(argmax), from its softmax);
+    each row's max exact; greedy rows' lowest-index argmax exact."""
+    inp = maker()
+    print(f"\n[case] row statistics {name} B={inp.B} K={inp.K} V={inp.V}", flush=True)
+    B, K, V = inp.B, inp.K, inp.V
+    S = (V + CHUNK - 1) // CHUNK
+    d = inputs_to_device(inp, DEV)
+    ws = torch.zeros(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=DEV)
+    specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"], d["uniforms"],
+                   draft_onehot=d["draft_onehot"], num_draft=d["num_draft"], workspace=ws,
+                   path=SPECDEC_PATH_STREAMING)
+    torch.cuda.synchronize()
+    n = B * (K + 1) * S * 4
+    part = ws[:n * PARTIAL.itemsize].cpu().numpy().view(PARTIAL).reshape(B, K + 1, S * 4)
+    kb = inp.draft_counts()
+    worst = 0.0
+    for b in range(B):
+        T = float(inp.temperature[b])
+        c32 = np.float32(np.log2(np.e)) if T == 0.0 else np.float32(np.log2(np.e)) / np.float32(T)
+        Tn = 1.0 if T == 0.0 else T
+        for i in range(kb[b] + 1):
+            z = oracle.logit_row(inp.logits, inp.logits_dtype, b, i)
+            pr = part[b, i]
+            M = float(pr["m"].max())
+            assert M == z.max(), (b, i)
+            for j in range(S * 4):              # each sub-chunk's max is its own
+                seg = z[j * SUB:(j + 1) * SUB]
+                assert pr["m"][j] == (seg.max() if seg.size else -np.inf), (b, i, j)
+            live = pr["m"] > -np.inf
+            s = float(np.sum(pr["s"][live].astype(np.float64)
+                             * np.exp2((pr["m"][live].astype(np.float64) - M) * float(c32))))
+            lse = M / Tn + np.log(s)            # exp2((z - M) * c) = exp((z - M) / T)
+            p = oracle.target_probs(z, Tn)
+            a = int(np.argmax(p))
+            lse_ref = z[a] / Tn - np.log(p[a])
+            rel = abs(lse - lse_ref) / abs(lse_ref)
+            worst = max(worst, rel)
+            assert rel <= 1e-6, (b, i, lse, lse_ref)
+            if T == 0.0:
+                am = int(np.argmax(z))
+                js = int(np.flatnonzero(pr["m"] == M)[0])
+                assert pr["arg"][js] == am, (b, i)
+    print(f"[report] worst lse relative error {worst:.3g}", flush=True)
 
 
 def test_call_on_a_side_stream_keeps_its_temporaries():
