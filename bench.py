@@ -9,10 +9,17 @@ scan, and the residual / bonus draw.  Inputs are resident in HBM before timing s
 copies of them are rotated step by step so the 256 MB Infinity Cache cannot serve a step from
 the previous one.
 
+Timing: W untimed warmup steps, then REPEATS (5) timed repeats of exactly K steps each, every
+repeat replayed from HIP graphs and bracketed by synchronisation and HIP events; the reported
+step time is the median repeat's, and every repeat's figure and their spread are reported beside
+it.  The other workloads are timed the same way (median of 5 repeats).
+
 Prints ONE JSON line: verified draft positions per second (sum_b k_b per step / step time),
 plus a roofline object for the streaming row-statistics kernel (algorithmic logit bytes per
 launch / its HIP-event-timed duration, against the 8 TB/s HBM peak) and the fp64 CPU oracle's
-rate on a bounded sample of the same workload.
+rate on a bounded sample of the same workload.  ``dtype`` names the arithmetic the path computes
+in (fp32 exponentials and sums; the accept tests and the draw's final scan in fp64); the target
+logits it reads are bf16 (``config.logits_dtype``).
 """
 from __future__ import annotations
 
@@ -21,6 +28,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -30,6 +38,8 @@ if ROOT not in sys.path:
 
 METRIC = "verified draft positions/sec and HBM GB/s (% of peak), B=64 V=128256 k=5"
 HBM_PEAK_GBS = 8000.0
+REPEATS = 5
+CPU_WORKER_CAP = 16   # the CPU share one GPU's host jobs may use, whatever the affinity mask shows
 HOT_KERNEL = "stats_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_kernel_batch64_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_verification_specdec_amd", "csrc",
@@ -113,8 +123,10 @@ def _cpu_shard(job):
 def cpu_baseline(inp, budget_s: float = 6.0, parallel_s: float = 1.5):
     """The fp64 oracle (as it stands) on the same inputs, run before the GPU is touched so that
     worker processes can be forked: (i) one thread, whole batches repeated for about
-    ``budget_s``; (ii) every host core (at most 16), the batch's sequences split into one shard
-    per forked worker, each worker repeating its shard for about ``parallel_s``."""
+    ``budget_s``; (ii) one forked worker per CPU of the affinity mask, at most CPU_WORKER_CAP,
+    the batch's sequences split into one shard per worker, each worker repeating its shard for
+    about ``parallel_s``.  ``cores`` is the number of workers used; ``affinity_cpus`` the size of
+    the mask."""
     global _CPU_INP
     import multiprocessing
 
@@ -131,7 +143,8 @@ def cpu_baseline(inp, budget_s: float = 6.0, parallel_s: float = 1.5):
             break
     single = dict(value=positions * n / el, unit="positions/s", cores=1,
                   sample=f"{n} full oracle calls on the B=64 V=128256 k=5 batch ({el:.1f} s)")
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(CPU_WORKER_CAP, affinity))
     shards = [r for r in np.array_split(np.arange(inp.B), cores) if len(r)]
     reps = max(1, int(parallel_s / (el / n / len(shards))))
     _CPU_INP = inp
@@ -149,16 +162,18 @@ def cpu_baseline(inp, budget_s: float = 6.0, parallel_s: float = 1.5):
     except OSError:
         pass
     return dict(value=positions * reps / el_p, unit="positions/s", cores=len(shards),
-                kind="oracle", cpu_model=model,
+                kind="oracle", cpu_model=model, affinity_cpus=affinity,
+                worker_cap=CPU_WORKER_CAP,
                 sample=f"{reps} passes over the B=64 V=128256 k=5 batch, its sequences split "
                        f"across {len(shards)} forked worker processes (one per host core, "
                        f"numpy fp64; {el_p:.1f} s)",
                 single_core=single)
 
 
-def algorithmic_bytes(inp, acc_np):
+def algorithmic_bytes(inp, acc_np, all_rejected: bool = False):
     """Bytes the method must move per call: every used target row once, ids, q gathers,
-    uniforms, temperatures, one draft row per rejected model-draft sampled sequence, outputs."""
+    uniforms, temperatures, one draft row per rejected model-draft sampled sequence, outputs.
+    ``all_rejected``: the upper bound, as if every sampled model-draft sequence were rejected."""
     import numpy as np
     kb = inp.draft_counts()
     sz = 2 if inp.logits_dtype == "bf16" else 4
@@ -166,16 +181,24 @@ def algorithmic_bytes(inp, acc_np):
     sampled = inp.temperature > 0
     onehot = np.zeros(inp.B, bool) if inp.draft_onehot is None else inp.draft_onehot.astype(bool)
     model = sampled & ~onehot
-    rejected = (acc_np >= 0) & (acc_np < kb)
+    rejected = np.ones(inp.B, bool) if all_rejected else (acc_np >= 0) & (acc_np < kb)
     logits = float(((kb + 1) * V * sz).sum())
     small = float((4 * kb + 4 * kb * model + 4 * (kb + 1) * sampled + 4 + 8 * (kb + 1) + 4).sum())
     draft_rows = float((rejected & model).sum() * 4 * V)
     return logits, logits + small + draft_rows
 
 
-def time_replayed(calls, steps, stream):
-    """Mean µs per call of ``calls`` (rotated) replayed from one HIP graph of ``steps`` calls,
-    bracketed by synchronisation and events, after one untimed replay."""
+def _median_and_spread(us):
+    """(median, {"repeats_us": each repeat's figure, "spread_pct": (max - min) / median})."""
+    m = statistics.median(us)
+    return m, {"repeats_us": [round(float(x), 4) for x in us],
+               "spread_pct": (max(us) - min(us)) / m * 100.0}
+
+
+def time_replayed(calls, steps, stream, repeats=REPEATS):
+    """µs per call of ``calls`` (rotated) replayed from one HIP graph of ``steps`` calls: the
+    median of ``repeats`` timed replays, each bracketed by synchronisation and events, after one
+    untimed replay; returns (median, {"repeats_us", "spread_pct"})."""
     import torch
     with torch.cuda.stream(stream):
         for c in calls:
@@ -188,13 +211,16 @@ def time_replayed(calls, steps, stream):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / steps
+    us = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / steps)
+    return _median_and_spread(us)
 
 
 def bench_ngram(dev, stream, steps=200, replicas=20, long=False):
@@ -221,7 +247,7 @@ def bench_ngram(dev, stream, steps=200, replicas=20, long=False):
         ln = torch.from_numpy(h.lengths).to(dev)
         calls.append(lambda t=t, ln=ln: specdec_ngram_propose(t, ln, K, n_min=n_min, n_max=n_max,
                                                               out=out, workspace=ws))
-    us = time_replayed(calls, steps, stream)
+    us, spread = time_replayed(calls, steps, stream)
     nd = out[1].cpu().numpy()
     toks = float(h.lengths.astype(np.int64).sum())
     nbytes = 4.0 * toks + 4.0 * h.B + 4.0 * h.B * (K + 1)
@@ -232,7 +258,7 @@ def bench_ngram(dev, stream, steps=200, replicas=20, long=False):
         "us_per_call": us, "history_tokens_per_s": toks / (us * 1e-6),
         "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
         "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "sequences_proposing": int((nd > 0).sum()),
+        "sequences_proposing": int((nd > 0).sum()), **spread,
     }
 
 
@@ -261,10 +287,10 @@ def bench_commit(dev, stream, steps=400):
         seq.copy_(base)
         specdec_commit(acc, out, seq, tokens=tokens, target_kv_len=tkv, draft_kv_len=dkv,
                        out=packed)
-    us = time_replayed([call], steps, stream)
+    us, spread = time_replayed([call], steps, stream)
     return {"workload": "B=512, K=8, accept lengths U{0..8}, history capacity 8192",
             "us_per_call_including_length_reset_copy": us,
-            "sequences_per_s": B / (us * 1e-6)}
+            "sequences_per_s": B / (us * 1e-6), **spread}
 
 
 def bench_workload(dev, stream, inp, description, steps=60, replicas=1):
@@ -284,9 +310,10 @@ def bench_workload(dev, stream, inp, description, steps=60, replicas=1):
                                     d["temperature"], d["uniforms"],
                                     draft_onehot=d["draft_onehot"], num_draft=d["num_draft"],
                                     workspace=ws, out=calls[0].out if calls else None))
-    us = time_replayed(calls, steps, stream)
+    us, spread = time_replayed(calls, steps, stream)
     acc = calls[0].out[0].cpu().numpy()
     _, nbytes = algorithmic_bytes(inp, acc)
+    _, upper = algorithmic_bytes(inp, acc, all_rejected=True)
     positions = int(inp.draft_counts().sum())
     del d, calls, ws
     torch.cuda.empty_cache()
@@ -294,7 +321,10 @@ def bench_workload(dev, stream, inp, description, steps=60, replicas=1):
             "verified_positions_per_s": positions / (us * 1e-6),
             "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
             "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "mean_accept_len": float(acc[acc >= 0].mean()), "invalid_rows": int((acc < 0).sum())}
+            "upper_bound_bytes_frac_of_hbm_peak": upper / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mean_accept_len": float(acc[acc >= 0].mean()), "invalid_rows": int((acc < 0).sum()),
+            "rejected_sequences": int(((acc >= 0) & (acc < inp.draft_counts())).sum()),
+            **spread}
 
 
 def bench_match(dev, stream, steps=300, replicas=6):
@@ -317,7 +347,7 @@ def bench_match(dev, stream, steps=300, replicas=6):
         d = inputs_to_device(inp, dev)
         calls.append(lambda d=d: specdec_verify_match(d["logits"], d["proposed"], d["temperature"],
                                                       d["uniforms"], out=out, workspace=ws))
-    us = time_replayed(calls, steps, stream)
+    us, spread = time_replayed(calls, steps, stream)
     acc = out[0].cpu().numpy()
     kb = inp.draft_counts()
     positions = int(kb.sum())
@@ -326,7 +356,7 @@ def bench_match(dev, stream, steps=300, replicas=6):
             "us_per_call": us, "verified_positions_per_s": positions / (us * 1e-6),
             "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
             "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "mean_accept_len": float(acc.mean())}
+            "mean_accept_len": float(acc.mean()), **spread}
 
 
 def bench_telemetry(dev, stream, steps=400):
@@ -344,10 +374,14 @@ def bench_telemetry(dev, stream, steps=400):
     cnt = telemetry_counters(4, dev)
     table = torch.tensor([3, 5, 8, 2], dtype=torch.int32, device=dev)
     nd2 = nd.clone()
-    us_t = time_replayed([lambda: specdec_telemetry_update(cnt, acc, num_draft=nd, route=route,
-                                                           K=K)], steps, stream)
-    us_a = time_replayed([lambda: specdec_apply_k(nd2, table, route=route)], steps, stream)
-    return {"workload": "B=512, K=8, 4 routes", "update_us": us_t, "apply_k_us": us_a}
+    us_t, spread_t = time_replayed([lambda: specdec_telemetry_update(cnt, acc, num_draft=nd,
+                                                                     route=route, K=K)],
+                                   steps, stream)
+    us_a, spread_a = time_replayed([lambda: specdec_apply_k(nd2, table, route=route)], steps,
+                                   stream)
+    return {"workload": "B=512, K=8, 4 routes", "update_us": us_t, "apply_k_us": us_a,
+            "update_spread_pct": spread_t["spread_pct"],
+            "apply_k_spread_pct": spread_a["spread_pct"]}
 
 
 def main():
@@ -459,21 +493,26 @@ def main():
         g_rem.replay()
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` whole steps, bracketed by synchronisation and HIP events.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(full):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
+    # Timed regions: REPEATS repeats of exactly `steps` whole steps, each bracketed by
+    # synchronisation and HIP events; the median repeat is the reported step time.
+    rep_ms, rep_wall = [], []
+    for _ in range(REPEATS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(full):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        rep_wall.append(time.perf_counter() - w0)
+        rep_ms.append(e0.elapsed_time(e1) / args.steps)
+    ms_per_step, spread = _median_and_spread(rep_ms)
+    spread["repeats_us"] = [round(x * 1e3, 4) for x in rep_ms]
+    wall = statistics.median(rep_wall)
 
     # The same steps launched eagerly, with HIP events recorded by the library around the
     # streaming row-statistics kernel of each step.  A spin kernel in front lets the host
@@ -491,6 +530,7 @@ def main():
     acc_np = acc.cpu().numpy()
     assert (acc_np >= 0).all(), "invalid rows in the benchmark batch"
     logit_bytes, call_bytes = algorithmic_bytes(inp, acc_np)
+    _, upper_bytes = algorithmic_bytes(inp, acc_np, all_rejected=True)
     positions = int(inp.draft_counts().sum())
     value = positions / (ms_per_step * 1e-3)
     achieved = logit_bytes / (hot_ms * 1e-3) / 1e9
@@ -532,7 +572,11 @@ def main():
             "algorithmic_bytes": call_bytes,
             "algorithmic_GBps": call_bytes / (ms_per_step * 1e-3) / 1e9,
             "frac_of_hbm_peak": call_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "upper_bound_bytes": upper_bytes,
+            "upper_bound_frac_of_hbm_peak":
+                upper_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rejected_sequences": int((acc_np < K).sum()),
+            "repeats": REPEATS, **spread,
         },
     }
     if not args.no_next_rows:
@@ -554,6 +598,10 @@ def main():
         res["other_workloads"] = {"large_batch_deep": bench_workload(
             dev, stream, large_batch_deep(),
             "B=256, k=8, V=152064, bf16 logits ~N(0,4^2) + 8 on 1% of entries, 25% greedy rows")}
+        print("[bench] large batch, deep calibrated draft", file=sys.stderr, flush=True)
+        res["other_workloads"]["large_batch_deep_calibrated"] = bench_workload(
+            dev, stream, large_batch_deep(calibrated=True),
+            "large_batch_deep with draft noise 0.3 (acceptance ~0.7): the k=8 bonus path")
         print("[bench] ragged mixed drafters", file=sys.stderr, flush=True)
         res["other_workloads"]["ragged_mixed"] = bench_workload(
             dev, stream, ragged_mixed(),
