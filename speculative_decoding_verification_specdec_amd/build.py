@@ -32,9 +32,28 @@ def hipcc() -> str:
     return str(cand) if cand.exists() else "hipcc"
 
 
-def build_library(verbose: bool = True) -> pathlib.Path:
-    tmp = OUTPUT.with_suffix(".so.tmp")
-    cmd = [hipcc(), *FLAGS, f"-I{ROOT / 'include'}", *map(str, SOURCES), "-o", str(tmp)]
+# The host code with AddressSanitizer (the device code is built as usual): for running the
+# host-side checks of the C ABI under the sanitizer on a machine without a GPU.
+ASAN_OUTPUT = PKG / "libspecdec_asan.so"
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to preload into the process that
+    loads the sanitized library)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    clang = pathlib.Path(rocm) / "llvm" / "bin" / "clang"
+    res = subprocess.run([str(clang), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    return res.stdout.strip()
+
+
+def build_library(verbose: bool = True, asan: bool = False) -> pathlib.Path:
+    out = ASAN_OUTPUT if asan else OUTPUT
+    tmp = out.with_suffix(".so.tmp")
+    cmd = [hipcc(), *FLAGS, *(ASAN_FLAGS if asan else []), f"-I{ROOT / 'include'}",
+           *map(str, SOURCES), "-o", str(tmp)]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,9 +63,9 @@ def build_library(verbose: bool = True) -> pathlib.Path:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, OUTPUT)
-    return OUTPUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build_library())
+    print(build_library(asan="--asan" in sys.argv[1:]))
