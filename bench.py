@@ -42,15 +42,19 @@ REPEATS = 5
 CPU_WORKER_CAP = 16   # the CPU share one GPU's host jobs may use, whatever the affinity mask shows
 HOT_KERNEL = "stats_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_kernel_batch64_counters.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_verification_specdec_amd", "csrc",
-                             "kernels.hip")
+# The streaming kernel's code: the kernel file and the device headers it is built from.
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_specdec_amd", "csrc", f)
+                  for f in ("kernels.hip", "kernels.h", "verify_dev.h", "wave_ops.h")]
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the kernel source's code: comments and blank lines stripped, so a comment
-    edit does not invalidate a counter summary taken on the same code."""
-    with open(KERNEL_SOURCE, encoding="utf-8") as f:
-        src = f.read()
+    """sha256[:16] of the streaming kernel's source code (its file and device headers, in that
+    order): comments and blank lines stripped, so a comment edit does not invalidate a counter
+    summary taken on the same code."""
+    src = ""
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     code = "\n".join(line.strip() for line in src.splitlines() if line.strip())
@@ -359,6 +363,99 @@ def bench_match(dev, stream, steps=300, replicas=6):
             "mean_accept_len": float(acc.mean()), **spread}
 
 
+def bench_group_pipeline(dev, groups, steps=400, replicas=4):
+    """The alternative of pipelining sequence groups across two streams, measured: the batch64
+    batch split into ``groups`` groups of sequences, each its own specdec_verify call with its own
+    workspace and output slices.  (a) the whole batch as one call; (b) the groups one after
+    another on one stream; (c) the groups alternating between two streams, group g + 1 waiting
+    (hipStreamWaitEvent) on an event recorded right after group g's streaming kernel, so that
+    its streaming can overlap group g's draw; the first stream waits for the last group's.  All
+    eager launches queued behind a spin kernel; µs per whole step; outputs compared bit for bit
+    with (a)'s."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from speculative_decoding_verification_specdec_amd import (inputs_to_device,
+                                                               specdec_workspace_size)
+    from speculative_decoding_verification_specdec_amd.binding import PreparedVerify
+    from speculative_decoding_verification_specdec_amd.inputs import batch64
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    inp = batch64()
+    B, K, V = inp.B, inp.K, inp.V
+    if B % groups:
+        raise SystemExit(f"--group-pipeline: {groups} does not divide B = {B}")
+    reps = [inputs_to_device(inp, dev) for _ in range(replicas)]
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def outputs():
+        return (torch.full((B,), -9, dtype=torch.int32, device=dev),
+                torch.full((B, K + 1), -9, dtype=torch.int32, device=dev),
+                torch.full((B, K + 1), -9.0, dtype=torch.float32, device=dev))
+
+    def make(G, out):
+        n = B // G
+        wss = [torch.zeros(specdec_workspace_size(n, K, V), dtype=torch.uint8, device=dev)
+               for _ in range(G)]
+        calls = []
+        for d in reps:
+            cs = []
+            for g in range(G):
+                sl = slice(g * n, (g + 1) * n)
+                cs.append(PreparedVerify(d["logits"][sl], d["draft_probs"][sl], d["proposed"][sl],
+                                         d["temperature"][sl], d["uniforms"][sl],
+                                         out=tuple(t[sl] for t in out), workspace=wss[g]))
+            calls.append(cs)
+        return calls
+
+    def run(G, pipelined):
+        out = outputs()
+        calls = make(G, out)
+        ev = HipEvents(steps * G)
+        join = HipEvents(steps)
+        for i in range(10):
+            for c in calls[i % replicas]:
+                c(stream=sA)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(sA):
+            torch.cuda._sleep(int(3e8))
+            e0.record(sA)
+        for i in range(steps):
+            cs = calls[i % replicas]
+            if not pipelined:
+                for c in cs:
+                    c(stream=sA)
+                continue
+            streams = [sA, sB]
+            for g, c in enumerate(cs):
+                s = streams[g % 2]
+                if g > 0:
+                    hip.hipStreamWaitEvent(s.cuda_stream, ev.pairs[i * G + g - 1][1], 0)
+                c(stream=s, hot_events=ev.pairs[i * G + g])
+            if (G - 1) % 2:
+                hip.hipEventRecord(join.pairs[i][0], sB.cuda_stream)
+                hip.hipStreamWaitEvent(sA.cuda_stream, join.pairs[i][0], 0)
+        e1.record(sA)
+        torch.cuda.synchronize()
+        ev.close()
+        join.close()
+        return e0.elapsed_time(e1) * 1e3 / steps, [t.cpu().numpy() for t in out]
+
+    whole_us, ref = run(1, False)
+    serial_us, o1 = run(groups, False)
+    piped_us, o2 = run(groups, True)
+    same = all(np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+               for o in (o1, o2) for a, b in zip(o, ref))
+    return {"workload": f"batch64 (B=64, k=5, V=128256, bf16) in {groups} groups of "
+                        f"{B // groups} sequences", "steps": steps,
+            "whole_batch_one_call_us": whole_us, "groups_one_stream_us": serial_us,
+            "groups_pipelined_two_streams_us": piped_us, "outputs_identical": bool(same)}
+
+
 def bench_telemetry(dev, stream, steps=400):
     """Telemetry update of a B=512, K=8 batch into 4 routes, and applying a 4-route plan."""
     import numpy as np
@@ -403,6 +500,9 @@ def main():
     ap.add_argument("--small-vocab-only", action="store_true",
                     help="only the small-vocabulary-path workloads (tiny vocabulary call, one-round "
                          "latency): for profiling that kernel")
+    ap.add_argument("--group-pipeline", type=int, default=0, metavar="G",
+                    help="only measure the two-stream sequence-group pipelining alternative "
+                         "(batch64 in G groups) against the whole-batch call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -419,7 +519,8 @@ def main():
     from speculative_decoding_verification_specdec_amd.inputs import batch64
 
     cpu = None
-    if not (args.no_cpu_baseline or args.copy_calibration or args.small_vocab_only):
+    if not (args.no_cpu_baseline or args.copy_calibration or args.small_vocab_only
+            or args.group_pipeline):
         # Before any GPU call: the all-core leg forks worker processes.
         print("[bench] timing the CPU oracle on the batch", file=sys.stderr, flush=True)
         cpu = cpu_baseline(batch64(), args.cpu_budget)
@@ -440,6 +541,9 @@ def main():
                                                                        SPECDEC_PATH_ONE_LAUNCH,
                                                                        PreparedVerify)
     path = SPECDEC_PATH_ONE_LAUNCH if args.path == "one_launch" else SPECDEC_PATH_AUTO
+    if args.group_pipeline:
+        print(json.dumps({"group_pipeline": bench_group_pipeline(dev, args.group_pipeline)}))
+        return
     if args.small_vocab_only:
         from speculative_decoding_verification_specdec_amd.inputs import tiny_vocab
         stream = torch.cuda.Stream()
