@@ -61,15 +61,16 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(bytes_alg_per_launch: float):
-    """HBM bytes per launch of the hot kernel from the committed rocprofv3 counter summary
+def measured_traffic(key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch of a kernel (``key``: the streaming kernel's line by default, or
+    "accept_draw_kernel_hbm_bytes_per_launch") from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration it records), or None when
     the summary is missing or was taken on a different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    t = re.search(r"^" + re.escape(key) + r":\s*([0-9.eE+]+)", txt, flags=re.M)
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
@@ -197,6 +198,17 @@ def _median_and_spread(us):
     m = statistics.median(us)
     return m, {"repeats_us": [round(float(x), 4) for x in us],
                "spread_pct": (max(us) - min(us)) / m * 100.0}
+
+
+def draft_row_bytes(inp, acc_np):
+    """The draw kernel's algorithmic bytes: one fp32 draft row per rejected, sampled,
+    model-draft sequence."""
+    import numpy as np
+    kb = inp.draft_counts()
+    sampled = inp.temperature > 0
+    onehot = np.zeros(inp.B, bool) if inp.draft_onehot is None else inp.draft_onehot.astype(bool)
+    rejected = (acc_np >= 0) & (acc_np < kb)
+    return float((rejected & sampled & ~onehot).sum() * 4 * inp.V)
 
 
 def time_replayed(calls, steps, stream, repeats=REPEATS):
@@ -621,15 +633,19 @@ def main():
     # The same steps launched eagerly, with HIP events recorded by the library around the
     # streaming row-statistics kernel of each step.  A spin kernel in front lets the host
     # queue every launch before the GPU reaches them, so the events bracket kernel time only.
-    hot = HipEvents(args.steps)
+    # The kernels after it (accept scan, draw sums, pick) are bracketed by a second pair.
+    hot, drw = HipEvents(args.steps), HipEvents(args.steps)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         torch.cuda._sleep(int(2e8))
         for i in range(args.steps):
-            calls[i % R](hot_events=hot.pairs[i])
+            calls[i % R](hot_events=hot.pairs[i], draw_events=drw.pairs[i])
     torch.cuda.synchronize()
     hot_ms = sum(hot.elapsed_ms(i) for i in range(args.steps)) / args.steps
+    draw_ms = (sum(drw.elapsed_ms(i) for i in range(args.steps)) / args.steps
+               if args.path == "auto" else None)
     hot.close()
+    drw.close()
 
     acc_np = acc.cpu().numpy()
     assert (acc_np >= 0).all(), "invalid rows in the benchmark batch"
@@ -638,7 +654,8 @@ def main():
     positions = int(inp.draft_counts().sum())
     value = positions / (ms_per_step * 1e-3)
     achieved = logit_bytes / (hot_ms * 1e-3) / 1e9
-    traffic = measured_traffic(logit_bytes)
+    traffic = measured_traffic()
+    draft_bytes = draft_row_bytes(inp, acc_np)
 
     res = {
         "metric": METRIC,
@@ -669,6 +686,20 @@ def main():
             "traffic": traffic,
             "kernel_us": hot_ms * 1e3,
             "bytes_per_launch": logit_bytes,
+        },
+        # The draw kernel (accept scan, draw sums and the pick, one launch here): its
+        # algorithmic bytes are the rejected rows' draft probabilities (the target rows it
+        # re-reads to form p - q are not counted).
+        "roofline_draw": None if draw_ms is None else {
+            "kernel": "accept_draw_kernel",
+            "bound": "hbm",
+            "achieved": draft_bytes / (draw_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": draft_bytes / (draw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic("accept_draw_kernel_hbm_bytes_per_launch"),
+            "kernel_us": draw_ms * 1e3,
+            "bytes_per_launch": draft_bytes,
         },
         "whole_step": {
             "us": ms_per_step * 1e3,

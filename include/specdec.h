@@ -179,6 +179,10 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
  *     logit-row kernel, or the small-vocabulary kernel on that path) when it starts and when it
  *     completes, so hipEventElapsedTime gives that kernel's own duration.  Either may be NULL.
  *   path: one of SPECDEC_PATH_*; any other value is SPECDEC_ERR_SHAPE.
+ *   draw_event_begin / draw_event_end: the same hook around the kernels that run after the
+ *     streaming kernel on the streaming path (accept scan, draw sums and pick): begin is recorded
+ *     when the first of them starts, end when the last completes.  Not recorded on the
+ *     small-vocabulary and one-launch paths (one kernel there).  Either may be NULL.
  *   spin_limit: SPECDEC_PATH_ONE_LAUNCH only: polls a workgroup makes while it waits for a
  *     hand-off from another workgroup of the launch (0 = the default, 2^20 polls, about a second;
  *     negative = SPECDEC_ERR_SHAPE).  A wait that gives up reports its sequence as invalid
@@ -190,6 +194,8 @@ typedef struct {
   void* hot_event_end;
   int32_t path;
   int32_t spin_limit;
+  void* draw_event_begin;
+  void* draw_event_end;
 } specdec_options;
 
 specdec_status specdec_verify_ex(const void* target_logits, int32_t logits_dtype,

@@ -28,7 +28,8 @@ class SpecdecError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("hot_event_begin", ctypes.c_void_p), ("hot_event_end", ctypes.c_void_p),
-                ("path", ctypes.c_int32), ("spin_limit", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("spin_limit", ctypes.c_int32),
+                ("draw_event_begin", ctypes.c_void_p), ("draw_event_end", ctypes.c_void_p)]
 
 
 # Execution paths of specdec_verify (include/specdec.h).
@@ -37,10 +38,14 @@ SPECDEC_PATH_AUTO, SPECDEC_PATH_STREAMING, SPECDEC_PATH_SMALL_VOCAB = 0, 1, 2
 SPECDEC_PATH_ONE_LAUNCH = 3
 
 
-def _options(hot_events, path, spin_limit=0):
-    ev = (None, None) if hot_events is None else tuple(
-        e if isinstance(e, int) or e is None else e.cuda_event for e in hot_events)
-    return _Options(ev[0], ev[1], int(path), int(spin_limit))
+def _event_pair(events):
+    return (None, None) if events is None else tuple(
+        e if isinstance(e, int) or e is None else e.cuda_event for e in events)
+
+
+def _options(hot_events, path, spin_limit=0, draw_events=None):
+    ev, dv = _event_pair(hot_events), _event_pair(draw_events)
+    return _Options(ev[0], ev[1], int(path), int(spin_limit), dv[0], dv[1])
 
 
 def library_path() -> pathlib.Path:
@@ -181,14 +186,15 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
                    uniforms: torch.Tensor, *, draft_onehot: torch.Tensor | None = None,
                    num_draft: torch.Tensor | None = None, out=None, workspace=None,
                    want_probs: bool = True, stream=None, hot_events=None,
-                   path: int = SPECDEC_PATH_AUTO, spin_limit: int = 0):
+                   path: int = SPECDEC_PATH_AUTO, spin_limit: int = 0, draw_events=None):
     """Batched verify.  Shapes: target_logits [B, K+1, V] (bf16 or fp32), draft_probs
     [B, K, V] fp32 or None, proposed [B, K] int32, temperature [B] fp32, uniforms [B, K+1]
     fp32, draft_onehot [B] uint8 or None, num_draft [B] int32 or None.  Returns
     (accept_len [B] int32, out_tokens [B, K+1] int32, out_probs [B, K+1] fp32 or None),
     enqueued on ``stream`` (default: torch's current stream) without synchronising.
     ``hot_events``: optional (begin, end) pair of hipEvent_t handles (ints) recorded around the
-    kernel that reads every target row.  ``path``: SPECDEC_PATH_AUTO (the one-kernel small-vocabulary
+    kernel that reads every target row; ``draw_events`` the same around the kernels after it
+    (streaming path only).  ``path``: SPECDEC_PATH_AUTO (the one-kernel small-vocabulary
     path when V <= SPECDEC_SMALL_V_MAX, else the streaming kernels), _STREAMING, _SMALL_VOCAB
     or _ONE_LAUNCH.
     ``workspace``: a uint8 tensor of at least specdec_workspace_size(B, K, V) bytes
@@ -219,10 +225,11 @@ def specdec_verify(target_logits: torch.Tensor, draft_probs: torch.Tensor | None
     args = (_ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_onehot), _ptr(proposed),
             _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B, K, V, _ptr(acc), _ptr(tok),
             _ptr(prb), _ptr(ws), ws.numel(), _stream_handle(stream))
-    if hot_events is None and path == SPECDEC_PATH_AUTO and spin_limit == 0:
+    if (hot_events is None and draw_events is None and path == SPECDEC_PATH_AUTO
+            and spin_limit == 0):
         status = lib.specdec_verify(*args)
     else:
-        opts = _options(hot_events, path, spin_limit)
+        opts = _options(hot_events, path, spin_limit, draw_events)
         status = lib.specdec_verify_ex(*args, ctypes.byref(opts))
     _raise(status, "specdec_verify")
     return acc, tok, prb
@@ -487,7 +494,7 @@ def inputs_to_device(inp, device) -> dict:
 
 class PreparedVerify:
     """A specdec_verify call with its arguments marshalled once (for tight loops and HIP-graph
-    capture).  ``__call__(stream=None, hot_events=None)`` enqueues it on ``stream`` (default:
+    capture).  ``__call__(stream=None, hot_events=None, draw_events=None)`` enqueues it on ``stream`` (default:
     torch's current stream) and raises on a non-zero status."""
 
     def __init__(self, target_logits, draft_probs, proposed, temperature, uniforms, *,
@@ -514,12 +521,12 @@ class PreparedVerify:
                      _ptr(proposed), _ptr(num_draft), _ptr(temperature), _ptr(uniforms), B,
                      K1 - 1, V, _ptr(acc), _ptr(tok), _ptr(prb), _ptr(self.ws), self.ws.numel())
 
-    def __call__(self, stream=None, hot_events=None):
+    def __call__(self, stream=None, hot_events=None, draw_events=None):
         s = _stream_handle(stream)
-        if hot_events is None and self.path == SPECDEC_PATH_AUTO:
+        if hot_events is None and draw_events is None and self.path == SPECDEC_PATH_AUTO:
             status = self.lib.specdec_verify(*self.args, s)
         else:
-            opts = _options(hot_events, self.path)
+            opts = _options(hot_events, self.path, 0, draw_events)
             status = self.lib.specdec_verify_ex(*self.args, s, ctypes.byref(opts))
         if status != 0:
             _raise(status, "specdec_verify")

@@ -68,6 +68,8 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.stream = static_cast<hipStream_t>(stream);
   a.hot_begin = opts ? static_cast<hipEvent_t>(opts->hot_event_begin) : nullptr;
   a.hot_end = opts ? static_cast<hipEvent_t>(opts->hot_event_end) : nullptr;
+  a.draw_begin = opts ? static_cast<hipEvent_t>(opts->draw_event_begin) : nullptr;
+  a.draw_end = opts ? static_cast<hipEvent_t>(opts->draw_event_end) : nullptr;
   a.path = opts ? opts->path : SPECDEC_PATH_AUTO;
   a.spin_limit = opts ? opts->spin_limit : 0;
   if (a.spin_limit < 0) return SPECDEC_ERR_SHAPE;

@@ -122,6 +122,8 @@ struct LaunchArgs {
   hipStream_t stream;
   hipEvent_t hot_begin;      // optional, recorded around the streaming (or small-vocabulary)
   hipEvent_t hot_end;        // kernel
+  hipEvent_t draw_begin;     // optional, recorded around the kernels after the streaming kernel
+  hipEvent_t draw_end;       // (streaming path)
   int path;                  // 0: automatic, 1: three launches, 2: small-vocabulary kernel,
                              // 3: one launch
   int spin_limit;            // polls of the one-launch path's bounded waits (0: the default)

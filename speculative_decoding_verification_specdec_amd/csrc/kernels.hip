@@ -787,28 +787,41 @@ hipError_t launch_typed(const LaunchArgs& a) {
            : phase == 2 ? accept_draw_for<LT, 2>(match, vec_draw)
                         : accept_draw_for<LT, 3>(match, vec_draw);
   };
+  // With measurement events, the first dispatch below records draw_begin at its start and the
+  // last one draw_end at its completion.
   const int phases[2] = {split ? 1 : (fine ? 3 : 0), 2};
-  for (int ph = 0; ph < (split ? 2 : 1); ++ph) {
+  const int nphase = split ? 2 : 1;
+  for (int ph = 0; ph < nphase; ++ph) {
     const int phase = phases[ph];
     const int gx = (phase == 1 || !draws) ? 1 : (phase == 3 ? S * kSegPerChunk : S);
     for (int b0 = 0; b0 < a.B; b0 += kMaxZ) {
       const dim3 grid(gx, min(kMaxZ, a.B - b0));
-      accept_draw(phase)<<<grid, kThreads, 0, a.stream>>>(
-          logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature, a.uniforms,
-          b0, a.K, a.V, S, a.greedy_all, ws.partials, ws.gathers, a.accept_len,
-          a.out_tokens, a.out_probs, ws.states, ws.segs, ws.segw);
+      hipEvent_t ev0 = (ph == 0 && b0 == 0) ? a.draw_begin : nullptr;
+      hipEvent_t ev1 = (!split && b0 + kMaxZ >= a.B) ? a.draw_end : nullptr;
+      if (ev0 || ev1)
+        hipExtLaunchKernelGGL(accept_draw(phase), grid, dim3(kThreads), 0, a.stream, ev0, ev1, 0,
+                              logits, a.draft_probs, a.onehot, a.proposed, a.num_draft,
+                              a.temperature, a.uniforms, b0, a.K, a.V, S, a.greedy_all,
+                              ws.partials, ws.gathers, a.accept_len, a.out_tokens, a.out_probs,
+                              ws.states, ws.segs, ws.segw);
+      else
+        accept_draw(phase)<<<grid, kThreads, 0, a.stream>>>(
+            logits, a.draft_probs, a.onehot, a.proposed, a.num_draft, a.temperature,
+            a.uniforms, b0, a.K, a.V, S, a.greedy_all, ws.partials, ws.gathers, a.accept_len,
+            a.out_tokens, a.out_probs, ws.states, ws.segs, ws.segw);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
   if (!split) return hipSuccess;
-  if (vec_draw)
-    pick_kernel<LT, true><<<grid_for(a.B), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
-        a.accept_len, a.out_tokens, a.out_probs);
+  auto pick = vec_draw ? pick_kernel<LT, true> : pick_kernel<LT, false>;
+  if (a.draw_end)
+    hipExtLaunchKernelGGL(pick, dim3(grid_for(a.B)), dim3(kThreads), 0, a.stream, nullptr,
+                          a.draw_end, 0, logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S,
+                          ws.states, ws.segs, a.accept_len, a.out_tokens, a.out_probs);
   else
-    pick_kernel<LT, false><<<grid_for(a.B), kThreads, 0, a.stream>>>(
-        logits, a.draft_probs, a.uniforms, a.B, a.K, a.V, S, ws.states, ws.segs,
-        a.accept_len, a.out_tokens, a.out_probs);
+    pick<<<grid_for(a.B), kThreads, 0, a.stream>>>(logits, a.draft_probs, a.uniforms, a.B, a.K,
+                                                   a.V, S, ws.states, ws.segs, a.accept_len,
+                                                   a.out_tokens, a.out_probs);
   return hipGetLastError();
 }
 
