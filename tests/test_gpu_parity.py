@@ -133,6 +133,14 @@ def test_parity_full_size(name):
     check(FULL[name]())
 
 
+def test_streaming_path_past_one_launch_per_kernel():
+    # B = 100000 sequences is more than a grid's y / z extent (65535): the streaming kernel and
+    # the scan and draw passes each run in two launches, and the pick kernel strides over them.
+    inp = gen.tiny_vocab()
+    assert inp.B > 65535
+    check(inp, path=SPECDEC_PATH_STREAMING)
+
+
 def test_greedy_entry_point_is_bit_exact():
     inp = gen.large_batch_deep(B=48, V=30011)
     d = inputs_to_device(inp, DEV)
@@ -196,6 +204,26 @@ def test_invalid_rows_are_poisoned_alone():
     bad = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, b}
     assert set(np.flatnonzero(ref.accept_len < 0)) == bad
     assert (acc[list(bad)] == -1).all() and (acc[[11]] >= 0).all()
+
+
+@pytest.mark.parametrize("path", [SPECDEC_PATH_STREAMING, SPECDEC_PATH_AUTO,
+                                  SPECDEC_PATH_ONE_LAUNCH])
+@pytest.mark.parametrize("V", [300, 20008])
+def test_a_batch_of_only_invalid_rows(path, V):
+    # Nothing to draw anywhere: every sequence is poisoned by a different rule, the draw passes
+    # find no work, and nothing else is written.
+    inp = gen.make_batch(6, 3, V, seed=58, dtype="f32", onehot_frac=0.3)
+    inp.temperature[0] = np.nan
+    inp.temperature[1] = -2.0
+    inp.num_draft = np.full(inp.B, 3, np.int32)
+    inp.num_draft[2] = 4
+    inp.logits[3, 1, 5] = np.inf
+    inp.proposed[4, 2] = V + 1
+    inp.uniforms[5, 3] = 1.5
+    acc, tok, prb = run_gpu(inp, path=path)
+    assert (acc == -1).all() and (tok == -1).all() and (prb == 0).all()
+    ref = oracle.verify(inp)
+    assert (ref.accept_len == -1).all()
 
 
 def test_empty_batch():
