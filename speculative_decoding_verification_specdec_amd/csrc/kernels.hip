@@ -417,8 +417,8 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     float* __restrict__ out_probs, SeqState* __restrict__ states, SegSums* __restrict__ segs,
     u64* __restrict__ segw) {
   constexpr bool kFine = kPhase == 3;
-  // Grids of one resident round (phases 0 and 3) pick in this kernel; the split phases 1 and 2
-  // leave it to the pick kernel.
+  // Draw grids of at most kDrawRound workgroups (phases 0 and 3) pick in this kernel; the split
+  // phases 1 and 2 leave it to the pick kernel.
   constexpr bool pick_here = kPhase == 0 || kPhase == 3;
   constexpr int kGroupsPerLane = kSeg / kGroup / 64 / (kFine ? kWaves : 1);  // scalar path
   __shared__ SeqState sh_st;
@@ -746,11 +746,14 @@ hipError_t launch_typed(const LaunchArgs& a) {
   // Greedy-only calls draw nothing, and match mode only draws plain samples of p (from the
   // partials): the chunk-0 workgroups that run the scan are enough.
   // Otherwise one workgroup per chunk of the row to draw from.
-  // A draw grid of more than one resident round (about six 256-thread workgroups per CU on 256
-  // CUs) scans once per sequence in a separate pass instead, and a pick kernel draws after it.
-  // Smaller grids pick inside the draw kernel: the chunk-0 workgroup of a sequence waits for its
-  // siblings' segment sums (at most one waiting workgroup per sequence, so never more than the
-  // chip holds) and draws.
+  // A draw grid of more than kDrawRound workgroups (a few resident rounds: five or six 256-thread
+  // workgroups per CU on 256 CUs) scans once per sequence in a separate pass instead, and a pick
+  // kernel draws after it.  Smaller grids pick inside the draw kernel: the chunk-0 workgroup of a
+  // sequence waits for its siblings' segment sums and draws.  That wait always ends: only chunk-0
+  // workgroups wait, each only for the chunks of its own sequence, which have the next linear ids
+  // and so are dispatched before any later sequence's chunk-0 workgroup; the oldest waiting
+  // workgroup therefore always has every sibling dispatched, whatever the chip holds at once.  (The
+  // wait is bounded all the same.)
   // A draw grid smaller than the chip (up to 256 chunks) takes one workgroup per 2048-token
   // segment instead of one per chunk.
   constexpr long long kDrawRound = 1536;
