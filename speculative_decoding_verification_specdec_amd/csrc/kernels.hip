@@ -749,11 +749,12 @@ hipError_t launch_typed(const LaunchArgs& a) {
   // A draw grid of more than kDrawRound workgroups (a few resident rounds: five or six 256-thread
   // workgroups per CU on 256 CUs) scans once per sequence in a separate pass instead, and a pick
   // kernel draws after it.  Smaller grids pick inside the draw kernel: the chunk-0 workgroup of a
-  // sequence waits for its siblings' segment sums and draws.  That wait always ends: only chunk-0
-  // workgroups wait, each only for the chunks of its own sequence, which have the next linear ids
-  // and so are dispatched before any later sequence's chunk-0 workgroup; the oldest waiting
-  // workgroup therefore always has every sibling dispatched, whatever the chip holds at once.  (The
-  // wait is bounded all the same.)
+  // sequence waits for its siblings' segment sums and draws.  That wait always ends, whatever the
+  // chip holds at once: only chunk-0 workgroups wait, each for the chunks of its own sequence (the
+  // next linear ids), and every XCD dispatches its share of the grid in order, so a sibling of the
+  // lowest waiting chunk-0 is queued behind lower-numbered workgroups only -- none of which waits
+  // except that chunk-0 itself -- and is dispatched once they finish.  (The wait is bounded all
+  // the same.)
   // A draw grid smaller than the chip (up to 256 chunks) takes one workgroup per 2048-token
   // segment instead of one per chunk.
   constexpr long long kDrawRound = 1536;
