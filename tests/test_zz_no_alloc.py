@@ -68,3 +68,43 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
                                     fake, fake, fake, None)
     assert st == -7
     assert b"scratch" in lib.specdec_status_string(st)
+
+
+def test_noalloc_at_the_largest_batch_its_scratch_holds():
+    # K = 3, V = 32000: the largest B whose workspace fits the scratch runs and matches
+    # specdec_verify bit for bit; one sequence more is refused before any launch.  One-hot drafts
+    # (no draft tensor), inputs drawn on the device: about 3 GB of bf16 logits.
+    lib = load_library()
+    K, V = 3, 32000
+    lim = lib.specdec_noalloc_scratch_bytes()
+    B = 1
+    while lib.specdec_workspace_size(2 * B, K, V) <= lim:
+        B *= 2
+    lo, hi = B, 2 * B                       # largest B with workspace_size(B) <= lim in [lo, hi)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if lib.specdec_workspace_size(mid, K, V) <= lim else (lo, mid)
+    B = lo
+    print(f"\n[case] noalloc largest batch B={B} K={K} V={V}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(941)
+    logits = (torch.randn((B, K + 1, V), generator=g, device=DEV) * 3.0).to(torch.bfloat16)
+    proposed = torch.randint(0, V, (B, K), generator=g, device=DEV, dtype=torch.int32)
+    temperature = torch.rand(B, generator=g, device=DEV) * 0.7 + 0.5
+    uniforms = torch.rand((B, K + 1), generator=g, device=DEV).clamp_(max=0.999999)
+    onehot = torch.ones(B, dtype=torch.uint8, device=DEV)
+    want = specdec_verify(logits, None, proposed, temperature, uniforms, draft_onehot=onehot)
+    out = (torch.empty(B, dtype=torch.int32, device=DEV),
+           torch.empty((B, K + 1), dtype=torch.int32, device=DEV),
+           torch.empty((B, K + 1), dtype=torch.float32, device=DEV))
+    got = specdec_verify_noalloc(logits, None, proposed, temperature, uniforms,
+                                 draft_onehot=onehot, out=out)
+    torch.cuda.synchronize()
+    for a, w in zip(got, want):
+        assert np.array_equal(_bits(a), _bits(w))
+    assert (got[0].cpu().numpy() >= 0).all()
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.specdec_verify_noalloc(fake, 1, None, fake, fake, None, fake, fake, B + 1, K, V,
+                                    fake, fake, fake, None)
+    assert st == -7
+    del logits, proposed, temperature, uniforms, onehot, want, out, got
+    torch.cuda.empty_cache()
