@@ -375,6 +375,39 @@ def bench_match(dev, stream, steps=300, replicas=6):
             "mean_accept_len": float(acc.mean()), **spread}
 
 
+def bench_greedy(dev, stream, steps=300, replicas=6):
+    """Greedy verify (specdec_verify_greedy: every row at temperature 0, accept x_i iff it is
+    the row's lowest argmax) on the same B=64, k=5, V=128256 bf16 batch: verified draft
+    positions per second and the algorithmic bytes (every used logit row once, ids, outputs; no
+    draft row, temperature or uniform is read) against the HBM peak."""
+    import torch
+    from speculative_decoding_verification_specdec_amd import (inputs_to_device,
+                                                               specdec_verify_greedy,
+                                                               specdec_workspace_size)
+    from speculative_decoding_verification_specdec_amd.inputs import batch64
+    inp = batch64()
+    B, K, V = inp.B, inp.K, inp.V
+    ws = torch.zeros(specdec_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+    out = (torch.empty(B, dtype=torch.int32, device=dev),
+           torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+           torch.empty((B, K + 1), dtype=torch.float32, device=dev))
+    calls = []
+    for _ in range(replicas):
+        d = inputs_to_device(inp, dev)
+        calls.append(lambda d=d: specdec_verify_greedy(d["logits"], d["proposed"], out=out,
+                                                       workspace=ws))
+    us, spread = time_replayed(calls, steps, stream)
+    acc = out[0].cpu().numpy()
+    kb = inp.draft_counts()
+    positions = int(kb.sum())
+    nbytes = float(((kb + 1) * V * 2).sum() + (4 * kb + 8 * (kb + 1) + 4).sum())
+    return {"workload": "batch64 (B=64, k=5, V=128256, bf16), greedy verify",
+            "us_per_call": us, "verified_positions_per_s": positions / (us * 1e-6),
+            "algorithmic_GBps": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mean_accept_len": float(acc.mean()), **spread}
+
+
 def bench_group_pipeline(dev, groups, steps=400, replicas=4):
     """The alternative of pipelining sequence groups across two streams, measured: the batch64
     batch split into ``groups`` groups of sequences, each its own specdec_verify call with its own
@@ -722,6 +755,8 @@ def main():
         res["next_rows"]["commit"] = bench_commit(dev, stream)
         print("[bench] sample-and-match verify", file=sys.stderr, flush=True)
         res["next_rows"]["verify_match"] = bench_match(dev, stream)
+        print("[bench] greedy verify", file=sys.stderr, flush=True)
+        res["next_rows"]["verify_greedy"] = bench_greedy(dev, stream)
         print("[bench] telemetry", file=sys.stderr, flush=True)
         res["next_rows"]["telemetry"] = bench_telemetry(dev, stream)
     if not args.no_other_workloads:
