@@ -33,7 +33,7 @@ def test_median_and_spread():
 
 
 def test_algorithmic_bytes_bounds():
-    # The survey's byte model on a tiny batch, worked by hand: B = 2, K = 2, V = 10, fp32 logits;
+    # The algorithmic byte model on a tiny batch, worked by hand: B = 2, K = 2, V = 10, fp32 logits;
     # sequence 0 a model draft (rejected at slot 1), sequence 1 one-hot (all accepted).
     import numpy as np
 
