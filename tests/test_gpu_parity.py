@@ -414,7 +414,14 @@ NEAR_IDENTICAL = {
     "near_identical_small_vocab": lambda: gen.make_batch(4096, 5, 500, seed=72, draft_scale=1.0,
                                                          draft_sigma=0.05, draft_at_row_temp=True,
                                                          name="near_identical_small_vocab"),
+    # About a hundred rejections on the streaming kernels (five chunks, a ragged last one).
+    "near_identical_many_rejections": lambda: gen.make_batch(1024, 5, 40000, seed=73,
+                                                             draft_scale=1.0, draft_sigma=0.05,
+                                                             draft_at_row_temp=True,
+                                                             name="near_identical_many"),
 }
+NEAR_IDENTICAL_MIN_REJECTIONS = {"near_identical_batch": 20, "near_identical_small_vocab": 300,
+                                 "near_identical_many_rejections": 80}
 
 
 @pytest.mark.parametrize("name", list(NEAR_IDENTICAL))
@@ -424,4 +431,4 @@ def test_parity_near_identical_drafter(name):
     ref = oracle.verify(inp)
     rejected = int(((ref.accept_len >= 0) & (ref.accept_len < inp.draft_counts())).sum())
     print("[rejections]", rejected, flush=True)
-    assert rejected >= 20
+    assert rejected >= NEAR_IDENTICAL_MIN_REJECTIONS[name]
