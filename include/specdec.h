@@ -25,7 +25,8 @@
  * the first mismatch (or as the bonus).  Sampling is inverse-CDF over ascending token id:
  * the first token whose running weight sum exceeds u times the total.  One-hot rows
  * (n-gram / prompt-lookup drafters, q_i = onehot(x_i)) accept iff u < p_i(x_i) and redraw
- * from p_i with x_i removed.
+ * from p_i with x_i removed.  A rejection whose residual max(0, p_i - q_i) has no mass (only
+ * possible when q_i is not a probability distribution) draws from p_i itself.
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is DEVICE memory on the current HIP device, except where
@@ -113,6 +114,10 @@ size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V);
  *                             specdec_workspace_size(B, K, V) bytes, 16-byte aligned.
  * stream                      hipStream_t (NULL = default stream).
  * The caller rolls both KV caches back to prefix + accept_len[b] + 1 tokens.
+ * On the streaming path the draw of a sequence is picked by one workgroup that waits, with a
+ * bound (2^20 polls, about a second), for the other workgroups of its sequence; they are always
+ * dispatched ahead of it, so the wait ends, but if it ever gave up (those workgroups unable to
+ * run for that long) the sequence would be reported invalid rather than the call hanging.
  */
 specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
                               const float* draft_probs, const uint8_t* draft_onehot,
@@ -158,9 +163,10 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
 /* Execution paths.  Rows of at most SPECDEC_SMALL_V_MAX tokens fit one wavefront's registers,
  * so by default such calls run one kernel in which a group of lanes handles each sequence (a
  * whole wave64, or 16 or 8 lanes of one for rows of at most 64 or 32 tokens; every row read once,
- * the draw taken from registers); larger vocabularies run the streaming kernels (three launches:
- * one 256-thread workgroup per 8192-logit chunk of each row, then the accept scan and draw, then
- * the pick).  SPECDEC_PATH_STREAMING forces the streaming kernels at any V,
+ * the draw taken from registers); larger vocabularies run the streaming kernels: one 256-thread
+ * workgroup per 8192-logit chunk of each row, then one launch for the accept scan, the draw and
+ * its pick (when B times the number of chunks exceeds 1536, three: a scan pass, the draw pass and a
+ * pick kernel).  SPECDEC_PATH_STREAMING forces the streaming kernels at any V,
  * SPECDEC_PATH_SMALL_VOCAB the small-vocabulary kernel (an error, SPECDEC_ERR_SHAPE, when
  * V > SPECDEC_SMALL_V_MAX), and SPECDEC_PATH_ONE_LAUNCH the same streaming work in a single launch
  * whose workgroups hand partial results to each other through the workspace (plus a small
