@@ -115,9 +115,10 @@ size_t specdec_workspace_size(int32_t B, int32_t K, int32_t V);
  * stream                      hipStream_t (NULL = default stream).
  * The caller rolls both KV caches back to prefix + accept_len[b] + 1 tokens.
  * On the streaming path the draw of a sequence is picked by one workgroup that waits, with a
- * bound (2^20 polls, about a second), for the other workgroups of its sequence; they are always
- * dispatched ahead of it, so the wait ends, but if it ever gave up (those workgroups unable to
- * run for that long) the sequence would be reported invalid rather than the call hanging.
+ * bound (2^20 polls, about a second), for the other workgroups of its sequence; they come right
+ * after it in dispatch order and none of them waits, so the wait ends, but if it ever gave up
+ * (those workgroups unable to run for that long) the sequence would be reported invalid rather
+ * than the call hanging.
  */
 specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
                               const float* draft_probs, const uint8_t* draft_onehot,
