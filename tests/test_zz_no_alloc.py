@@ -108,3 +108,42 @@ def test_noalloc_at_the_largest_batch_its_scratch_holds():
     assert st == -7
     del logits, proposed, temperature, uniforms, onehot, want, out, got
     torch.cuda.empty_cache()
+
+
+def test_noalloc_calls_replay_from_a_hip_graph():
+    # The callers it is for: two calls captured in one HIP graph (after a first eager call on the
+    # device), replayed several times with eager work in between, each replay bit-identical to
+    # the eager results.
+    inp = [gen.make_batch(24, 4, 30000, seed=951, onehot_frac=0.25, ragged=True),
+           gen.make_batch(8, 2, 700, seed=952, dtype="f32")]
+    d = [inputs_to_device(x, DEV) for x in inp]
+    outs = [(torch.empty(x.B, dtype=torch.int32, device=DEV),
+             torch.empty((x.B, x.K + 1), dtype=torch.int32, device=DEV),
+             torch.empty((x.B, x.K + 1), dtype=torch.float32, device=DEV)) for x in inp]
+
+    def calls():
+        for dd, out in zip(d, outs):
+            specdec_verify_noalloc(dd["logits"], dd["draft_probs"], dd["proposed"],
+                                   dd["temperature"], dd["uniforms"],
+                                   draft_onehot=dd["draft_onehot"], num_draft=dd["num_draft"],
+                                   out=out)
+    calls()
+    torch.cuda.synchronize()
+    want = [[_bits(t).copy() for t in out] for out in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for out in outs:
+            for t in out:
+                t.fill_(-3)
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        del junk
+        for out, w in zip(outs, want):
+            for t, wt in zip(out, w):
+                assert np.array_equal(_bits(t), wt), rep
