@@ -134,8 +134,10 @@ specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
  * device holds for the life of the process; its address is looked up once per device, on the
  * first call made with that device current.  The call allocates nothing (no hipMalloc, no
  * library allocation).  Arguments, outputs, data errors and results are those of
- * specdec_verify (automatic path) with the same inputs.  Returns SPECDEC_ERR_SCRATCH, before
- * any launch, when specdec_workspace_size(B, K, V) exceeds the scratch (for example B = 64,
+ * specdec_verify (automatic path) with the same inputs.  Its argument checks (sizes, dtype,
+ * NULL and misaligned pointers, with specdec_verify's status codes) run on the host before any
+ * HIP call; after them it returns SPECDEC_ERR_SCRATCH, still before any HIP call, when
+ * specdec_workspace_size(B, K, V) exceeds the scratch (for example B = 64,
  * K = 5, V = 128256 needs about 1.0 MB; B = 512, K = 8, V = 128256 about 11 MB).  Every call
  * on one device shares that device's scratch: calls that overlap in time on one device (other
  * streams, other threads) race; consecutive calls on one stream do not. */

@@ -27,24 +27,46 @@ specdec_status check_sizes(int32_t B, int32_t K, int32_t V, int32_t dtype) {
   return SPECDEC_OK;
 }
 
-specdec_status run(const void* target_logits, int32_t logits_dtype, const float* draft_probs,
-                   const uint8_t* draft_onehot, const int32_t* proposed,
-                   const int32_t* num_draft, const float* temperature, const float* uniforms,
-                   int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
-                   float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
-                   const specdec_options* opts, bool greedy_all, bool match = false) {
+}  // namespace
+
+namespace specdec {
+
+specdec_status check_verify_args(const void* target_logits, int32_t logits_dtype,
+                                 const float* draft_probs, const int32_t* proposed,
+                                 const int32_t* num_draft, const float* temperature,
+                                 const float* uniforms, int32_t B, int32_t K, int32_t V,
+                                 const int32_t* accept_len, const int32_t* out_tokens,
+                                 const float* out_probs, bool greedy_all) {
   specdec_status st = check_sizes(B, K, V, logits_dtype);
-  if (st != SPECDEC_OK) return st;
-  if (B == 0) return SPECDEC_OK;
-  if (!target_logits || !accept_len || !out_tokens || !workspace) return SPECDEC_ERR_NULL;
+  if (st != SPECDEC_OK || B == 0) return st;
+  if (!target_logits || !accept_len || !out_tokens) return SPECDEC_ERR_NULL;
   if (K > 0 && !proposed) return SPECDEC_ERR_NULL;
   if (!greedy_all && (!temperature || !uniforms)) return SPECDEC_ERR_NULL;
   const size_t esize = logits_dtype == SPECDEC_BF16 ? 2 : 4;
   if (misaligned(target_logits, esize) || misaligned(draft_probs, 4) ||
       misaligned(proposed, 4) || misaligned(num_draft, 4) || misaligned(temperature, 4) ||
       misaligned(uniforms, 4) || misaligned(accept_len, 4) || misaligned(out_tokens, 4) ||
-      misaligned(out_probs, 4) || misaligned(workspace, 16))
+      misaligned(out_probs, 4))
     return SPECDEC_ERR_ALIGN;
+  return SPECDEC_OK;
+}
+
+}  // namespace specdec
+
+namespace {
+
+specdec_status run(const void* target_logits, int32_t logits_dtype, const float* draft_probs,
+                   const uint8_t* draft_onehot, const int32_t* proposed,
+                   const int32_t* num_draft, const float* temperature, const float* uniforms,
+                   int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                   float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
+                   const specdec_options* opts, bool greedy_all, bool match = false) {
+  const specdec_status st = specdec::check_verify_args(
+      target_logits, logits_dtype, draft_probs, proposed, num_draft, temperature, uniforms, B, K,
+      V, accept_len, out_tokens, out_probs, greedy_all);
+  if (st != SPECDEC_OK || B == 0) return st;
+  if (!workspace) return SPECDEC_ERR_NULL;
+  if (misaligned(workspace, 16)) return SPECDEC_ERR_ALIGN;
   if (workspace_bytes < specdec::workspace_bytes(B, K, V)) return SPECDEC_ERR_WORKSPACE;
 
   specdec::LaunchArgs a{};

@@ -39,6 +39,16 @@ void* scratch_address() {
 
 }  // namespace
 
+namespace specdec {
+// Host checks of a verify call's arguments other than its workspace (api.cpp).
+specdec_status check_verify_args(const void* target_logits, int32_t logits_dtype,
+                                 const float* draft_probs, const int32_t* proposed,
+                                 const int32_t* num_draft, const float* temperature,
+                                 const float* uniforms, int32_t B, int32_t K, int32_t V,
+                                 const int32_t* accept_len, const int32_t* out_tokens,
+                                 const float* out_probs, bool greedy_all);
+}  // namespace specdec
+
 extern "C" {
 
 size_t specdec_noalloc_scratch_bytes(void) { return SPECDEC_NOALLOC_SCRATCH_BYTES; }
@@ -49,12 +59,13 @@ specdec_status specdec_verify_noalloc(const void* target_logits, int32_t logits_
                                       const float* temperature, const float* uniforms, int32_t B,
                                       int32_t K, int32_t V, int32_t* accept_len,
                                       int32_t* out_tokens, float* out_probs, void* stream) {
-  // Sizes first: a call whose workspace would not fit the array is refused before anything
-  // touches the device.
-  const size_t need = specdec_workspace_size(B, K, V);
-  if (B > 0 && need == 0) return SPECDEC_ERR_SHAPE;
-  if (need > SPECDEC_NOALLOC_SCRATCH_BYTES) return SPECDEC_ERR_SCRATCH;
-  if (B == 0) return SPECDEC_OK;
+  // Every host check first -- the arguments as specdec_verify checks them, then whether the
+  // workspace fits the array -- so that a refused call never touches the device.
+  const specdec_status st = specdec::check_verify_args(
+      target_logits, logits_dtype, draft_probs, proposed, num_draft, temperature, uniforms, B, K,
+      V, accept_len, out_tokens, out_probs, false);
+  if (st != SPECDEC_OK || B == 0) return st;
+  if (specdec_workspace_size(B, K, V) > SPECDEC_NOALLOC_SCRATCH_BYTES) return SPECDEC_ERR_SCRATCH;
   void* ws = scratch_address();
   if (ws == nullptr) return SPECDEC_ERR_LAUNCH;
   return specdec_verify(target_logits, logits_dtype, draft_probs, draft_onehot, proposed,

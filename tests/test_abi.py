@@ -80,6 +80,33 @@ def test_host_side_errors(lib, kw, status):
     assert _verify(lib, **kw) == status
 
 
+def _noalloc(lib, **kw):
+    a = dict(logits=FAKE, dtype=1, q=FAKE, onehot=None, prop=FAKE, nd=None, T=FAKE, U=FAKE,
+             B=4, K=3, V=64, acc=FAKE, tok=FAKE, prb=FAKE, stream=None)
+    a.update(kw)
+    return lib.specdec_verify_noalloc(a["logits"], a["dtype"], a["q"], a["onehot"], a["prop"],
+                                      a["nd"], a["T"], a["U"], a["B"], a["K"], a["V"], a["acc"],
+                                      a["tok"], a["prb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -2), (dict(K=64), -2), (dict(V=0), -2), (dict(dtype=7), -3),
+    (dict(logits=None), -1), (dict(acc=None), -1), (dict(tok=None), -1), (dict(prop=None), -1),
+    (dict(T=None), -1), (dict(U=None), -1),
+    (dict(logits=FAKE + 1), -4), (dict(q=FAKE + 2), -4), (dict(tok=FAKE + 2), -4),
+    (dict(B=1 << 20, K=5, V=128256), -7),
+])
+def test_noalloc_host_side_errors(lib, kw, status):
+    # The entry point without a workspace checks its arguments as specdec_verify does, and then
+    # whether the workspace fits its built-in scratch, all before any HIP call.
+    assert _noalloc(lib, **kw) == status
+
+
+def test_noalloc_empty_batch_is_a_no_op(lib):
+    assert _noalloc(lib, B=0, logits=None, acc=None, tok=None) == 0
+    assert lib.specdec_noalloc_scratch_bytes() == 32 << 20
+
+
 def test_path_option_errors(lib):
     # An unknown path, and the small-vocabulary path asked for a vocabulary above its limit, are shape
     # errors found before any launch.

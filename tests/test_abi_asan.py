@@ -1,6 +1,6 @@
 """The C ABI's host-side code under AddressSanitizer, on the CPU: tests/test_abi.py (argument
 checks, status codes, workspace sizes, the host planner arithmetic, the no-alloc entry point's
-size check) run in a child process against libspecdec_asan.so -- the same sources with the host
+host checks) run in a child process against libspecdec_asan.so -- the same sources with the host
 code built with -fsanitize=address, the device code as usual -- with the sanitizer's runtime
 preloaded.  The sanitized library is rebuilt when it is missing or older than a source.  Skipped
 where the runtime is absent, or where the environment already preloads a library (the sanitizer
