@@ -70,20 +70,35 @@ def test_several_tiles_and_load_paths(cap, misalign):
     check(h, 8, 1, 4, misalign=misalign)
 
 
-def test_matches_that_straddle_a_tile_boundary():
-    # History ending in the run 1 2 3 4 whose only earlier occurrence straddles position 8192,
-    # the boundary between the first two 8192-position tiles.
-    cap = 16400
+@pytest.mark.parametrize("cap,at", [(16400, 8192), (16400, 512), (16400, 1024), (16400, 8704),
+                                    (16402, 8192)])
+def test_matches_that_straddle_a_tile_boundary(cap, at):
+    # History ending in the run 1 2 3 4 whose only earlier occurrence straddles position `at`: the
+    # boundary between the first two 8192-position tiles, or between 512-position steps searched by
+    # different waves of the one-workgroup-per-history kernel (capacity a multiple of 4), or, with
+    # capacity 16402, the tile boundary on the 4-byte load path.
     toks = np.full((1, cap), hist.PAD_TOKEN, dtype=np.int32)
     L = 16390
     body = (np.arange(L) % 997 + 10).astype(np.int32)        # only values >= 10 elsewhere
-    body[8190:8194] = [1, 2, 3, 4]
-    body[8194] = 77
+    body[at - 2:at + 2] = [1, 2, 3, 4]
+    body[at + 2] = 77
     body[L - 4:] = [1, 2, 3, 4]
     toks[0, :L] = body
-    h = hist.Histories(toks, np.array([L], dtype=np.int32), 1000, name="straddle")
+    h = hist.Histories(toks, np.array([L], dtype=np.int32), 1000, name=f"straddle{at}")
     prop, nd = check(h, 5, 1, 4)
     assert nd[0] == 5 and prop[0, 0] == 77
+
+
+@pytest.mark.parametrize("cap,V,n_max", [(8196, 3, 32), (16384, 40, 8), (40000, 7, 32),
+                                         (65536, 2, 32)])
+def test_one_workgroup_per_history_path(cap, V, n_max):
+    # Capacities above one tile with 16-byte rows: one workgroup per history, its waves taking
+    # 512-position steps in turn.  Lengths from 0 to the capacity (some waves get no step), tiny
+    # vocabularies (candidates everywhere, runs crossing step boundaries and reaching 31 tokens
+    # back into the step before), and the degenerate histories.
+    h = hist.make_histories(24, cap, V, seed=500 + cap + V, len_range=(0, cap), seg_range=(1, 40),
+                            edge_cases=True, name=f"history_path_V{V}")
+    check(h, 12, 1, n_max)
 
 
 def test_invalid_lengths_and_k0():
