@@ -254,9 +254,10 @@ specdec_status specdec_verify_match(const void* target_logits, int32_t logits_dt
  * num_draft   [B]      out   int32 (the verify step's num_draft).
  * workspace                  device scratch of >= specdec_ngram_workspace_size(B, capacity)
  *                            bytes, 16-byte aligned; no initialisation needed.
- * One kernel launch when tokens is 16-byte aligned and capacity a multiple of 4 (one workgroup
- * per history; the workspace is then unused), else two (per-tile keys in the workspace, then
- * one wave per history takes their maximum and copies the proposal) once capacity > 8192.
+ * One kernel launch, one workgroup per history, when capacity <= 8192 or the rows allow 16-byte
+ * loads (tokens 16-byte aligned, capacity a multiple of 4); the workspace is then unused.
+ * Otherwise two: per-tile keys in the workspace, then one wave per history takes their maximum
+ * and copies the proposal.
  * Returns SPECDEC_ERR_SHAPE for out-of-range sizes or n_min / n_max, otherwise as for
  * specdec_verify. */
 #define SPECDEC_NGRAM_MAX_N 32
