@@ -148,18 +148,9 @@ __device__ void stream_part(const KArgs& a, u64* rec, int b, int i, int s, int k
   } else {
     st = fold_wave<LT, kVec, false>(x, c, c0, lane, -1, lane_max, pre);
   }
-  int arg = 0;
-  if (T == 0.f) {
-    // Greedy row: the lowest token index attaining the sub-chunk max.  Only lanes whose own
-    // max is that max search their registers.
-    int am = INT_MAX;
-    if (lane_max == st.m) {
-#pragma unroll
-      for (int j = kPerThread - 1; j >= 0; --j)
-        if (x[j] == st.m) am = tok_of<LT, kVec>(c0, lane, j);
-    }
-    arg = wave_min(am);
-  }
+  // Greedy row: the lowest token index attaining the sub-chunk max.
+  const int arg = T == 0.f ? lowest_token_of<LT, kVec>(x, st.m, c0) : 0;
+  (void)lane_max;
   if (lane < 4) {
     const uint32_t v = lane == 0   ? __float_as_uint(st.m)
                        : lane == 1 ? __float_as_uint(st.s)

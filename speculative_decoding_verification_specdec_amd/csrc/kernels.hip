@@ -232,18 +232,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   } else {
     st = fold_wave<LT, kVec, false>(x, c, c0, lane, -1, lane_max, pre);
   }
-  int arg = 0;
-  if (T == 0.f) {
-    // Greedy row: the lowest token index attaining the sub-chunk max.  Only lanes whose own
-    // max is that max search their registers.
-    int a = INT_MAX;
-    if (lane_max == st.m) {
-#pragma unroll
-      for (int j = kPerThread - 1; j >= 0; --j)
-        if (x[j] == st.m) a = tok_of<LT, kVec>(c0, lane, j);
-    }
-    arg = wave_min(a);
-  }
+  // Greedy row: the lowest token index attaining the sub-chunk max.
+  const int arg = T == 0.f ? lowest_token_of<LT, kVec>(x, st.m, c0) : 0;
+  (void)lane_max;
   if (lane == 0)
     partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, pre};
 }

@@ -206,6 +206,40 @@ __device__ __forceinline__ void load_sub(const LT* __restrict__ row, int c0, int
   }
 }
 
+// The lowest token index of the wave's sub-chunk holding the value M (INT_MAX when none does),
+// from one ballot per register: tokens ascend with (16-byte vector u, lane, element k) on the
+// vector path and with (register j, lane) on the scalar one, so the first register group with a
+// hit, its lowest hit lane and that lane's first hit element name the token.  The result is
+// wave-uniform; no cross-lane reduction is needed.
+template <typename LT, bool kVec>
+__device__ __forceinline__ int lowest_token_of(const float (&x)[kPerThread], float M, int c0) {
+  if constexpr (kVec) {
+    constexpr int P = Vec<LT>::kPer;
+    constexpr int U = kPerThread / P;
+    for (int u = 0; u < U; ++u) {
+      unsigned long long hit[P];
+      unsigned long long any = 0ull;
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        hit[k] = __ballot(x[u * P + k] == M);
+        any |= hit[k];
+      }
+      if (any != 0ull) {
+        const int l = __ffsll(static_cast<long long>(any)) - 1;
+#pragma unroll
+        for (int k = 0; k < P; ++k)
+          if ((hit[k] >> l) & 1ull) return c0 + (u * 64 + l) * P + k;
+      }
+    }
+  } else {
+    for (int j = 0; j < kPerThread; ++j) {
+      const unsigned long long hit = __ballot(x[j] == M);
+      if (hit != 0ull) return c0 + j * 64 + __ffsll(static_cast<long long>(hit)) - 1;
+    }
+  }
+  return INT_MAX;
+}
+
 template <typename LT, bool kVec>
 __device__ __forceinline__ int tok_of(int c0, int lane, int j) {
   if constexpr (kVec) {
