@@ -533,9 +533,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["auto", "one_launch"], default="auto",
-                    help="streaming path of the headline call: the default three launches, or the "
-                         "one-launch alternative kept for comparison")
+    ap.add_argument("--path", choices=["auto", "one_launch", "quad"], default="auto",
+                    help="streaming path of the headline call: the default three launches, or one of "
+                         "the one-launch alternatives kept for comparison (workgroups per 8192-token "
+                         "tile, or four workgroups per sequence)")
     ap.add_argument("--cpu-budget", type=float, default=6.0,
                     help="seconds of the single-thread oracle leg")
     ap.add_argument("--no-next-rows", action="store_true",
@@ -584,8 +585,10 @@ def main():
         return
     from speculative_decoding_verification_specdec_amd.binding import (SPECDEC_PATH_AUTO,
                                                                        SPECDEC_PATH_ONE_LAUNCH,
+                                                                       SPECDEC_PATH_QUAD,
                                                                        PreparedVerify)
-    path = SPECDEC_PATH_ONE_LAUNCH if args.path == "one_launch" else SPECDEC_PATH_AUTO
+    path = {"one_launch": SPECDEC_PATH_ONE_LAUNCH, "quad": SPECDEC_PATH_QUAD}.get(args.path,
+                                                                               SPECDEC_PATH_AUTO)
     if args.group_pipeline:
         print(json.dumps({"group_pipeline": bench_group_pipeline(dev, args.group_pipeline)}))
         return
@@ -687,7 +690,8 @@ def main():
     positions = int(inp.draft_counts().sum())
     value = positions / (ms_per_step * 1e-3)
     achieved = logit_bytes / (hot_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    # The counters summarised under profiles/ are the default path's streaming kernel's.
+    traffic = measured_traffic() if args.path == "auto" else None
     draft_bytes = draft_row_bytes(inp, acc_np)
 
     res = {
@@ -710,7 +714,9 @@ def main():
             "replicas_rotated": args.replicas,
         },
         "roofline": {
-            "kernel": HOT_KERNEL,
+            # On the one-launch alternatives the timed kernel does the whole call.
+            "kernel": {"auto": HOT_KERNEL, "one_launch": "verify_kernel",
+                       "quad": "quad_verify_kernel"}[args.path],
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

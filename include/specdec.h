@@ -173,14 +173,23 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
  * SPECDEC_PATH_SMALL_VOCAB the small-vocabulary kernel (an error, SPECDEC_ERR_SHAPE, when
  * V > SPECDEC_SMALL_V_MAX), and SPECDEC_PATH_ONE_LAUNCH the same streaming work in a single launch
  * whose workgroups hand partial results to each other through the workspace (plus a small
- * zero-fill launch before it); it is slower on MI355X and kept for comparison.  Every path
- * implements the same rule and passes the same parity tests.  specdec_verify_greedy and
- * specdec_verify_match take the automatic choice. */
+ * zero-fill launch before it); it is slower on MI355X and kept for comparison.
+ * SPECDEC_PATH_QUAD runs one launch of four 1024-thread workgroups per sequence, each streaming a
+ * quarter of every row and exchanging quarter statistics and draw sums with the others through
+ * tagged words in the workspace (no initialisation needed; each sequence keeps a counter there
+ * that every call advances); it takes rows of whole 8-token groups (V a multiple of 8), 16-byte
+ * aligned logits and draft rows, at most 32 2048-token segments per quarter (V <= 262144), no
+ * sample-and-match mode, and no more sequences than leave all 4 B workgroups resident on the
+ * device at once (B <= 64 on MI355X), else SPECDEC_ERR_SHAPE.  It measured even with the default
+ * at B = 64, k = 5, V = 128256 and slower on smaller or ragged batches, and is kept for
+ * comparison.  Every path implements the same rule and passes the same parity tests.
+ * specdec_verify_greedy and specdec_verify_match take the automatic choice. */
 #define SPECDEC_SMALL_V_MAX 1024
 #define SPECDEC_PATH_AUTO 0
 #define SPECDEC_PATH_STREAMING 1
 #define SPECDEC_PATH_SMALL_VOCAB 2
 #define SPECDEC_PATH_ONE_LAUNCH 3
+#define SPECDEC_PATH_QUAD 4
 
 /* Options of specdec_verify_ex.
  *   hot_event_begin / hot_event_end: measurement hook, HIP events (hipEvent_t, host handles)
@@ -192,8 +201,8 @@ specdec_status specdec_verify_greedy(const void* target_logits, int32_t logits_d
  *     streaming kernel on the streaming path (accept scan, draw sums and pick): begin is recorded
  *     when the first of them starts, end when the last completes.  Not recorded on the
  *     small-vocabulary and one-launch paths (one kernel there).  Either may be NULL.
- *   spin_limit: SPECDEC_PATH_ONE_LAUNCH only: polls a workgroup makes while it waits for a
- *     hand-off from another workgroup of the launch (0 = the default, 2^20 polls, about a second;
+ *   spin_limit: SPECDEC_PATH_ONE_LAUNCH and SPECDEC_PATH_QUAD: polls a workgroup makes while it
+ *     waits for a hand-off from another workgroup of the launch (0 = the default, 2^20 polls, about a second;
  *     negative = SPECDEC_ERR_SHAPE).  A wait that gives up reports its sequence as invalid
  *     (accept_len -1) instead of waiting longer, so the launch always completes; a small limit
  *     exercises that path in tests.

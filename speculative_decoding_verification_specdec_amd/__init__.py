@@ -11,7 +11,7 @@ from .binding import (SpecdecError, specdec_verify, specdec_verify_greedy, specd
                       specdec_commit, specdec_verify_match, specdec_telemetry_update,
                       specdec_apply_k, specdec_plan_k, telemetry_counters,
                       SPECDEC_PATH_AUTO, SPECDEC_PATH_STREAMING, SPECDEC_PATH_SMALL_VOCAB,
-                      SPECDEC_SMALL_V_MAX, SPECDEC_PATH_ONE_LAUNCH, new_workspace,
+                      SPECDEC_SMALL_V_MAX, SPECDEC_PATH_ONE_LAUNCH, SPECDEC_PATH_QUAD, new_workspace,
                       specdec_verify_noalloc)
 
 __all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_workspace_size",
@@ -20,4 +20,5 @@ __all__ = ["SpecdecError", "specdec_verify", "specdec_verify_greedy", "specdec_w
            "specdec_verify_match", "specdec_telemetry_update", "specdec_apply_k",
            "specdec_plan_k", "telemetry_counters", "SPECDEC_PATH_AUTO", "SPECDEC_PATH_STREAMING",
            "SPECDEC_PATH_SMALL_VOCAB", "SPECDEC_SMALL_V_MAX", "SPECDEC_PATH_ONE_LAUNCH",
+           "SPECDEC_PATH_QUAD",
            "new_workspace", "specdec_verify_noalloc"]

@@ -36,6 +36,7 @@ class _Options(ctypes.Structure):
 SPECDEC_SMALL_V_MAX = 1024
 SPECDEC_PATH_AUTO, SPECDEC_PATH_STREAMING, SPECDEC_PATH_SMALL_VOCAB = 0, 1, 2
 SPECDEC_PATH_ONE_LAUNCH = 3
+SPECDEC_PATH_QUAD = 4
 
 
 def _event_pair(events):

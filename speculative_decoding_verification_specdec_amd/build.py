@@ -12,7 +12,7 @@ import sys
 PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 SOURCES = [PKG / "csrc" / "kernels.hip", PKG / "csrc" / "fused.hip", PKG / "csrc" / "small.hip", PKG / "csrc" / "ngram.hip",
-           PKG / "csrc" / "commit.hip", PKG / "csrc" / "noalloc.hip",
+           PKG / "csrc" / "commit.hip", PKG / "csrc" / "noalloc.hip", PKG / "csrc" / "quad.hip",
            PKG / "csrc" / "telemetry.hip", PKG / "csrc" / "api.cpp", PKG / "csrc" / "telemetry.cpp"]
 HEADERS = [PKG / "csrc" / "kernels.h", PKG / "csrc" / "verify_dev.h", PKG / "csrc" / "wave_ops.h", ROOT / "include" / "specdec.h"]
 OUTPUT = PKG / "libspecdec.so"

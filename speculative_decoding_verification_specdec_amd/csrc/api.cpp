@@ -8,7 +8,8 @@
 #include "specdec.h"
 
 static_assert(SPECDEC_SMALL_V_MAX == specdec::kSmallVMax, "small-vocabulary path limit");
-static_assert(SPECDEC_PATH_ONE_LAUNCH == 3, "path numbering shared with kernels.h");
+static_assert(SPECDEC_PATH_ONE_LAUNCH == 3 && SPECDEC_PATH_QUAD == 4,
+              "path numbering shared with kernels.h");
 
 namespace {
 
@@ -96,10 +97,12 @@ specdec_status run(const void* target_logits, int32_t logits_dtype, const float*
   a.spin_limit = opts ? opts->spin_limit : 0;
   if (a.spin_limit < 0) return SPECDEC_ERR_SHAPE;
   if (a.path != SPECDEC_PATH_AUTO && a.path != SPECDEC_PATH_STREAMING &&
-      a.path != SPECDEC_PATH_SMALL_VOCAB && a.path != SPECDEC_PATH_ONE_LAUNCH)
+      a.path != SPECDEC_PATH_SMALL_VOCAB && a.path != SPECDEC_PATH_ONE_LAUNCH &&
+      a.path != SPECDEC_PATH_QUAD)
     return SPECDEC_ERR_SHAPE;
   if (a.path == SPECDEC_PATH_SMALL_VOCAB && V > SPECDEC_SMALL_V_MAX)
     return SPECDEC_ERR_SHAPE;
+  if (a.path == SPECDEC_PATH_QUAD && !specdec::quad_eligible(a)) return SPECDEC_ERR_SHAPE;
   return specdec::launch_verify(a) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 

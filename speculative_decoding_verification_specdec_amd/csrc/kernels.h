@@ -125,12 +125,22 @@ struct LaunchArgs {
   hipEvent_t draw_begin;     // optional, recorded around the kernels after the streaming kernel
   hipEvent_t draw_end;       // (streaming path)
   int path;                  // 0: automatic, 1: three launches, 2: small-vocabulary kernel,
-                             // 3: one launch
+                             // 3: one launch, 4: four workgroups per sequence, one launch
   int spin_limit;            // polls of the one-launch path's bounded waits (0: the default)
 };
 
 // Largest vocabulary the small-vocabulary path takes (four 4-token quads per lane of a wave).
 constexpr int kSmallVMax = 1024;
+
+// Four workgroups per sequence, one launch (quad.hip): quarter q of every row covers tokens
+// [q * span, (q + 1) * span), span a whole number of 2048-token segments, at most kMaxQuadSeg.
+constexpr int kMaxQuadSeg = 32;
+__host__ __device__ inline int quad_span(int V) {
+  return (V + 4 * kSeg - 1) / (4 * kSeg) * kSeg;
+}
+size_t quad_workspace_bytes(int B, int K, int V);
+bool quad_eligible(const LaunchArgs& a);  // shapes, alignment, and the whole grid resident at once
+hipError_t launch_quad(const LaunchArgs& a);
 
 hipError_t launch_verify(const LaunchArgs& a);
 hipError_t launch_small_verify(const LaunchArgs& a);  // small.hip; V <= kSmallVMax

@@ -239,60 +239,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     partials[r * (S * kWaves) + s * kWaves + wave] = RowPartial{st.m, st.s, arg, pre};
 }
 
-// ------------------------------------------------------------------------------------------
-// Inverse-CDF draw ("Decodificação especulativa explicada", section "Amostragem especulativa em
-// numpy, com prova": the first running sum above u times the total, over ascending token id),
-// from per-segment weight sums: one fp64 DPP scan over the segment sums finds the segment holding
-// u * total (plain p when the draw's total is not positive), then a workgroup scan of that one
-// segment finds the token.
-// ------------------------------------------------------------------------------------------
-struct PickLds {
-  int seg, plain, flag, hit[kWaves], lastpos[kWaves];
-  float zhit[kWaves], zlast[kWaves];
-  double t, base, wtot[kWaves];
-};
-
-// First step, in wave 0: lane l holds the sums (lw: the draw's weights; le: those of p) of its
-// segments [l * P, l * P + P); seg_at(j, plain) gives segment j's sum again.  Leaves the segment,
-// the target u * total and the running sum before the segment in ps.  Returns false (in every
-// lane) when the weights' total is NaN -- a draft row holding a value that is not a probability
-// -- and the sequence is to be reported invalid.
-template <typename SegAt>
-__device__ __forceinline__ bool find_draw_segment(double lw, double le, float u, int nseg, int P,
-                                                  SegAt seg_at, PickLds& ps, int lane) {
-  const int j0 = lane * P;
-  const double iw = wave_inclusive_scan(lw), ie = wave_inclusive_scan(le);
-  const double total_w = read_lane_d(iw, 63);
-  if (total_w != total_w) return false;
-  const bool plain = !(total_w > 0.0);  // empty residual: draw from p itself
-  const double inc = plain ? ie : iw;
-  const double own = plain ? le : lw;
-  const double R = read_lane_d(inc, 63);
-  const double t = static_cast<double>(u) * R;
-  // The first lane whose running total passes t holds the segment; if rounding left t at the
-  // very top, the last lane with positive weight does.
-  const unsigned long long hit = __ballot(own > 0.0 && inc > t);
-  const unsigned long long pos = __ballot(own > 0.0);
-  const int hl = hit ? __ffsll(static_cast<long long>(hit)) - 1
-                     : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
-  if (lane == hl) {
-    double run = inc - own;  // running sum before the lane's segments
-    int seg = -1, lastpos = -1;
-    double base_seg = 0.0, base_last = 0.0;
-    for (int q = 0; q < P && j0 + q < nseg; ++q) {
-      const double v = seg_at(j0 + q, plain);
-      if (v > 0.0) {
-        if (run + v > t) { seg = j0 + q; base_seg = run; break; }
-        lastpos = j0 + q;
-        base_last = run;
-      }
-      run += v;
-    }
-    if (seg < 0) { seg = lastpos >= 0 ? lastpos : j0; base_seg = base_last; }
-    ps.seg = seg; ps.plain = plain; ps.t = t; ps.base = base_seg;
-  }
-  return true;
-}
 
 // Second step, the whole workgroup (after a barrier): scan segment ps.seg of row z (draft row
 // q_row for a residual, else null) in ascending token order; thread 0 writes the token and its
@@ -844,11 +790,12 @@ WorkspaceLayout workspace_layout(int B, int K, int V) {
 
 size_t workspace_bytes(int B, int K, int V) {
   const size_t one = static_cast<size_t>(B) * static_cast<size_t>(record_layout(K, V).words) * 8;
-  return std::max(workspace_layout(B, K, V).total, one);
+  return std::max({workspace_layout(B, K, V).total, one, quad_workspace_bytes(B, K, V)});
 }
 
 hipError_t launch_verify(const LaunchArgs& a) {
   if (a.path == 3) return launch_one_launch(a);
+  if (a.path == 4) return quad_eligible(a) ? launch_quad(a) : hipErrorInvalidConfiguration;
   // Rows of at most kSmallVMax tokens fit one wave's registers: one kernel, a group of lanes
   // per sequence (small.hip), unless the streaming kernels are asked for.
   const bool small = a.V <= kSmallVMax && a.path != 1;

@@ -111,7 +111,8 @@ def test_path_option_errors(lib):
     # An unknown path, and the small-vocabulary path asked for a vocabulary above its limit, are shape
     # errors found before any launch.
     import ctypes
-    from speculative_decoding_verification_specdec_amd.binding import (SPECDEC_PATH_SMALL_VOCAB,
+    from speculative_decoding_verification_specdec_amd.binding import (SPECDEC_PATH_QUAD,
+                                                                       SPECDEC_PATH_SMALL_VOCAB,
                                                                        SPECDEC_SMALL_V_MAX,
                                                                        _Options)
     # Layout of specdec_options: two pointers, two int32, two pointers.
@@ -126,8 +127,11 @@ def test_path_option_errors(lib):
         a = [FAKE, 1, FAKE, None, FAKE, None, FAKE, FAKE, 4, 3, V, FAKE, FAKE, FAKE, FAKE, 1 << 30,
              None]
         return lib.specdec_verify_ex(*a, ctypes.byref(_Options(None, None, path)))
-    assert ex(4, 64) == -2 and ex(-1, 64) == -2
+    assert ex(5, 64) == -2 and ex(-1, 64) == -2
     assert ex(SPECDEC_PATH_SMALL_VOCAB, SPECDEC_SMALL_V_MAX + 1) == -2
+    # The four-workgroups-per-sequence path takes rows of whole 16-byte vectors only (checked
+    # before anything touches the device).
+    assert ex(SPECDEC_PATH_QUAD, 20003) == -2
 
 
 def test_empty_batch_is_a_no_op(lib):
