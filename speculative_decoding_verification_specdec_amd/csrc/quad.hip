@@ -34,6 +34,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 
 #include "kernels.h"
@@ -517,18 +518,20 @@ __global__ __launch_bounds__(kQThreads) void quad_verify_kernel(
 
 template <typename LT>
 int quad_capacity() {
-  // Workgroups of this kernel the device holds at once (cached per device).
-  static int cache[64] = {0};
+  // Workgroups of this kernel the current device holds at once (cached per device; threads that
+  // race to fill an entry store the same value).
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] != 0) return cache[dev];
+  const int known = cache[dev].load(std::memory_order_relaxed);
+  if (known != 0) return known;
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quad_verify_kernel<LT>, kQThreads, 0) !=
           hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  cache[dev] = per_cu * cus;
-  return cache[dev];
+  cache[dev].store(per_cu * cus, std::memory_order_relaxed);
+  return per_cu * cus;
 }
 
 template <typename LT>
