@@ -134,3 +134,24 @@ def test_quad_workspace_left_by_the_streaming_path():
         torch.cuda.synchronize()
         rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
         assert rep["mismatch"] == 0, (path, rep["details"])
+
+
+def quad_case(seed):
+    # Seeded random shapes the path takes: V a multiple of 8 from 8 (three empty quarters) up to
+    # 262144 (32 segments a quarter), K up to 63, B up to 64, both dtypes, mixed rows.
+    g = np.random.default_rng(5000 + seed)
+    V = 8 * int(g.choice([int(g.integers(1, 128)), int(g.integers(128, 4096)),
+                          int(g.integers(4096, 32769))]))
+    K = int(g.choice([int(g.integers(0, 9)), int(g.integers(9, 64))]))
+    B = int(g.integers(1, max(2, min(65, 4_000_000 // ((K + 1) * V)))))
+    return gen.make_batch(B, K, V, seed=6000 + seed, dtype=str(g.choice(["bf16", "f32"])),
+                          greedy_frac=float(g.choice([0.0, 0.2, 1.0])),
+                          onehot_frac=float(g.choice([0.0, 0.3])),
+                          ragged=K > 0 and bool(g.integers(0, 2)),
+                          draft_at_row_temp=bool(g.integers(0, 2)),
+                          draft_sigma=float(g.choice([0.2, 1.5])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_quad_random_shapes(seed):
+    check(quad_case(seed), path=SPECDEC_PATH_QUAD)
