@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kQThreads) void quad_verify_kernel(
   __shared__ SeqState sh_st;
   __shared__ QuadPick sh_pick;
   __shared__ PickLds sh_ps;
-  __shared__ int sh_fail, sh_A, sh_draw_ok;
+  __shared__ int sh_fail, sh_draw_ok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qq = static_cast<int>(blockIdx.x) & 3;
   const int b = b0 + static_cast<int>(blockIdx.x >> 2);
@@ -304,10 +304,7 @@ __global__ __launch_bounds__(kQThreads) void quad_verify_kernel(
   __syncthreads();
   if (wave == 0 && !failed1) {
     const ScanOut so = accept_sequence(in, draft_probs != nullptr, kb_raw, T, c, K, V, sh_rows, lane);
-    if (lane == 0) {
-      sh_st = so.st;
-      sh_A = so.A;
-    }
+    if (lane == 0) sh_st = so.st;
     // Workgroup 0 writes the scan's outputs; the drawn slot is left to the pick.
     if (qq == 0) {
       const bool pending = so.st.mode != kNone;
