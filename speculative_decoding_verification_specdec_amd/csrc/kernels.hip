@@ -466,7 +466,16 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     const int seg0 = kFine ? (t % kSegPerChunk) * kSeg + wave * span : wave * kSeg;
     const int c0 = s * kChunk, n = min(kChunk, V - c0);
     double lw = 0.0, le = 0.0;
-    if constexpr (kVec) {
+    // A one-hot residual is p itself outside the segment that holds the rejected draft x: there
+    // its sums are the streaming kernel's partial rescaled to the row max, as for a bonus draw,
+    // and nothing is loaded; x's own segment is summed exactly below (taking e(x) out of the
+    // partial's sum could cancel when x dominates the segment).  Lane 0 of the wave (with fine
+    // items, of wave 0) holds the value, so the sums below add zeros to it.
+    const int seg_w = kFine ? t : s * kSegPerChunk + wave;  // the segment this wave sums into
+    if (st.mode == kResidualOnehot && seg_w != st.excl / kSeg) {
+      if (lane == 0 && (!kFine || wave == 0))
+        lw = le = partial_seg_sum(partials + row * nseg, seg_w, st);
+    } else if constexpr (kVec) {
       // Lane l owns the 4-token quads l, l + 64, ... of the wave's span: every load instruction
       // of the wave reads one contiguous span (4 logits, 8 or 16 bytes, and 4 fp32 draft
       // probabilities, 16 bytes, per lane), and all of them go out before any is unpacked.
