@@ -132,7 +132,8 @@ specdec_status specdec_verify(const void* target_logits, int32_t logits_dtype,
  * (code under HIP-graph capture, tight serving loops, harnesses that forbid allocation).  The
  * workspace is a file-scope device array of SPECDEC_NOALLOC_SCRATCH_BYTES (32 MiB) that each
  * device holds for the life of the process; its address is looked up once per device, on the
- * first call made with that device current.  The call allocates nothing (no hipMalloc, no
+ * first call whose stream belongs to that device (the null stream: the current device), the
+ * caller's current device being left as it was.  The call allocates nothing (no hipMalloc, no
  * library allocation).  Arguments, outputs, data errors and results are those of
  * specdec_verify (automatic path) with the same inputs.  Its argument checks (sizes, dtype,
  * NULL and misaligned pointers, with specdec_verify's status codes) run on the host before any

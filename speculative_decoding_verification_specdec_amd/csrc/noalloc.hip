@@ -4,8 +4,8 @@
 //
 // The array `scratch` holds SPECDEC_NOALLOC_SCRATCH_BYTES per device for the life of the process.
 // In host code its name is only a host-side stand-in, so each device's address is looked up once
-// (hipGetSymbolAddress, with that device current, on the first call there) and only that address
-// is handed to the kernels.  Every call on a device shares that device's array: calls that
+// (hipGetSymbolAddress, with that device current, on the first call whose stream belongs to it)
+// and only that address is handed to the kernels.  Every call on a device shares that device's array: calls that
 // overlap in time on one device race (the verify kernels need no initialised workspace, so
 // consecutive calls do not).
 #include <hip/hip_runtime.h>
@@ -24,14 +24,28 @@ constexpr int kMaxDevices = 64;
 void* g_scratch[kMaxDevices] = {};
 std::mutex g_scratch_mutex;
 
-// This device's address of `scratch`, looked up on the first call on the device; null on error.
-void* scratch_address() {
+// The address of `scratch` on the device the kernels will run on -- the stream's device (the
+// null stream: the current device) -- looked up on the first call there with that device made
+// current for the lookup (and the caller's current device restored); null on error.
+void* scratch_address(hipStream_t stream) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+    dev = static_cast<int>(d);
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (g_scratch[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (err != hipSuccess) return nullptr;
     g_scratch[dev] = p;
   }
   return g_scratch[dev];
@@ -66,7 +80,7 @@ specdec_status specdec_verify_noalloc(const void* target_logits, int32_t logits_
       V, accept_len, out_tokens, out_probs, false);
   if (st != SPECDEC_OK || B == 0) return st;
   if (specdec_workspace_size(B, K, V) > SPECDEC_NOALLOC_SCRATCH_BYTES) return SPECDEC_ERR_SCRATCH;
-  void* ws = scratch_address();
+  void* ws = scratch_address(static_cast<hipStream_t>(stream));
   if (ws == nullptr) return SPECDEC_ERR_LAUNCH;
   return specdec_verify(target_logits, logits_dtype, draft_probs, draft_onehot, proposed,
                         num_draft, temperature, uniforms, B, K, V, accept_len, out_tokens,

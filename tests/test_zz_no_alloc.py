@@ -57,6 +57,28 @@ def test_noalloc_matches_verify_on_two_calls_the_second_smaller():
         del d, want, out, got
 
 
+def test_noalloc_on_a_created_stream():
+    # The scratch is the one of the device the call's stream belongs to: a call enqueued on a
+    # created stream (not the null stream) is bit-identical to specdec_verify.
+    inp = gen.make_batch(16, 4, 30000, seed=934, onehot_frac=0.25, ragged=True)
+    print(f"\n[case] noalloc on a created stream B={inp.B} K={inp.K} V={inp.V}", flush=True)
+    d = inputs_to_device(inp, DEV)
+    want = specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
+                          d["uniforms"], draft_onehot=d["draft_onehot"], num_draft=d["num_draft"])
+    out = (torch.full((inp.B,), -7, dtype=torch.int32, device=DEV),
+           torch.full((inp.B, inp.K + 1), -7, dtype=torch.int32, device=DEV),
+           torch.full((inp.B, inp.K + 1), -7.0, dtype=torch.float32, device=DEV))
+    s = torch.cuda.Stream()
+    assert s.cuda_stream != 0
+    s.wait_stream(torch.cuda.current_stream())
+    got = specdec_verify_noalloc(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
+                                 d["uniforms"], draft_onehot=d["draft_onehot"],
+                                 num_draft=d["num_draft"], out=out, stream=s)
+    s.synchronize()
+    for g, w in zip(got, want):
+        assert np.array_equal(_bits(g), _bits(w))
+
+
 def test_noalloc_refuses_sizes_beyond_its_scratch():
     # Checked on the host before any launch: B = 4096, K = 8, V = 128256 needs more than 32 MiB.
     lib = load_library()
