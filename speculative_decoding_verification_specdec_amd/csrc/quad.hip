@@ -514,19 +514,33 @@ __global__ __launch_bounds__(kQThreads) void quad_verify_kernel(
 }
 
 template <typename LT>
-int quad_capacity() {
-  // Workgroups of this kernel the current device holds at once (cached per device; threads that
-  // race to fill an entry store the same value).
+int quad_capacity(hipStream_t stream) {
+  // Workgroups of this kernel that the device the call runs on -- the stream's (the null stream:
+  // the current device) -- holds at once; cached per device (threads that race to fill an entry
+  // store the same value).  The occupancy query runs with that device current, and the caller's
+  // current device is restored.
   static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int dev = -1;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return 0;
+    dev = static_cast<int>(d);
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return 0;
+  }
+  if (dev < 0 || dev >= 64) return 0;
   const int known = cache[dev].load(std::memory_order_relaxed);
   if (known != 0) return known;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return 0;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return 0;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quad_verify_kernel<LT>, kQThreads, 0) !=
-          hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  const bool ok =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quad_verify_kernel<LT>, kQThreads,
+                                                   0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  if (cur != dev && hipSetDevice(cur) != hipSuccess) return 0;
+  if (!ok) return 0;
   cache[dev].store(per_cu * cus, std::memory_order_relaxed);
   return per_cu * cus;
 }
@@ -561,7 +575,7 @@ bool quad_eligible(const LaunchArgs& a) {
       (a.draft_probs != nullptr && reinterpret_cast<uintptr_t>(a.draft_probs) % 16 != 0))
     return false;
   if ((quad_span(a.V) + kSeg - 1) / kSeg > kMaxQuadSeg) return false;
-  const int cap = a.logits_bf16 ? quad_capacity<uint16_t>() : quad_capacity<float>();
+  const int cap = a.logits_bf16 ? quad_capacity<uint16_t>(a.stream) : quad_capacity<float>(a.stream);
   return static_cast<long long>(a.B) * kQuarters <= cap;
 }
 
