@@ -289,6 +289,40 @@ BAD_Q_CASES = {
 }
 
 
+# One-hot residuals (p without the rejected draft x): the draw sums every segment except x's from
+# the streaming kernel's partials and x's segment exactly.  Every row is one-hot and rejected at
+# slot 0, with x at the edges of 2048-token segments and 8192-token chunks and at the row's end;
+# in every other row x holds about 99.8 % of row 0's mass (z(x) = max + 9 at T = 1), so the
+# residual is what is left beside it and x's segment must be summed without it.  On every draw
+# grid: one workgroup per segment, one resident round, the split grid with its pick kernel; and
+# on the scalar path (V not a multiple of 8).
+ONEHOT_CASES = {
+    "fine": (16, 3, 30000),
+    "fine_scalar": (16, 3, 30001),
+    "one_round": (96, 3, 40000),
+    "split": (400, 2, 40000),
+    "split_scalar": (400, 2, 40003),
+}
+
+
+@pytest.mark.parametrize("name", list(ONEHOT_CASES))
+def test_onehot_residual_at_segment_edges(name):
+    B, K, V = ONEHOT_CASES[name]
+    inp = gen.make_batch(B, K, V, seed=58, dtype="f32", onehot_frac=1.0, temp_const=1.0)
+    L, X, U = inp.logits, inp.proposed, inp.uniforms
+    edges = [0, 1, 2047, 2048, 2049, 8191, 8192, 16383, V - 2049, V - 2048, V - 2, V - 1]
+    for b in range(B):
+        x = edges[b % len(edges)]
+        X[b, 0] = x
+        U[b, 0] = np.float32(0.99999988)
+        if (b // len(edges)) % 2 == 0:
+            L[b, 0, x] = L[b, 0].max() + 9.0
+    check(inp)
+    acc, tok, _ = run_gpu(inp)
+    assert (acc == 0).all()
+    assert (tok[:, 0] != X[:, 0]).all()
+
+
 @pytest.mark.parametrize("name", list(BAD_Q_CASES))
 def test_bad_entries_in_draft_rows(name):
     # In half the rejected model-draft sequences, one entry of the rejected slot's draft row (the
