@@ -289,6 +289,17 @@ BAD_Q_CASES = {
 }
 
 
+def test_pick_inside_a_draw_grid_larger_than_the_chip_holds():
+    # 88 sequences x 16 chunks = 1408 draw workgroups: the draw kernel still picks inside (grids of
+    # at most 1536), but at its occupancy the chip holds fewer at once (1280 on MI355X), so some
+    # chunk-0 workgroups wait while siblings are still queued -- the wait ends because the queue
+    # ahead of a sibling holds no other waiting workgroup.  Every sequence must come out exact.
+    inp = gen.make_batch(88, 2, 131072, seed=59, onehot_frac=0.25, greedy_frac=0.1)
+    rep = check(inp)
+    acc, _, _ = run_gpu(inp)
+    assert (acc >= 0).all(), rep
+
+
 # One-hot residuals (p without the rejected draft x): the draw sums every segment except x's from
 # the streaming kernel's partials and x's segment exactly.  Every row is one-hot and rejected at
 # slot 0, with x at the edges of 2048-token segments and 8192-token chunks and at the row's end;
