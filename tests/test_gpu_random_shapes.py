@@ -3,7 +3,9 @@ small-vocabulary limit), dtype and row mix drawn per case, each compared with th
 default path and, for V <= SPECDEC_SMALL_V_MAX, on the streaming kernels too; every other case
 also through the sample-and-match entry point and, the others, through the greedy entry point
 (every row at temperature 0, bit-exact).  Same bar as the other parity tests (oracle/parity.py).
-The n-gram drafter gets its own seeded random shapes (bit-exact against its oracle)."""
+A second family of seeded shapes has draw grids past one resident round (the split passes),
+mostly with one-hot rows.  The n-gram drafter gets its own seeded random shapes (bit-exact
+against its oracle)."""
 import numpy as np
 import pytest
 import torch
@@ -54,6 +56,41 @@ def test_random_shape_parity(seed):
         assert rep["mismatch"] == 0, rep["details"]
         limit = boundary_limit(expected_boundary(inp, ref))
         assert rep["boundary"] <= limit, (rep, limit)
+
+
+def split_case(seed):
+    # Draw grids past one resident round (B x chunks > 1536): the scan pass, the draw-only pass
+    # and the pick kernel; mostly one-hot rows, whose residual sums come from the partials outside
+    # the rejected draft's segment.
+    g = np.random.default_rng(5000 + seed)
+    B = int(g.choice([128, 256, 512]))
+    K = int(g.integers(1, 5))
+    s_min = 1536 // B + 1
+    V = int(g.integers(max(8192 * (s_min - 1) + 1, 12000), 8192 * (s_min + 3)))
+    if g.integers(0, 2):
+        V -= V % 8
+    return gen.make_batch(B, K, V, seed=6000 + seed, dtype=str(g.choice(["bf16", "f32"])),
+                          onehot_frac=float(g.choice([0.5, 0.9, 1.0])),
+                          greedy_frac=float(g.choice([0.0, 0.1])), ragged=bool(g.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_split_grid_parity(seed):
+    inp = split_case(seed)
+    assert inp.B * ((inp.V + 8191) // 8192) > 1536
+    print(f"\n[case] split seed={seed} B={inp.B} K={inp.K} V={inp.V} {inp.logits_dtype}",
+          flush=True)
+    ref = oracle.verify(inp)
+    d = inputs_to_device(inp, DEV)
+    acc, tok, prb = specdec_verify(d["logits"], d["draft_probs"], d["proposed"], d["temperature"],
+                                   d["uniforms"], draft_onehot=d["draft_onehot"],
+                                   num_draft=d["num_draft"])
+    torch.cuda.synchronize()
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    print("[report]", {k: v for k, v in rep.items() if k != "details"}, flush=True)
+    assert rep["mismatch"] == 0, rep["details"]
+    limit = boundary_limit(expected_boundary(inp, ref))
+    assert rep["boundary"] <= limit, (rep, limit)
 
 
 @pytest.mark.parametrize("seed", range(0, N_CASES, 2))
