@@ -432,13 +432,9 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
       if (wave == 0) {
         double lw = 0.0;
         for (int q = 0; q < P && j0 + q < nseg; ++q) lw += partial_seg_sum(prow, j0 + q, st);
-        // (Sums of p, rescaled partials of a validated row: never NaN.)  A lane with one
-        // segment holds its sum already (lw = 0 + that sum, exactly): no second load.
+        // (Sums of p, rescaled partials of a validated row: never NaN.)
         (void)find_draw_segment(lw, lw, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol],
-                                nseg, P,
-                                [&](int j, bool) {
-                                  return P == 1 ? lw : partial_seg_sum(prow, j, st);
-                                },
+                                nseg, P, [&](int j, bool) { return partial_seg_sum(prow, j, st); },
                                 sh_pick, lane);
       }
       __syncthreads();
@@ -575,8 +571,6 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
       drawable = find_draw_segment(lw, le, uniforms[static_cast<long long>(b) * (K + 1) + st.ucol],
                                    nseg, P,
                                    [&](int j, bool plain) {
-                                     // One segment per lane: its sums are lw and le already.
-                                     if (P == 1) return plain ? le : lw;
                                      double w, e;
                                      seg_words(sw + j * 4, w, e);
                                      return plain ? e : w;
@@ -637,8 +631,6 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(
     if (wave == 0) {
       const bool ok = find_draw_segment(lw, le, read_lane_f(u_lane, st.ucol), nseg, P,
                                         [&](int j, bool plain) {
-                                          // One segment per lane: its sums are lw and le.
-                                          if (P == 1) return plain ? le : lw;
                                           return plain ? segs[j].e : segs[j].w;
                                         },
                                         ps, lane);

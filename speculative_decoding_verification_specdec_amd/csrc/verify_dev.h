@@ -499,7 +499,8 @@ struct PickLds {
 };
 
 // First step, in wave 0: lane l holds the sums (lw: the draw's weights; le: those of p) of its
-// segments [l * P, l * P + P); seg_at(j, plain) gives segment j's sum again.  Leaves the segment,
+// segments [l * P, l * P + P); seg_at(j, plain) gives segment j's sum again (not called when
+// each lane has one segment).  Leaves the segment,
 // the target u * total and the running sum before the segment in ps.  Returns false (in every
 // lane) when the weights' total is NaN -- a draft row holding a value that is not a probability
 // -- and the sequence is to be reported invalid.
@@ -526,7 +527,8 @@ __device__ __forceinline__ bool find_draw_segment(double lw, double le, float u,
     int seg = -1, lastpos = -1;
     double base_seg = 0.0, base_last = 0.0;
     for (int q = 0; q < P && j0 + q < nseg; ++q) {
-      const double v = seg_at(j0 + q, plain);
+      // A lane with one segment holds its sum already (own = 0 + that sum, exactly).
+      const double v = P == 1 ? own : seg_at(j0 + q, plain);
       if (v > 0.0) {
         if (run + v > t) { seg = j0 + q; base_seg = run; break; }
         lastpos = j0 + q;
