@@ -19,7 +19,8 @@
 //       the chunk-0 workgroup emits every token already known (accepted drafts, greedy argmaxes) and
 //       records what remains to be drawn.  Then the workgroup sums the draw's weights -- s * max(0, p
 //       - q) or p without the rejected draft -- over each 2048-token segment of its chunk (fp64 DPP
-//       wave sums); a plain draw of p takes those sums from the streaming kernel's partials instead.
+//       wave sums); a plain draw of p takes those sums from the streaming kernel's partials instead,
+//       and so does a one-hot residual in every segment but the rejected draft's.
 //   pick_kernel  one workgroup per sequence that needs a draw: one fp64 DPP scan over the
 //       segment sums finds the segment holding u * total, then a scan of that one segment in
 //       ascending token order finds the first running sum above u * total.
