@@ -338,8 +338,8 @@ constexpr int kPickSpinLimit = 1 << 20;
 // Accept scan + draw weight sums.  Grid: x = chunk of the row to draw from, y = sequence (offset
 // by b0).  kPhase 0: every workgroup runs its sequence's accept scan (all waves merge partials,
 // wave 0 decides) and the chunk-0 workgroup writes the scan's outputs and the draw state; then
-// wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns 4-token quads
-// l, l + 64, ...), in fp64.  kPhase 1: the scan only (one workgroup per sequence).  kPhase 2:
+// wave w sums the draw weights of 2048-token segment w of the chunk (lane l owns the 8-token
+// groups l, l + 64, ... of bf16 rows, the 4-token quads of fp32 ones), in fp64.  kPhase 1: the scan only (one workgroup per sequence).  kPhase 2:
 // the draw only, from the state kPhase 1 wrote.  kPhase 3: as kPhase 0, but one workgroup per
 // 2048-token segment, its four waves a quarter each (grids too small to fill the chip: a
 // workgroup alone pulls its bytes through one CU's few outstanding misses).
@@ -472,10 +472,43 @@ __global__ __launch_bounds__(kThreads, 4) void accept_draw_kernel(
     if (st.mode == kResidualOnehot && seg_w != st.excl / kSeg) {
       if (lane == 0 && (!kFine || wave == 0))
         lw = le = partial_seg_sum(partials + row * nseg, seg_w, st);
+    } else if constexpr (kVec && sizeof(LT) == 2) {
+      // bf16 rows: lane l owns the 8-token groups l, l + 64, ... of the wave's span, one 16-byte
+      // target load and two 16-byte draft loads per group, all issued before any is unpacked
+      // (every load 16 bytes wide: 4-token quads would load the logits 8 bytes at a time).
+      constexpr int kG8 = kSeg / 8 / 64 / (kFine ? kWaves : 1);  // 4, or 1
+      uint4 zr[kG8], qa[kG8], qb[kG8];
+#pragma unroll
+      for (int h = 0; h < kG8; ++h) {
+        const int v0 = c0 + seg0 + (h * 64 + lane) * 8;
+        const bool in = v0 < c0 + n;
+        zr[h] = in ? plain_load(z + v0) : make_uint4(0, 0, 0, 0);
+        qa[h] = (in && q != nullptr) ? plain_load(q + v0) : make_uint4(0, 0, 0, 0);
+        qb[h] = (in && q != nullptr) ? plain_load(q + v0 + 4) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int h = 0; h < kG8; ++h) {
+        const int v0 = seg0 + (h * 64 + lane) * 8;
+        float zv[8], qv[8];
+        unpack(zr[h], zv, static_cast<const uint16_t*>(nullptr));
+        unpack(qa[h], qv, static_cast<const float*>(nullptr));
+        unpack(qb[h], qv + 4, static_cast<const float*>(nullptr));
+        const int cnt = min(8, n - v0);
+        float gw = 0.f, ge = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float e = 0.f;
+          const float w = k < cnt ? draw_weight(zv[k], qv[k], c0 + v0 + k, st, false, e) : 0.f;
+          gw += w;
+          ge += k < cnt ? e : 0.f;
+        }
+        lw += gw;
+        le += ge;
+      }
     } else if constexpr (kVec) {
-      // Lane l owns the 4-token quads l, l + 64, ... of the wave's span: every load instruction
-      // of the wave reads one contiguous span (4 logits, 8 or 16 bytes, and 4 fp32 draft
-      // probabilities, 16 bytes, per lane), and all of them go out before any is unpacked.
+      // fp32 rows: lane l owns the 4-token quads l, l + 64, ... of the wave's span: every load
+      // instruction of the wave reads one contiguous span (4 logits and 4 draft probabilities,
+      // 16 bytes each, per lane), and all of them go out before any is unpacked.
       constexpr int kQuads = kSeg / 4 / 64 / (kFine ? kWaves : 1);  // 8, or 2
       DrawVec<LT> zr[kQuads];
       uint4 qr[kQuads];
