@@ -13,6 +13,8 @@ constexpr int kChunk = 8192;                // logits per row chunk (one workgro
 constexpr int kGroup = 8;                   // consecutive tokens per thread in the draw passes
 constexpr int kSeg = kThreads * kGroup;     // 2048 tokens per draw segment
 constexpr int kSegPerChunk = kChunk / kSeg; // 4
+constexpr unsigned kXcdBlock = 64;          // tiles per XCD block in the blocked streaming order
+constexpr unsigned long long kXcdBlockMinBytes = 256ull << 20;  // streams that take it
 
 // Per (row, 2048-token sub-chunk) partial statistics of the streaming pass.  The 16-byte
 // records (also SeqState, Gather, SegSums) are 16-byte aligned so each is one vector load.

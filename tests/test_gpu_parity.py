@@ -16,6 +16,7 @@ from speculative_decoding_verification_specdec_amd import (SPECDEC_PATH_AUTO,
                                                            SPECDEC_PATH_STREAMING,
                                                            SPECDEC_SMALL_V_MAX, inputs_to_device,
                                                            specdec_verify, specdec_verify_greedy,
+                                                           specdec_verify_match,
                                                            specdec_workspace_size)
 from speculative_decoding_verification_specdec_amd import inputs as gen
 
@@ -139,6 +140,34 @@ def test_streaming_path_past_one_launch_per_kernel():
     inp = gen.tiny_vocab()
     assert inp.B > 65535
     check(inp, path=SPECDEC_PATH_STREAMING)
+
+
+def test_blocked_tile_order_on_a_long_stream():
+    # 112 sequences x 9 rows x 152064 bf16 logits, no padding rows: 314 MB in 19152 streaming
+    # tiles, past the size at which the streaming kernel deals blocks of tiles to the XCDs in
+    # turn; 19152 is not a multiple of a whole round of blocks (512 tiles), so the last 208 tiles
+    # keep the plain order.  The sampled verify (a quarter of the rows greedy), the greedy entry
+    # point and sample-and-match, each against the oracle.
+    inp = gen.large_batch_deep(B=112, seed=71)
+    assert inp.num_draft is None and inp.B * (inp.K + 1) * 19 * 8192 * 2 >= 256 << 20
+    d = inputs_to_device(inp, DEV)
+    check(inp)
+    acc, tok, prb = specdec_verify_greedy(d["logits"], d["proposed"])
+    torch.cuda.synchronize()
+    g = gen.VerifyInputs(inp.logits, inp.logits_dtype, None, None, inp.proposed, inp.num_draft,
+                         np.zeros(inp.B, np.float32), inp.uniforms, name="greedy")
+    ref = oracle.verify(g)
+    assert np.array_equal(acc.cpu().numpy(), ref.accept_len)
+    assert np.array_equal(tok.cpu().numpy(), ref.out_tokens)
+    rep = compare(g, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy())
+    assert rep["mismatch"] == 0 and rep["boundary"] == 0, rep
+    acc, tok, prb = specdec_verify_match(d["logits"], d["proposed"], d["temperature"],
+                                         d["uniforms"])
+    torch.cuda.synchronize()
+    ref = oracle.verify_match(inp)
+    rep = compare(inp, ref, acc.cpu().numpy(), tok.cpu().numpy(), prb.cpu().numpy(), mode="match")
+    assert rep["mismatch"] == 0, rep["details"]
+    assert rep["boundary"] <= boundary_limit(expected_boundary(inp, ref, mode="match")), rep
 
 
 def test_greedy_entry_point_is_bit_exact():
