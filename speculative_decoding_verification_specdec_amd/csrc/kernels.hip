@@ -780,8 +780,10 @@ hipError_t launch_typed(const LaunchArgs& a) {
     // once) loses 10 us on 1 GB.
     const unsigned long long tiles =
         static_cast<unsigned long long>(grid.x) * grid.y * grid.z;
+    const unsigned long long bytes =
+        static_cast<unsigned long long>(grid.y) * grid.z * static_cast<unsigned>(a.V) * sizeof(LT);
     const auto stats = stats_for(a.num_draft == nullptr && tiles < (1ull << 31) &&
-                                 tiles * kChunk * sizeof(LT) >= kXcdBlockMinBytes);
+                                 bytes >= kXcdBlockMinBytes);
     hipEvent_t ev0 = b0 == 0 ? a.hot_begin : nullptr;
     hipEvent_t ev1 = b0 + kMaxZ >= a.B ? a.hot_end : nullptr;
     if (ev0 || ev1)

@@ -143,13 +143,13 @@ def test_streaming_path_past_one_launch_per_kernel():
 
 
 def test_blocked_tile_order_on_a_long_stream():
-    # 112 sequences x 9 rows x 152064 bf16 logits, no padding rows: 314 MB in 19152 streaming
-    # tiles, past the size at which the streaming kernel deals blocks of tiles to the XCDs in
-    # turn; 19152 is not a multiple of a whole round of blocks (512 tiles), so the last 208 tiles
-    # keep the plain order.  The sampled verify (a quarter of the rows greedy), the greedy entry
+    # 112 sequences x 9 rows x 152064 bf16 logits, no padding rows: 306 MB (292 MiB) in 19152
+    # streaming tiles, past the 256 MiB at which the streaming kernel deals blocks of tiles to the
+    # XCDs in turn; 19152 is not a multiple of a whole round of blocks (512 tiles), so the last 208
+    # tiles keep the plain order.  The sampled verify (a quarter of the rows greedy), the greedy entry
     # point and sample-and-match, each against the oracle.
     inp = gen.large_batch_deep(B=112, seed=71)
-    assert inp.num_draft is None and inp.B * (inp.K + 1) * 19 * 8192 * 2 >= 256 << 20
+    assert inp.num_draft is None and inp.B * (inp.K + 1) * inp.V * 2 >= 256 << 20
     d = inputs_to_device(inp, DEV)
     check(inp)
     acc, tok, prb = specdec_verify_greedy(d["logits"], d["proposed"])
